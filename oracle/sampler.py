@@ -1,0 +1,99 @@
+"""Oracle for the per-canvas accept / renoise / convergence step, in fp64.
+
+Definitions followed:
+
+* Entropy-bounded acceptance (Technical Report part 2/6, sec. 3.3 "Entropy-bounded token
+  refinement"; DiffusionGemma Explained, "Sampling" -> "Keep a low-entropy prefix and
+  renoise the rest"; vLLM blog, sampler section): order positions by entropy, lowest
+  first, and accept the longest prefix of that order whose entropies *before* the
+  position sum to at most the budget: position of rank k is accepted iff
+  sum_{j<k} H_(j) <= budget.  Readings: the comparison is "<=" (the executable code on the
+  DiffusionGemma Explained page); ties in entropy are ordered by position (stable sort).
+* Accepted positions take their Gumbel-max sample; every other position is renoised with a
+  uniform token drawn from the Philox renoise stream.
+* Stability / convergence (Technical Report sec. 3.3 "Adaptive stopping heuristic";
+  DiffusionGemma Explained, "Check for early stopping"; vLLM blog, convergence): the argmax
+  canvas equals the previous step's argmax canvas at every position -> stable_count + 1,
+  else 0; the canvas has converged when stable_count >= stability_threshold and the mean
+  entropy is strictly below confidence_threshold.  prev_argmax = -1 marks "no previous
+  canvas".
+* Commit canvases (vLLM blog: a converged canvas is committed as its clean argmax): the
+  next tokens are the argmax tokens, every position counts as accepted, the state resets
+  (prev_argmax = -1, stable_count = 0) and converged = 0; mean entropy is not written.
+
+Margins reported for the parity tests:
+  mu_acc(i) = min(|P_rank(i) - budget|, min |H_i - H_j| over positions j with the other
+  decision); mu_conv = |mean H - confidence_threshold|.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import philox
+
+
+@dataclass
+class SamplerResult:
+    next_tokens: np.ndarray     # int64 [R]
+    accept: np.ndarray          # uint8 [R]
+    converged: np.ndarray       # uint8 [n]
+    mean_entropy: np.ndarray    # fp64 [n], NaN for commit canvases
+    prev_argmax: np.ndarray     # int64 [R] (updated state)
+    stable_count: np.ndarray    # int64 [n] (updated state)
+    mu_accept: np.ndarray       # fp64 [R], inf for commit canvases
+    mu_conv: np.ndarray         # fp64 [n], inf for commit canvases
+
+
+def accept_renoise(entropy, argmax_tok, gumbel_tok, commit, n_canvas: int, C: int, V: int,
+                   budget: float, confidence: float, stability: int, seed: int, step,
+                   prev_argmax, stable_count) -> SamplerResult:
+    H = np.asarray(entropy, dtype=np.float64)
+    am = np.asarray(argmax_tok, dtype=np.int64)
+    gt = np.asarray(gumbel_tok, dtype=np.int64)
+    prev = np.array(prev_argmax, dtype=np.int64, copy=True)
+    cnt = np.array(stable_count, dtype=np.int64, copy=True)
+    step = np.broadcast_to(np.asarray(step, dtype=np.int64), (n_canvas,))
+    R = n_canvas * C
+    nxt = np.zeros(R, dtype=np.int64)
+    acc = np.zeros(R, dtype=np.uint8)
+    conv = np.zeros(n_canvas, dtype=np.uint8)
+    meanH = np.full(n_canvas, np.nan)
+    mu_acc = np.full(R, np.inf)
+    mu_conv = np.full(n_canvas, np.inf)
+    for c in range(n_canvas):
+        rows = np.arange(c * C, (c + 1) * C)
+        if commit is not None and commit[c]:
+            nxt[rows] = am[rows]
+            acc[rows] = 1
+            prev[rows] = -1
+            cnt[c] = 0
+            conv[c] = 0
+            continue
+        h = H[rows]
+        order = sorted(range(C), key=lambda i: (h[i], i))
+        before = 0.0
+        prefix = np.zeros(C)
+        for k, i in enumerate(order):
+            prefix[i] = before
+            before += h[i]
+        a = prefix <= budget
+        acc[rows] = a.astype(np.uint8)
+        ren = philox.renoise_tokens(rows, V, seed, int(step[c]))
+        nxt[rows] = np.where(a, gt[rows], ren)
+        same = bool(np.all(am[rows] == prev[rows]))
+        cnt[c] = cnt[c] + 1 if same else 0
+        prev[rows] = am[rows]
+        meanH[c] = float(np.sum(h)) / C
+        conv[c] = 1 if (cnt[c] >= stability and meanH[c] < confidence) else 0
+        # margins
+        for i in range(C):
+            m = abs(prefix[i] - budget)
+            other = h[a != a[i]]
+            if other.size:
+                m = min(m, float(np.min(np.abs(other - h[i]))))
+            mu_acc[rows[i]] = m
+        mu_conv[c] = abs(meanH[c] - confidence)
+    return SamplerResult(next_tokens=nxt, accept=acc, converged=conv, mean_entropy=meanH,
+                         prev_argmax=prev, stable_count=cnt, mu_accept=mu_acc, mu_conv=mu_conv)

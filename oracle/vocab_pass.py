@@ -1,0 +1,115 @@
+"""Oracle for the vocab pass: per canvas position, everything the sampler needs from the
+tied-unembedding logits, computed from the plain definitions in fp64.
+
+Definitions followed (cited by page and section):
+
+* logits  S_v = sum_k h_k E_{v,k} with the tied embedding E[V, d] used as the unembedding
+  (DiffusionGemma Explained, "Tied embeddings" / final logits; Technical Report part 2/6,
+  sec. 3.2 eq. (5)).
+* tempered distribution  p = Softmax(S / T)  (Technical Report sec. 3.2 eq. (6);
+  DiffusionGemma Explained, "Sampling" -> "Apply temperature").
+* lse = log sum_v exp(S_v / T); entropy H = -sum_v p_v log p_v = sum_v p_v (lse - z_v)
+  (DiffusionGemma Explained, "Sampling" -> "Compute entropy").
+* argmax token: the smallest v attaining max S (deterministic prediction used by the
+  stability test; Technical Report sec. 3.3 "Adaptive stopping heuristic"; vLLM blog,
+  convergence: committed tokens are the clean argmax).
+* Gumbel-max sample: the smallest v attaining max (z_v + g_v), g_v standard Gumbel noise
+  from the Philox layout in ``oracle.philox`` (vLLM blog, sampler section: the candidate
+  token is argmax(logits / T + Gumbel noise); DiffusionGemma Explained, "Sampling": accepted
+  positions take a sample of their distribution).
+* self-conditioning expectation sc = sum_v p_v E_v = p_hat_0 E (Technical Report sec. 3.2
+  eq. (6), the argument of FFW; DiffusionGemma Explained, "Self-conditioning").
+
+Rows of commit canvases produce only the argmax token (vLLM blog: a converged canvas emits
+its clean argmax and gets no further sampling or self-conditioning).
+
+Decision margins (reported, used by the parity tests to exempt near-ties):
+  mu_A = S_(1) - S_(2) and mu_G = y_(1) - y_(2) over distinct vocab indices.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import philox
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact fp64 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+@dataclass
+class RowResult:
+    rows: np.ndarray        # global row ids
+    lse: np.ndarray         # fp64, NaN for commit rows
+    entropy: np.ndarray     # fp64, NaN for commit rows
+    argmax: np.ndarray      # int64
+    gumbel: np.ndarray      # int64, -1 for commit rows
+    sc: Optional[np.ndarray]  # fp64 [n, d], NaN rows for commit rows
+    mu_argmax: np.ndarray   # fp64 margins
+    mu_gumbel: np.ndarray   # fp64 margins, inf for commit rows
+
+
+def _top2_margin(x: np.ndarray) -> float:
+    if x.shape[0] < 2:
+        return np.inf
+    i = int(np.argmax(x))
+    best = x[i]
+    rest = np.delete(x, i)
+    return float(best - rest.max())
+
+
+def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
+                    temperature_row: np.ndarray, commit_row: np.ndarray,
+                    seed: int, step_row: np.ndarray, want_sc: bool = True,
+                    row_block: int = 64) -> RowResult:
+    """Oracle results for the listed global rows.
+
+    E64            fp64 [V, d] (the widened bf16 embedding)
+    h_bits         bf16 bits [R, d] of the whole batch (only ``rows`` are read)
+    temperature_row, commit_row, step_row: per global row (indexable by row id)
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    V, d = E64.shape
+    n = rows.shape[0]
+    lse = np.full(n, np.nan)
+    ent = np.full(n, np.nan)
+    amax = np.zeros(n, dtype=np.int64)
+    gtok = np.full(n, -1, dtype=np.int64)
+    mu_a = np.zeros(n)
+    mu_g = np.full(n, np.inf)
+    sc = np.full((n, d), np.nan) if want_sc else None
+    for b0 in range(0, n, row_block):
+        b1 = min(n, b0 + row_block)
+        hb = widen_bf16(h_bits[rows[b0:b1]])
+        S = hb @ E64.T                                   # [b, V] fp64 logits
+        for j in range(b1 - b0):
+            i = b0 + j
+            r = int(rows[i])
+            s = S[j]
+            amax[i] = int(np.argmax(s))                  # first index attaining the max
+            mu_a[i] = _top2_margin(s)
+            if commit_row[r]:
+                continue
+            T = float(temperature_row[r])
+            z = s / T
+            m = z.max()
+            lse[i] = m + np.log(np.sum(np.exp(z - m)))
+            p = np.exp(z - lse[i])
+            ent[i] = float(np.sum(p * (lse[i] - z)))
+            g = philox.gumbel_noise(r, V, seed, int(step_row[r]))
+            y = z + g
+            gtok[i] = int(np.argmax(y))
+            mu_g[i] = _top2_margin(y)
+            if want_sc:
+                sc[i] = p @ E64
+    return RowResult(rows=rows, lse=lse, entropy=ent, argmax=amax, gumbel=gtok, sc=sc,
+                     mu_argmax=mu_a, mu_gumbel=mu_g)
+
+
+def per_row(values_per_canvas: np.ndarray, C: int) -> np.ndarray:
+    return np.repeat(np.asarray(values_per_canvas), C)
