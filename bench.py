@@ -1,0 +1,161 @@
+"""Benchmark of one denoising step of the hot path on one MI355X.
+
+A step = dg_vocab_pass + dg_accept_renoise over one batch of canvases, inputs resident in
+HBM.  Default workload: the batched serving step (32 canvases x 256 positions, V = 262144,
+d = 2816, 8 canvases commit).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched|large_v|lite|tiny]
+                    [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(wl) -> float:
+    """2 R V d for the logits of every row + 2 R_nc V d for the expectation of non-commit rows."""
+    R = wl.R
+    R_nc = int((wl.commit == 0).sum()) * wl.C
+    return 2.0 * R * wl.V * wl.d + 2.0 * R_nc * wl.V * wl.d
+
+
+def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
+    """The fp64 oracle, untuned, on a bounded sample of rows of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import vocab_pass as ovp
+    t0 = time.perf_counter()
+    E64 = ovp.widen_bf16(wl.E)
+    widen_s = time.perf_counter() - t0
+    T = np.repeat(wl.temperature, wl.C)
+    cm = np.repeat(wl.commit.astype(bool), wl.C)
+    st = np.repeat(wl.step, wl.C)
+    nc_rows = np.nonzero(~cm)[0]
+    rows_done, spent, k = 0, 0.0, 0
+    chunk = 4
+    while spent < budget_s and k * chunk < nc_rows.size:
+        rows = nc_rows[k * chunk:(k + 1) * chunk]
+        t0 = time.perf_counter()
+        ovp.vocab_pass_rows(E64, wl.h, rows, T, cm, wl.seed, st, want_sc=True)
+        spent += time.perf_counter() - t0
+        rows_done += rows.size
+        k += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": rows_done / spent, "unit": "canvas-positions/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows_done} non-commit positions of the {wl.name} workload, full vocabulary "
+                      f"(logits, softmax, entropy, argmax, Gumbel, selfcond), fp64 numpy, "
+                      f"{spent:.1f}s; bf16->fp64 widening of E ({widen_s:.1f}s) excluded"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="batched")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the vocabulary pass shards by canvas or by vocabulary; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from denoise_step_sampler_amd import runner, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] building inputs for workload {args.workload}")
+    wl = synth.workload(args.workload, seed=args.seed)
+    b = runner.from_workload(wl)
+    stream = torch.cuda.current_stream()
+    seed = args.seed
+
+    def step(k):
+        b.step.fill_(k)
+        runner.vocab_pass(b, seed, stream)
+        runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, plus per-launch events around the vocabulary pass
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        b.step.fill_(args.warmup + k)
+        ev[k][0].record(stream)
+        runner.vocab_pass(b, seed, stream)
+        ev[k][1].record(stream)
+        runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    vp_ms = [a.elapsed_time(z) for a, z in ev]
+    vp_avg = float(np.mean(vp_ms))
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.3f}s), "
+        f"vocab pass {vp_avg:.3f} ms (min {min(vp_ms):.3f})")
+
+    flops = algorithmic_flops(wl)
+    ach_tflops = flops / (vp_avg * 1e-3) / 1e12
+    positions = wl.R
+    res = {
+        "metric": "canvas-positions/sec per denoise step",
+        "value": positions / (ms_step * 1e-3),
+        "unit": "canvas-positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
+                   "d": wl.d, "commit_canvases": int(wl.commit.sum()),
+                   "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget},
+        "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "roofline": {
+            "kernel": "dg_vocab_pass",
+            "bound": "mfma", "achieved": ach_tflops, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": ach_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+            "algorithmic_flops_per_launch": flops, "avg_launch_ms": vp_avg},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f}s of oracle work)")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

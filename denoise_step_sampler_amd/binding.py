@@ -1,0 +1,163 @@
+"""Python binding of libdg.so: argument marshalling only.
+
+Every function takes torch CUDA tensors (device memory owned by the caller), checks dtype,
+device and contiguity, and hands raw pointers and sizes to the C entry point of the same
+name.  All arithmetic happens in the HIP kernels.  There is no fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdg.so")
+
+DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = range(5)
+DG_CANVAS = 256
+
+EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_accept_renoise", "dg_q_sample",
+            "dg_status_string", "dg_last_error")
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdg.so (after torch, so that the library shares torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, I, U64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+    lib.dg_vocab_pass_workspace_size.argtypes = [I, I, I, I]
+    lib.dg_vocab_pass_workspace_size.restype = SZ
+    lib.dg_vocab_pass.argtypes = [P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P]
+    lib.dg_vocab_pass.restype = I
+    lib.dg_accept_renoise.argtypes = [P, P, P, P, I, I, I, F, F, I, U64, P, P, P, P, P, P, P, P]
+    lib.dg_accept_renoise.restype = I
+    lib.dg_q_sample.argtypes = [P, I, I, I, P, U64, P, P]
+    lib.dg_q_sample.restype = I
+    lib.dg_status_string.argtypes = [I]
+    lib.dg_status_string.restype = ctypes.c_char_p
+    lib.dg_last_error.argtypes = []
+    lib.dg_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != DG_OK:
+        lib = load()
+        raise DGError(status, f"{lib.dg_status_string(status).decode()}: "
+                              f"{lib.dg_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: torch.dtype, numel: Optional[int], name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def dg_vocab_pass_workspace_size(n_canvas: int, C: int, V: int, d: int) -> int:
+    return int(load().dg_vocab_pass_workspace_size(n_canvas, C, V, d))
+
+
+def dg_vocab_pass(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: int, V: int, d: int,
+                  temperature: torch.Tensor, commit: Optional[torch.Tensor], seed: int,
+                  step: torch.Tensor, lse: Optional[torch.Tensor], entropy: torch.Tensor,
+                  argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                  selfcond: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    """E, h: bf16 bit patterns as torch.int16/uint16 or torch.bfloat16."""
+    R = n_canvas * C
+    lib = load()
+    eb = _bf16_ptr(E, V * d, "E")
+    hb = _bf16_ptr(h, R * d, "h")
+    st = lib.dg_vocab_pass(
+        eb, hb, n_canvas, C, V, d,
+        _ptr(temperature, torch.float32, n_canvas, "temperature"),
+        _ptr(commit, torch.uint8, n_canvas, "commit"),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(step, torch.int32, n_canvas, "step"),
+        _ptr(lse, torch.float32, R, "lse"),
+        _ptr(entropy, torch.float32, R, "entropy"),
+        _ptr(argmax_tok, torch.int32, R, "argmax_tok"),
+        _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
+        _ptr(selfcond, torch.float32, R * d, "selfcond"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check(st)
+
+
+def _bf16_ptr(t: torch.Tensor, numel: int, name: str):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected bf16 bits")
+    return _ptr(t, t.dtype, numel, name)
+
+
+def dg_accept_renoise(entropy: torch.Tensor, argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                      commit: Optional[torch.Tensor], n_canvas: int, C: int, V: int,
+                      entropy_budget: float, confidence_threshold: float,
+                      stability_threshold: int, seed: int, step: torch.Tensor,
+                      prev_argmax: torch.Tensor, stable_count: torch.Tensor,
+                      next_tokens: torch.Tensor, accept_mask: Optional[torch.Tensor],
+                      converged: torch.Tensor, mean_entropy: Optional[torch.Tensor],
+                      stream=None) -> None:
+    R = n_canvas * C
+    st = load().dg_accept_renoise(
+        _ptr(entropy, torch.float32, R, "entropy"),
+        _ptr(argmax_tok, torch.int32, R, "argmax_tok"),
+        _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
+        _ptr(commit, torch.uint8, n_canvas, "commit"),
+        n_canvas, C, V, float(entropy_budget), float(confidence_threshold),
+        int(stability_threshold), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(step, torch.int32, n_canvas, "step"),
+        _ptr(prev_argmax, torch.int32, R, "prev_argmax"),
+        _ptr(stable_count, torch.int32, n_canvas, "stable_count"),
+        _ptr(next_tokens, torch.int32, R, "next_tokens"),
+        _ptr(accept_mask, torch.uint8, R, "accept_mask"),
+        _ptr(converged, torch.uint8, n_canvas, "converged"),
+        _ptr(mean_entropy, torch.float32, n_canvas, "mean_entropy"),
+        _stream(stream))
+    _check(st)
+
+
+def dg_q_sample(x0: torch.Tensor, n_canvas: int, C: int, V: int, kappa: torch.Tensor, seed: int,
+                xt: torch.Tensor, stream=None) -> None:
+    R = n_canvas * C
+    st = load().dg_q_sample(
+        _ptr(x0, torch.int32, R, "x0"), n_canvas, C, V,
+        _ptr(kappa, torch.float32, n_canvas, "kappa"),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(xt, torch.int32, R, "xt"), _stream(stream))
+    _check(st)

@@ -1,0 +1,173 @@
+// C ABI of libdg.so: host-side validation, workspace sizing and launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dg_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dg_status fail(dg_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dg_status fail(dg_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dg_status hip_fail(hipError_t e, const char* what) {
+  return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void split_seed(uint64_t seed, uint32_t* k0, uint32_t* k1) {
+  *k0 = (uint32_t)(seed & 0xFFFFFFFFull);
+  *k1 = (uint32_t)(seed >> 32);
+}
+
+dg_status check_canvas(int n_canvas, int C) {
+  if (n_canvas < 1 || n_canvas > DG_MAX_CANVASES)
+    return fail(DG_ERR_INVALID_ARG, "n_canvas=%d outside [1, %d]", n_canvas, DG_MAX_CANVASES);
+  if (C != DG_CANVAS) return fail(DG_ERR_UNSUPPORTED, "C=%d: only C=%d is supported", C, DG_CANVAS);
+  return DG_OK;
+}
+
+dg_status check_vocab_shape(int n_canvas, int C, int V, int d) {
+  dg_status s = check_canvas(n_canvas, C);
+  if (s != DG_OK) return s;
+  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
+  if (d < 1 || d > DG_MAX_D) return fail(DG_ERR_INVALID_ARG, "d=%d outside [1, %d]", d, DG_MAX_D);
+  if (d % 64 != 0) return fail(DG_ERR_UNSUPPORTED, "d=%d: d must be a multiple of 64", d);
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_UNSUPPORTED: return "unsupported";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* dg_last_error(void) { return g_err; }
+
+size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d) {
+  char keep[sizeof(g_err)];
+  memcpy(keep, g_err, sizeof(g_err));
+  const dg_status s = check_vocab_shape(n_canvas, C, V, d);
+  memcpy(g_err, keep, sizeof(g_err));
+  if (s != DG_OK) return 0;
+  return dg::vocab_plan(n_canvas, V, d).bytes;
+}
+
+dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
+                        const float* temperature, const uint8_t* commit, uint64_t seed,
+                        const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
+                        int32_t* gumbel_tok, float* selfcond, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  dg_status s = check_vocab_shape(n_canvas, C, V, d);
+  if (s != DG_OK) return s;
+  if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
+    return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(E) || !aligned16(h))
+    return fail(DG_ERR_INVALID_ARG, "E and h must be 16-byte aligned");
+  if (selfcond && !aligned16(selfcond))
+    return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
+  const dg::VocabPlan plan = dg::vocab_plan(n_canvas, V, d);
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                plan.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  dg::VocabArgs a{};
+  a.E = E;
+  a.h = h;
+  a.n_canvas = n_canvas;
+  a.V = V;
+  a.d = d;
+  a.temperature = temperature;
+  a.commit = commit;
+  split_seed(seed, &a.k0, &a.k1);
+  a.step = step;
+  a.lse = lse;
+  a.entropy = entropy;
+  a.argmax_tok = argmax_tok;
+  a.gumbel_tok = gumbel_tok;
+  a.selfcond = selfcond;
+  const hipError_t e = dg::vocab_pass_launch(a, plan, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
+  return DG_OK;
+}
+
+dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
+                            const int32_t* gumbel_tok, const uint8_t* commit, int n_canvas, int C,
+                            int V, float entropy_budget, float confidence_threshold,
+                            int stability_threshold, uint64_t seed, const int32_t* step,
+                            int32_t* prev_argmax, int32_t* stable_count, int32_t* next_tokens,
+                            uint8_t* accept_mask, uint8_t* converged, float* mean_entropy,
+                            void* stream) {
+  g_err[0] = 0;
+  dg_status s = check_canvas(n_canvas, C);
+  if (s != DG_OK) return s;
+  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
+  if (!entropy || !argmax_tok || !gumbel_tok || !step || !prev_argmax || !stable_count ||
+      !next_tokens || !converged)
+    return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!(entropy_budget >= 0.0f) || !isfinite(entropy_budget))
+    return fail(DG_ERR_INVALID_ARG, "entropy_budget must be finite and >= 0");
+  if (!isfinite(confidence_threshold))
+    return fail(DG_ERR_INVALID_ARG, "confidence_threshold must be finite");
+  if (stability_threshold < 1)
+    return fail(DG_ERR_INVALID_ARG, "stability_threshold must be >= 1");
+  dg::AcceptArgs a{};
+  a.entropy = entropy;
+  a.argmax_tok = argmax_tok;
+  a.gumbel_tok = gumbel_tok;
+  a.commit = commit;
+  a.n_canvas = n_canvas;
+  a.V = V;
+  a.budget = entropy_budget;
+  a.confidence = confidence_threshold;
+  a.stability = stability_threshold;
+  split_seed(seed, &a.k0, &a.k1);
+  a.step = step;
+  a.prev_argmax = prev_argmax;
+  a.stable_count = stable_count;
+  a.next_tokens = next_tokens;
+  a.accept_mask = accept_mask;
+  a.converged = converged;
+  a.mean_entropy = mean_entropy;
+  const hipError_t e = dg::accept_renoise_launch(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "accept/renoise launch");
+  return DG_OK;
+}
+
+dg_status dg_q_sample(const int32_t* x0, int n_canvas, int C, int V, const float* kappa,
+                      uint64_t seed, int32_t* xt, void* stream) {
+  g_err[0] = 0;
+  dg_status s = check_canvas(n_canvas, C);
+  if (s != DG_OK) return s;
+  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
+  if (!x0 || !kappa || !xt) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((const void*)x0 == (const void*)xt) return fail(DG_ERR_INVALID_ARG, "xt may not alias x0");
+  uint32_t k0, k1;
+  split_seed(seed, &k0, &k1);
+  const hipError_t e = dg::q_sample_launch(x0, n_canvas, V, kappa, k0, k1, xt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "q_sample launch");
+  return DG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Device-side helpers for the gfx950 kernels: vector types, MFMA accumulator layout,
+// Philox4x32-10, the noise maps, bf16 packing and wave64 reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Stream tags of the Philox counters (fourth counter word).
+constexpr uint32_t kTagGumbel = 0x47554D42u;
+constexpr uint32_t kTagRenoise = 0x52454E4Fu;
+constexpr uint32_t kTagQSample = 0x51534D50u;
+
+// ---------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64-bit
+// multiplications by fixed odd constants, the high halves mixed into the other two words
+// with the round key; the key advances by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
+    u32x4 n;
+    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.y = (uint32_t)p1;
+    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.w = (uint32_t)p0;
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Uniform token in [0, V): floor(x * V / 2^32).
+__device__ __forceinline__ int uniform_token(uint32_t x, uint32_t V) {
+  return (int)__umulhi(x, V);
+}
+
+// Hardware base-2 log / exp (v_log_f32, v_exp_f32).
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Gumbel noise in base-2 units, g * log2(e) = -log2(-ln u), for the 32-bit word x with
+// u = ((x >> 9) + 0.5) 2^-23.  -ln u is taken from w = 1 - u (exact in fp32) by its series
+// when w < 1/16, so that draws near u = 1 (the large Gumbel values that decide the sample)
+// keep full relative precision; otherwise from the hardware log2.
+__device__ __forceinline__ float gumbel2_from_word(uint32_t x) {
+  const float u = ((float)(x >> 9) + 0.5f) * 0x1p-23f;
+  const float w = ((float)((~x) >> 9) + 0.5f) * 0x1p-23f;
+  const float series =
+      w * (1.0f + w * (0.5f + w * (0.33333333f + w * (0.25f + w * (0.2f + w * 0.16666667f)))));
+  const float direct = -hw_log2(u) * kLn2;
+  const float e = (w < 0.0625f) ? series : direct;
+  return -hw_log2(e);
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 packing, round to nearest even (inputs finite).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------------------
+// MFMA v_mfma_f32_32x32x16_bf16.  Operand fragments: lane l holds 8 consecutive K values of
+// row (l % 32) of A (M x K) and of column (l % 32) of B (K x N), K half (l / 32).  The same
+// K slots are used for A and B, so the product is the full K = 16 sum.
+// Accumulator: lane l, element i holds D[m][n] with n = l % 32 and
+// m = 8 (i / 4) + 4 (l / 32) + (i % 4).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ int acc32_m(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave64 reductions.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+
+// (value, index) pair: larger value wins, ties go to the smaller index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+// Online-softmax partial in base-2 units: max m, l = sum 2^(z-m), a = sum 2^(z-m) (z-m).
+__device__ __forceinline__ void lse_merge(float& m, float& l, float& a, float m2, float l2,
+                                          float a2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;  // both empty
+  const float d1 = m - M, d2 = m2 - M;
+  const float s1 = (m == -INFINITY) ? 0.0f : hw_exp2(d1);
+  const float s2 = (m2 == -INFINITY) ? 0.0f : hw_exp2(d2);
+  const float t1 = (m == -INFINITY) ? 0.0f : s1 * (a + d1 * l);
+  const float t2 = (m2 == -INFINITY) ? 0.0f : s2 * (a2 + d2 * l2);
+  l = s1 * l + s2 * l2;
+  a = t1 + t2;
+  m = M;
+}
+
+}  // namespace dg

@@ -1,0 +1,85 @@
+// Internal host/device interfaces shared by the translation units of libdg.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dg.h"
+
+namespace dg {
+
+// Arguments of one vocabulary pass (device pointers).
+struct VocabArgs {
+  const uint16_t* E;
+  const uint16_t* h;
+  int n_canvas;
+  int V;
+  int d;
+  const float* temperature;
+  const uint8_t* commit;
+  uint32_t k0, k1;  // Philox key
+  const int32_t* step;
+  float* lse;
+  float* entropy;
+  int32_t* argmax_tok;
+  int32_t* gumbel_tok;
+  float* selfcond;
+};
+
+// Workspace carve-up.
+struct VocabWs {
+  float* t_m;     // [n_tiles][R] tile max of z * log2(e)
+  float* t_l;     // [n_tiles][R] sum 2^(z2 - m)
+  float* t_a;     // [n_tiles][R] sum 2^(z2 - m) (z2 - m)
+  float* t_amv;   // [n_tiles][R] argmax logit
+  int* t_ami;     // [n_tiles][R] argmax index
+  float* t_gv;    // [n_tiles][R] Gumbel key (base-2 units)
+  int* t_gi;      // [n_tiles][R] Gumbel index
+  float* prob;    // [R][vpad] 2^(z2 - m_tile), or null when no expectation is asked for
+  float* row_m;   // [R] row max (base-2 units)
+  float* row_linv;  // [R] 1 / sum
+  float* accp;    // [n_split][R][d] expectation partials
+  int n_tiles;
+  size_t vpad;
+  int n_split;
+};
+
+struct VocabPlan {
+  size_t R;
+  int n_tiles;
+  size_t vpad;
+  int ds;
+  int n_split;
+  size_t off_tstat, off_prob, off_row, off_accp;
+  size_t bytes;
+};
+
+VocabPlan vocab_plan(int n_canvas, int V, int d);
+hipError_t vocab_pass_launch(const VocabArgs& a, const VocabPlan& p, void* workspace,
+                             hipStream_t stream);
+
+struct AcceptArgs {
+  const float* entropy;
+  const int32_t* argmax_tok;
+  const int32_t* gumbel_tok;
+  const uint8_t* commit;
+  int n_canvas;
+  int V;
+  float budget;
+  float confidence;
+  int stability;
+  uint32_t k0, k1;
+  const int32_t* step;
+  int32_t* prev_argmax;
+  int32_t* stable_count;
+  int32_t* next_tokens;
+  uint8_t* accept_mask;
+  uint8_t* converged;
+  float* mean_entropy;
+};
+hipError_t accept_renoise_launch(const AcceptArgs& a, hipStream_t stream);
+
+hipError_t q_sample_launch(const int32_t* x0, int n_canvas, int V, const float* kappa,
+                           uint32_t k0, uint32_t k1, int32_t* xt, hipStream_t stream);
+
+}  // namespace dg

@@ -1,0 +1,108 @@
+"""Device-side buffers and one-call wrappers around the C entry points.
+
+Allocation of inputs, outputs, state and workspace with torch (device memory only); every
+computation is a libdg.so call.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """bf16 bit patterns (uint16) -> device int16 tensor holding the same bytes."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+@dataclass
+class VocabBuffers:
+    n_canvas: int
+    V: int
+    d: int
+    E: torch.Tensor
+    h: torch.Tensor
+    temperature: torch.Tensor
+    commit: Optional[torch.Tensor]
+    step: torch.Tensor
+    lse: torch.Tensor
+    entropy: torch.Tensor
+    argmax_tok: torch.Tensor
+    gumbel_tok: torch.Tensor
+    selfcond: Optional[torch.Tensor]
+    workspace: torch.Tensor
+    # sampler state and outputs
+    prev_argmax: torch.Tensor
+    stable_count: torch.Tensor
+    next_tokens: torch.Tensor
+    accept_mask: torch.Tensor
+    converged: torch.Tensor
+    mean_entropy: torch.Tensor
+    C: int = B.DG_CANVAS
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def R(self) -> int:
+        return self.n_canvas * self.C
+
+
+def allocate(n_canvas: int, V: int, d: int, E: torch.Tensor, h: torch.Tensor,
+             temperature, commit, step, want_selfcond: bool = True,
+             sentinel: float = float("nan"), device="cuda") -> VocabBuffers:
+    R = n_canvas * B.DG_CANVAS
+    f32 = dict(dtype=torch.float32, device=device)
+    i32 = dict(dtype=torch.int32, device=device)
+    u8 = dict(dtype=torch.uint8, device=device)
+    ws_bytes = B.dg_vocab_pass_workspace_size(n_canvas, B.DG_CANVAS, V, d)
+    if ws_bytes == 0:
+        raise ValueError(f"unsupported shape n={n_canvas} V={V} d={d}")
+    return VocabBuffers(
+        n_canvas=n_canvas, V=V, d=d, E=E, h=h,
+        temperature=torch.as_tensor(np.asarray(temperature, np.float32)).to(device),
+        commit=None if commit is None else torch.as_tensor(np.asarray(commit, np.uint8)).to(device),
+        step=torch.as_tensor(np.asarray(step, np.int32)).to(device),
+        lse=torch.full((R,), sentinel, **f32),
+        entropy=torch.full((R,), sentinel, **f32),
+        argmax_tok=torch.full((R,), -7, **i32),
+        gumbel_tok=torch.full((R,), -7, **i32),
+        selfcond=torch.full((R, d), sentinel, **f32) if want_selfcond else None,
+        workspace=torch.empty(ws_bytes, **u8),
+        prev_argmax=torch.full((R,), -1, **i32),
+        stable_count=torch.zeros(n_canvas, **i32),
+        next_tokens=torch.full((R,), -7, **i32),
+        accept_mask=torch.full((R,), 7, **u8),
+        converged=torch.full((n_canvas,), 7, **u8),
+        mean_entropy=torch.full((n_canvas,), sentinel, **f32))
+
+
+def from_workload(wl, want_selfcond: bool = True, device="cuda", E: Optional[torch.Tensor] = None,
+                  commit_any: Optional[bool] = None) -> VocabBuffers:
+    E_t = bf16_tensor(wl.E, device) if E is None else E
+    commit = wl.commit if (commit_any if commit_any is not None else bool(wl.commit.any())) else None
+    return allocate(wl.n_canvas, wl.V, wl.d, E_t, bf16_tensor(wl.h, device), wl.temperature,
+                    commit, wl.step, want_selfcond=want_selfcond, device=device)
+
+
+def vocab_pass(b: VocabBuffers, seed: int, stream=None) -> None:
+    B.dg_vocab_pass(b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step,
+                    b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace,
+                    stream=stream)
+
+
+def accept_renoise(b: VocabBuffers, budget: float, confidence: float, stability: int, seed: int,
+                   stream=None) -> None:
+    B.dg_accept_renoise(b.entropy, b.argmax_tok, b.gumbel_tok, b.commit, b.n_canvas, b.C, b.V,
+                        budget, confidence, stability, seed, b.step, b.prev_argmax,
+                        b.stable_count, b.next_tokens, b.accept_mask, b.converged,
+                        b.mean_entropy, stream=stream)
+
+
+def denoise_step(b: VocabBuffers, budget: float, confidence: float, stability: int, seed: int,
+                 stream=None) -> None:
+    """One step of the hot path: vocabulary pass, then accept/renoise/convergence."""
+    vocab_pass(b, seed, stream)
+    accept_renoise(b, budget, confidence, stability, seed, stream)

@@ -1,0 +1,147 @@
+/* dg.h -- C ABI of libdg.so: the per-step hot path of uniform-state block-diffusion
+ * decoding over 256-position canvases with a tied embedding, for AMD MI355X (gfx950).
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *  [TR]   "DiffusionGemma Technical Report -- part 2/6": sec. 2.1.1 eq. (1) forward process,
+ *         sec. 3.2 eq. (5)-(6) denoising iteration, sec. 3.3 entropy-bounded sampler,
+ *         temperature annealing and adaptive stopping.
+ *  [EXP]  "DiffusionGemma Explained": "Sampling" (temperature, entropy, low-entropy prefix,
+ *         renoise, early stop), "Lazy Sampling", tied embeddings and self-conditioning.
+ *  [VLLM] "DiffusionGemma: the first dLLM natively supported in vLLM": the sampler step
+ *         (Gumbel-max candidate, entropy bound, renoise, argmax record, convergence) and
+ *         per-request state kept in preallocated GPU tensors.
+ *  [LITE] "DiffusionGemma-Lite DIFFUSION.html": closed-form forward corruption (q_sample),
+ *         chunked p@E and chunked logsumexp (prior art for the split-vocabulary combine).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns every buffer; the
+ *    library keeps no pointer past the call and allocates nothing.  Buffers must stay valid
+ *    until the work queued on `stream` has completed.
+ *  - Work is queued on `stream` (a hipStream_t; 0 = the null stream) and the call returns
+ *    without waiting for it.  No call synchronises the device.
+ *  - Arguments are validated on the host before anything is queued.  On a validation error
+ *    nothing is queued and no output is written; dg_last_error() describes the error.
+ *  - Values the host cannot check without a device read (non-finite E or h, temperature <= 0,
+ *    token ids outside [0, V)) give unspecified outputs but never out-of-bounds accesses
+ *    of the caller's buffers.
+ *  - Layouts: bf16 is IEEE binary32 truncated to its top 16 bits, stored as uint16_t.
+ *    Row r = c * C + i is position i of canvas c.  All matrices are row-major.
+ *  - Random numbers: Philox4x32-10 (Salmon et al., SC'11) with key (seed & 0xffffffff,
+ *    seed >> 32).  Counters: Gumbel noise of (row r, vocab v) at step s: (v >> 2, r, s,
+ *    0x47554D42), word v & 3; renoise token of row r at step s: (0, r, s, 0x52454E4F),
+ *    word 0; q_sample of row r: (0, r, 0, 0x51534D50), words 0 (keep test) and 1 (token).
+ *    Uniform in (0,1): u = ((x >> 9) + 0.5) * 2^-23.  Uniform token: (x * V) >> 32.
+ *  - The library is thread-safe; calls on different streams may overlap.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, non-finite scalar */
+  DG_ERR_UNSUPPORTED = 2, /* valid but not implemented (C != 256, d % 64 != 0, ...) */
+  DG_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than dg_vocab_pass_workspace_size */
+  DG_ERR_HIP = 4          /* a HIP runtime call failed; see dg_last_error() */
+} dg_status;
+
+/* Size limits checked by every entry point. */
+#define DG_CANVAS 256        /* positions per canvas (the only supported C) */
+#define DG_MAX_D 8192        /* largest hidden width */
+#define DG_MAX_CANVASES 4096 /* largest number of canvases per call */
+
+/* Bytes of device workspace dg_vocab_pass needs for this shape ([host], pure function;
+ * returns 0 for a shape dg_vocab_pass would reject). */
+size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d);
+
+/* dg_vocab_pass -- the fused vocabulary pass of one denoising step.
+ *
+ * For each row r (canvas c = r / C) with logits S[r, v] = sum_k h[r, k] E[v, k] (the tied
+ * embedding used as the unembedding, [TR] eq. (5); [EXP] tied embeddings) and tempered
+ * logits z = S / temperature[c] ([TR] eq. (6); [EXP] "Apply temperature"):
+ *   lse[r]        = log sum_v exp(z_v)
+ *   entropy[r]    = -sum_v p_v log p_v,  p = softmax(z)            ([EXP] "Compute entropy")
+ *   argmax_tok[r] = smallest v attaining max_v S[r, v]              ([VLLM] clean argmax)
+ *   gumbel_tok[r] = smallest v attaining max_v (z_v + g_v), g = -ln(-ln u) with u from the
+ *                   Gumbel counter of (r, v, step[c])                ([VLLM] Gumbel-max)
+ *   selfcond[r,:] = sum_v p_v E[v, :]                    ([TR] eq. (6), the argument of FFW)
+ * The [R, V] logits are never written to memory.  For a commit canvas (commit[c] != 0) only
+ * argmax_tok is written; its rows of lse, entropy, gumbel_tok and selfcond are untouched.
+ *
+ *  E            [V, d] bf16, read only.
+ *  h            [n_canvas * C, d] bf16 final hidden states, read only.
+ *  n_canvas     1 .. DG_MAX_CANVASES.   C: must be DG_CANVAS.
+ *  V            1 .. 2^30.   d: 64 .. DG_MAX_D, multiple of 64.
+ *  temperature  [n_canvas] fp32, > 0.
+ *  commit       [n_canvas] uint8 or NULL (no canvas commits).
+ *  seed         Philox key.   step: [n_canvas] int32 step ids (third Gumbel counter word).
+ *  lse          [R] fp32 or NULL.    entropy: [R] fp32 (nats).
+ *  argmax_tok   [R] int32.           gumbel_tok: [R] int32.
+ *  selfcond     [R, d] fp32 or NULL (then the expectation is not computed).
+ *  workspace    device scratch of at least dg_vocab_pass_workspace_size(n_canvas, C, V, d)
+ *               bytes; its contents on entry do not matter and are clobbered.
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP. */
+dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
+                        const float* temperature, const uint8_t* commit, uint64_t seed,
+                        const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
+                        int32_t* gumbel_tok, float* selfcond, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* dg_accept_renoise -- per-canvas acceptance, renoising and convergence of one step.
+ *
+ * For a canvas that does not commit ([TR] sec. 3.3 "Entropy-bounded token refinement",
+ * "Adaptive stopping heuristic"; [EXP] "Keep a low-entropy prefix and renoise the rest",
+ * "Check for early stopping"; [VLLM] sampler step):
+ *   order its C positions by (entropy, position) ascending; position of rank k is accepted
+ *   iff the entropies of ranks 0..k-1 sum to <= entropy_budget (rank 0 always accepted);
+ *   next_tokens = accepted ? gumbel_tok : uniform token from the renoise counter (r, step[c]);
+ *   stable = (argmax_tok == prev_argmax at every position); stable_count = stable ?
+ *   stable_count + 1 : 0; prev_argmax = argmax_tok; mean_entropy = mean of the C entropies;
+ *   converged = stable_count >= stability_threshold && mean_entropy < confidence_threshold.
+ *   The prefix sums and the mean are taken in fp64.
+ * A commit canvas ([VLLM] commit emits the clean argmax): next_tokens = argmax_tok,
+ * accept_mask = 1, prev_argmax = -1, stable_count = 0, converged = 0, mean_entropy untouched.
+ *
+ *  entropy, argmax_tok, gumbel_tok  [R] inputs as produced by dg_vocab_pass (entropy and
+ *               gumbel_tok are not read for commit canvases).
+ *  commit       [n_canvas] uint8 or NULL.     V: vocabulary size (renoise range).
+ *  entropy_budget >= 0 and finite;  confidence_threshold finite;  stability_threshold >= 1.
+ *  prev_argmax  [R] int32 in/out (-1 = no previous canvas).  stable_count: [n_canvas] in/out.
+ *  next_tokens  [R] int32 out.   accept_mask: [R] uint8 out or NULL.
+ *  converged    [n_canvas] uint8 out.   mean_entropy: [n_canvas] fp32 out or NULL.
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
+                            const int32_t* gumbel_tok, const uint8_t* commit, int n_canvas, int C,
+                            int V, float entropy_budget, float confidence_threshold,
+                            int stability_threshold, uint64_t seed, const int32_t* step,
+                            int32_t* prev_argmax, int32_t* stable_count, int32_t* next_tokens,
+                            uint8_t* accept_mask, uint8_t* converged, float* mean_entropy,
+                            void* stream);
+
+/* dg_q_sample -- closed-form forward corruption ([TR] sec. 2.1.1 eq. (1); [LITE] forward
+ * process, one draw, never iterating the chain): row r of canvas c keeps x0[r] iff
+ * (w0 >> 8) < floor(kappa[c] * 2^24), else takes the uniform token of w1, with (w0, w1)
+ * the q_sample counter words of r.  P(xt = x0) = kappa + (1 - kappa) / V up to the 24-bit
+ * quantisation of kappa.
+ *  x0     [n_canvas * C] int32 clean tokens.   kappa: [n_canvas] fp32 in [0, 1].
+ *  xt     [n_canvas * C] int32 out (may not alias x0).
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+dg_status dg_q_sample(const int32_t* x0, int n_canvas, int C, int V, const float* kappa,
+                      uint64_t seed, int32_t* xt, void* stream);
+
+/* Static text of a status code ([host]). */
+const char* dg_status_string(dg_status s);
+/* Message of the last error raised on the calling host thread ([host], thread-local; "" if
+ * none).  Valid until the next dg_* call on that thread. */
+const char* dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H_ */

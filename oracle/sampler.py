@@ -27,6 +27,7 @@ Margins reported for the parity tests:
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -85,7 +86,7 @@ def accept_renoise(entropy, argmax_tok, gumbel_tok, commit, n_canvas: int, C: in
         same = bool(np.all(am[rows] == prev[rows]))
         cnt[c] = cnt[c] + 1 if same else 0
         prev[rows] = am[rows]
-        meanH[c] = float(np.sum(h)) / C
+        meanH[c] = math.fsum(h) / C
         conv[c] = 1 if (cnt[c] >= stability and meanH[c] < confidence) else 0
         # margins
         for i in range(C):

@@ -1,0 +1,122 @@
+"""The C-ABI library loads without a GPU, exports every symbol include/dg.h declares, and
+rejects invalid arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "denoise_step_sampler_amd", "libdg.so")
+HDR = os.path.join(ROOT, "include", "dg.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdg.so not built")
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_0-9]+)\s*\(", text)))
+
+
+def _lib():
+    import torch  # noqa: F401  (share torch's HIP runtime)
+    from denoise_step_sampler_amd import binding
+    return binding.load(LIB)
+
+
+def test_header_symbols_exported():
+    decl = _declared()
+    assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_accept_renoise",
+                         "dg_q_sample", "dg_status_string", "dg_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [s for s in decl if s not in exported]
+    assert not missing, missing
+    lib = _lib()
+    for s in decl:
+        assert hasattr(lib, s)
+
+
+def test_workspace_size_pure_host():
+    lib = _lib()
+    f = lib.dg_vocab_pass_workspace_size
+    assert f(1, 256, 4096, 256) > 0
+    assert f(32, 256, 262144, 2816) > f(1, 256, 262144, 2816) > 0
+    assert f(1, 128, 4096, 256) == 0      # C != 256
+    assert f(1, 256, 4096, 96) == 0       # d % 64
+    assert f(0, 256, 4096, 256) == 0
+    assert f(1, 256, 0, 256) == 0
+    assert f(1, 256, 4096, 8192 + 64) == 0
+
+
+def _vp(lib, **kw):
+    args = dict(E=1 << 20, h=1 << 20, n=1, C=256, V=4096, d=256, T=1 << 20, commit=None, seed=0,
+                step=1 << 20, lse=None, H=1 << 20, am=1 << 20, gm=1 << 20, sc=None, ws=1 << 20,
+                wsb=1 << 40, stream=None)
+    args.update(kw)
+    return lib.dg_vocab_pass(args["E"], args["h"], args["n"], args["C"], args["V"], args["d"],
+                             args["T"], args["commit"], args["seed"], args["step"], args["lse"],
+                             args["H"], args["am"], args["gm"], args["sc"], args["ws"],
+                             args["wsb"], args["stream"])
+
+
+def test_vocab_pass_validation_errors():
+    """Every case fails validation, so no pointer is dereferenced and no kernel is queued."""
+    from denoise_step_sampler_amd.binding import (DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED,
+                                                  DG_ERR_WORKSPACE)
+    lib = _lib()
+    assert _vp(lib, E=None) == DG_ERR_INVALID_ARG
+    assert _vp(lib, H=None) == DG_ERR_INVALID_ARG
+    assert _vp(lib, C=128) == DG_ERR_UNSUPPORTED
+    assert b"C=128" in lib.dg_last_error()
+    assert _vp(lib, d=96) == DG_ERR_UNSUPPORTED
+    assert _vp(lib, n=0) == DG_ERR_INVALID_ARG
+    assert _vp(lib, V=0) == DG_ERR_INVALID_ARG
+    assert _vp(lib, E=(1 << 20) + 2) == DG_ERR_INVALID_ARG          # misaligned
+    assert _vp(lib, ws=None) == DG_ERR_WORKSPACE
+    assert _vp(lib, wsb=16) == DG_ERR_WORKSPACE
+    assert b"needed" in lib.dg_last_error()
+    assert lib.dg_status_string(DG_ERR_WORKSPACE) == b"workspace too small"
+
+
+def test_accept_and_qsample_validation_errors():
+    from denoise_step_sampler_amd.binding import DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED
+    lib = _lib()
+    P = 1 << 20
+
+    def ar(**kw):
+        a = dict(H=P, am=P, gm=P, commit=None, n=1, C=256, V=100, budget=4.0, conf=0.1, thr=1,
+                 seed=0, step=P, prev=P, cnt=P, nxt=P, acc=None, conv=P, mean=None)
+        a.update(kw)
+        return lib.dg_accept_renoise(a["H"], a["am"], a["gm"], a["commit"], a["n"], a["C"], a["V"],
+                                     a["budget"], a["conf"], a["thr"], a["seed"], a["step"],
+                                     a["prev"], a["cnt"], a["nxt"], a["acc"], a["conv"], a["mean"],
+                                     None)
+    assert ar(budget=-1.0) == DG_ERR_INVALID_ARG
+    assert ar(budget=float("nan")) == DG_ERR_INVALID_ARG
+    assert ar(budget=float("inf")) == DG_ERR_INVALID_ARG
+    assert ar(conf=float("nan")) == DG_ERR_INVALID_ARG
+    assert ar(thr=0) == DG_ERR_INVALID_ARG
+    assert ar(prev=None) == DG_ERR_INVALID_ARG
+    assert ar(C=255) == DG_ERR_UNSUPPORTED
+    assert ar(V=0) == DG_ERR_INVALID_ARG
+    q = lib.dg_q_sample
+    assert q(P, 1, 256, 10, P, 0, P, None) == DG_ERR_INVALID_ARG     # xt aliases x0
+    assert q(P, 1, 256, 10, None, 0, P + 4096, None) == DG_ERR_INVALID_ARG
+    assert q(P, 1, 256, 0, P, 0, P + 4096, None) == DG_ERR_INVALID_ARG
+    assert q(P, 5000, 256, 10, P, 0, P + 4096, None) == DG_ERR_INVALID_ARG
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    import torch  # noqa: F401
+    from denoise_step_sampler_amd import binding
+    saved = binding._lib
+    binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="no CPU fallback"):
+            binding.load(str(tmp_path / "absent.so"))
+    finally:
+        binding._lib = saved

@@ -1,0 +1,148 @@
+"""Parity of dg_vocab_pass (through the C ABI) with the fp64 oracle."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from denoise_step_sampler_amd import synth
+from oracle import vocab_pass as ovp
+from parity import compare_vocab
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from denoise_step_sampler_amd import binding
+    binding.load()
+    yield
+
+
+def _run(wl, seed, want_sc=True, E_t=None):
+    from denoise_step_sampler_amd import runner
+    b = runner.from_workload(wl, want_selfcond=want_sc, E=E_t)
+    runner.vocab_pass(b, seed)
+    torch.cuda.synchronize()
+    return b
+
+
+def _host(b, rows):
+    out = {"lse": b.lse.cpu().numpy()[rows], "entropy": b.entropy.cpu().numpy()[rows],
+           "argmax": b.argmax_tok.cpu().numpy()[rows], "gumbel": b.gumbel_tok.cpu().numpy()[rows]}
+    out["sc"] = None if b.selfcond is None else b.selfcond.cpu().numpy()[rows]
+    return out
+
+
+def _oracle(wl, rows, seed, E64=None, want_sc=True):
+    E64 = ovp.widen_bf16(wl.E) if E64 is None else E64
+    T = np.repeat(wl.temperature, wl.C)
+    cm = np.repeat(wl.commit.astype(bool), wl.C)
+    st = np.repeat(wl.step, wl.C)
+    return ovp.vocab_pass_rows(E64, wl.h, rows, T, cm, seed, st, want_sc=want_sc), cm
+
+
+def _check(wl, seed, rows=None, want_sc=True, E64=None, E_t=None, label=""):
+    _say(f"[vocab_pass] {label} n={wl.n_canvas} V={wl.V} d={wl.d} seed={seed}")
+    b = _run(wl, seed, want_sc, E_t=E_t)
+    rows = np.arange(wl.R) if rows is None else np.asarray(rows)
+    ref, cm = _oracle(wl, rows, seed, E64=E64, want_sc=want_sc)
+    rep = compare_vocab(_host(b, rows), ref, cm)
+    _say("   ", rep)
+    return b, rep
+
+
+def test_tiny_workload_full():
+    wl = synth.workload("tiny")
+    _check(wl, seed=0, label="tiny")
+
+
+@pytest.mark.parametrize("V,d,n", [(1000, 128, 2), (50, 64, 1), (129, 192, 1), (1, 64, 1)])
+def test_ragged_vocab_and_widths(V, d, n):
+    """Vocabulary tails (V % 128 != 0, V < one tile, V = 1), d not a multiple of 128."""
+    wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=3)
+    wl.temperature = np.linspace(0.7, 1.3, n).astype(np.float32)
+    wl.step = np.arange(n, dtype=np.int32) + 5
+    if n > 1:
+        wl.commit = np.array([0, 1] * (n // 2), np.uint8)
+    _check(wl, seed=0xDEADBEEF12345, label="ragged")
+
+
+def test_uniform_and_peaked_rows():
+    """h = 0 rows: entropy = lse = ln V, argmax 0, selfcond = mean E.  Peaked rows: argmax =
+    Gumbel = target, entropy ~ 0."""
+    wl = synth.workload("tiny", V=3000, d=256, seed=4)
+    h = wl.h.copy()
+    h[:64] = 0
+    t = wl.targets[64:128]
+    h[64:128] = synth.round_to_bf16(60.0 * synth.bf16_to_f32(wl.E[t]))
+    wl.h = h
+    b, _ = _check(wl, seed=1, label="uniform+peaked")
+    H = b.entropy.cpu().numpy()
+    assert np.allclose(H[:64], math.log(3000), rtol=1e-5)
+    assert np.all(b.argmax_tok.cpu().numpy()[:64] == 0)
+    mean_e = synth.bf16_to_f32(wl.E).astype(np.float64).mean(0)
+    sc = b.selfcond.cpu().numpy()[:64]
+    assert np.all(np.linalg.norm(sc - mean_e, axis=1) <= 2e-3 * np.linalg.norm(mean_e))
+    assert np.array_equal(b.argmax_tok.cpu().numpy()[64:128], t)
+    assert np.array_equal(b.gumbel_tok.cpu().numpy()[64:128], t)
+
+
+def test_no_selfcond_and_determinism():
+    wl = synth.workload("tiny", V=2000, d=128, n_canvas=2, seed=6)
+    b1 = _run(wl, 9, want_sc=False)
+    b2 = _run(wl, 9, want_sc=True)
+    b3 = _run(wl, 9, want_sc=True)
+    for k in ("lse", "entropy", "argmax_tok", "gumbel_tok"):
+        x1, x2 = getattr(b1, k).cpu().numpy(), getattr(b2, k).cpu().numpy()
+        assert np.array_equal(x1.view(np.uint32), x2.view(np.uint32)), k
+    assert np.array_equal(b2.selfcond.cpu().numpy().view(np.uint32),
+                          b3.selfcond.cpu().numpy().view(np.uint32))
+    b4 = _run(wl, 10, want_sc=False)   # other seed, other samples
+    assert not np.array_equal(b1.gumbel_tok.cpu().numpy(), b4.gumbel_tok.cpu().numpy())
+
+
+def test_lite_workload_sampled_rows():
+    wl = synth.workload("lite")
+    rows = np.random.default_rng(0).choice(wl.R, size=96, replace=False)
+    _check(wl, seed=0, rows=np.sort(rows), label="lite")
+
+
+@pytest.fixture(scope="module")
+def large():
+    _say("[vocab_pass] generating V=262144 d=2816 embedding")
+    E = synth.make_embedding(262144, 2816, seed=0)
+    from denoise_step_sampler_amd import runner
+    E_t = runner.bf16_tensor(E)
+    E64 = ovp.widen_bf16(E)
+    yield E, E_t, E64
+
+
+def test_large_vocab_single_canvas_sampled(large):
+    E, E_t, E64 = large
+    wl = synth.workload("large_v", E=E)
+    rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
+    _check(wl, seed=0, rows=rows, E64=E64, E_t=E_t, label="large_v")
+
+
+def test_batched_serving_step_sampled(large):
+    E, E_t, E64 = large
+    wl = synth.workload("batched", E=E)
+    rng = np.random.default_rng(1)
+    canv = [0, 3, 5, 7, 22, 31]   # 3, 7, 31 commit
+    rows = np.sort(np.concatenate([c * 256 + rng.choice(256, 3, replace=False) for c in canv]))
+    b, rep = _check(wl, seed=0, rows=rows, E64=E64, E_t=E_t, label="batched")
+    assert rep["commit_rows"] == 9
+    # every commit row of every commit canvas untouched except argmax
+    cm = np.repeat(wl.commit.astype(bool), 256)
+    assert np.all(np.isnan(b.entropy.cpu().numpy()[cm]))
+    assert np.all(b.argmax_tok.cpu().numpy() >= 0)
