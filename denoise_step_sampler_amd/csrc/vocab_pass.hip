@@ -29,6 +29,87 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Epilogue helpers of k_vp_tile.  A lane holds one row r and, in four 32x32 accumulator
+// blocks, the logits of vocabulary entries v0 + 32 mb + acc32_m(i, lane).
+__device__ __forceinline__ void blk_argmax_max(const f32x16& s, int vb0, int V, float c2,
+                                               float& bv, int& bi, float& m) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int v = vb0 + 8 * (i >> 2) + (i & 3);
+    if (v < V) {
+      argmax_merge(bv, bi, s[i], v);
+      m = fmaxf(m, s[i] * c2);
+    }
+  }
+}
+
+// Softmax partial, Gumbel candidate and (optionally) unnormalised probabilities of one block.
+__device__ __forceinline__ void blk_softmax_gumbel(const f32x16& s, int vb0, int V, float c2,
+                                                   float m, uint32_t r, uint32_t step,
+                                                   uint32_t k0, uint32_t k1, float* prow,
+                                                   float& ls, float& as, float& gv, int& gi) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int vb = vb0 + 8 * q;
+    const u32x4 wd = philox4x32_10(u32x4{(uint32_t)vb >> 2, r, step, kTagGumbel}, k0, k1);
+    float pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = vb + j;
+      const float z2 = s[4 * q + j] * c2;
+      float p = 0.0f;
+      if (v < V) {
+        const float dz = z2 - m;
+        p = hw_exp2(dz);
+        ls += p;
+        as += p * dz;
+        argmax_merge(gv, gi, z2 + gumbel2_from_word(wd[j]), v);
+      }
+      pv[j] = p;
+    }
+    if (prow != nullptr) *reinterpret_cast<f32x4*>(prow + vb) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+  }
+}
+
+__device__ __forceinline__ void tile_row_epilogue(const f32x16& s0, const f32x16& s1,
+                                                  const f32x16& s2, const f32x16& s3,
+                                                  const VocabArgs& a, const VocabWs& ws, int tile,
+                                                  int r, int v0, int lane, float c2,
+                                                  uint32_t step, bool is_commit, size_t R) {
+  const int vb0 = v0 + 4 * (lane >> 5);
+  float bv = -INFINITY, m = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  blk_argmax_max(s0, vb0, a.V, c2, bv, bi, m);
+  blk_argmax_max(s1, vb0 + 32, a.V, c2, bv, bi, m);
+  blk_argmax_max(s2, vb0 + 64, a.V, c2, bv, bi, m);
+  blk_argmax_max(s3, vb0 + 96, a.V, c2, bv, bi, m);
+  argmax_merge(bv, bi, xor_f(bv, 32), xor_i(bi, 32));
+  const size_t so = (size_t)tile * R + r;
+  if (lane < 32) {
+    ws.t_amv[so] = bv;
+    ws.t_ami[so] = bi;
+  }
+  if (is_commit) return;
+  m = fmaxf(m, xor_f(m, 32));
+  float ls = 0.0f, as = 0.0f, gv = -INFINITY;
+  int gi = 0x7FFFFFFF;
+  float* prow = ws.prob != nullptr ? ws.prob + (size_t)r * ws.vpad : nullptr;
+  blk_softmax_gumbel(s0, vb0, a.V, c2, m, r, step, a.k0, a.k1, prow, ls, as, gv, gi);
+  blk_softmax_gumbel(s1, vb0 + 32, a.V, c2, m, r, step, a.k0, a.k1, prow, ls, as, gv, gi);
+  blk_softmax_gumbel(s2, vb0 + 64, a.V, c2, m, r, step, a.k0, a.k1, prow, ls, as, gv, gi);
+  blk_softmax_gumbel(s3, vb0 + 96, a.V, c2, m, r, step, a.k0, a.k1, prow, ls, as, gv, gi);
+  ls += xor_f(ls, 32);
+  as += xor_f(as, 32);
+  argmax_merge(gv, gi, xor_f(gv, 32), xor_i(gi, 32));
+  if (lane < 32) {
+    ws.t_m[so] = m;
+    ws.t_l[so] = ls;
+    ws.t_a[so] = as;
+    ws.t_gv[so] = gv;
+    ws.t_gi[so] = gi;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // k_vp_tile: logits tile + epilogue.
 // grid (n_tiles, n_canvas), block 256 = 4 waves; wave w owns rows [64w, 64w + 64) of the
@@ -115,80 +196,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_vp_tile(VocabArgs a, VocabWs ws
 
   // --- epilogue: lane holds, for each row block nb, row (64w + 32nb + lane%32) and 64 of the
   // tile's vocabulary entries; lane ^ 32 holds the other 64.
-  const float T = a.temperature[c];
-  const float c2 = kLog2e / T;
+  const float c2 = kLog2e / a.temperature[c];
   const uint32_t step = (uint32_t)a.step[c];
   const size_t R = (size_t)a.n_canvas * DG_CANVAS;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = row0 + 64 * w + 32 * nb + fr;
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 32 * mb + acc32_m(i, lane);
-        if (v < a.V) argmax_merge(bv, bi, acc[mb][nb][i], v);
-      }
-    argmax_merge(bv, bi, xor_f(bv, 32), xor_i(bi, 32));
-    const size_t so = (size_t)tile * R + r;
-    if (lane < 32) {
-      ws.t_amv[so] = bv;
-      ws.t_ami[so] = bi;
-    }
-    if (is_commit) continue;
-
-    float m = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = v0 + 32 * mb + acc32_m(i, lane);
-        if (v < a.V) m = fmaxf(m, acc[mb][nb][i] * c2);
-      }
-    m = fmaxf(m, xor_f(m, 32));
-    float ls = 0.0f, as = 0.0f;
-    float gv = -INFINITY;
-    int gi = 0x7FFFFFFF;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int vb = v0 + 32 * mb + 8 * q + 4 * (lane >> 5);
-        const u32x4 wd = philox4x32_10(u32x4{(uint32_t)vb >> 2, (uint32_t)r, step, kTagGumbel},
-                                       a.k0, a.k1);
-        float pv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = vb + j;
-          const float z2 = acc[mb][nb][4 * q + j] * c2;
-          float p = 0.0f;
-          if (v < a.V) {
-            const float dz = z2 - m;
-            p = hw_exp2(dz);
-            ls += p;
-            as += p * dz;
-            argmax_merge(gv, gi, z2 + gumbel2_from_word(wd[j]), v);
-          }
-          pv[j] = p;
-        }
-        if (ws.prob != nullptr) {
-          *reinterpret_cast<f32x4*>(ws.prob + (size_t)r * ws.vpad + vb) =
-              f32x4{pv[0], pv[1], pv[2], pv[3]};
-        }
-      }
-    ls += xor_f(ls, 32);
-    as += xor_f(as, 32);
-    argmax_merge(gv, gi, xor_f(gv, 32), xor_i(gi, 32));
-    if (lane < 32) {
-      ws.t_m[so] = m;
-      ws.t_l[so] = ls;
-      ws.t_a[so] = as;
-      ws.t_gv[so] = gv;
-      ws.t_gi[so] = gi;
-    }
-  }
+  const int r0 = row0 + 64 * w + fr;
+  tile_row_epilogue(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a, ws, tile, r0, v0, lane, c2,
+                    step, is_commit, R);
+  tile_row_epilogue(acc[0][1], acc[1][1], acc[2][1], acc[3][1], a, ws, tile, r0 + 32, v0, lane,
+                    c2, step, is_commit, R);
 }
 
 // ---------------------------------------------------------------------------------------
