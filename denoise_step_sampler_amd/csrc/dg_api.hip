@@ -2,6 +2,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "dg_internal.h"
@@ -21,6 +22,32 @@ dg_status fail(dg_status s, const char* fmt, ...) {
 
 dg_status hip_fail(hipError_t e, const char* what) {
   return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Path of the vocabulary pass: the fused cooperative kernel when its tiling covers d and the
+// device holds at least one 16-workgroup group per XCD; otherwise the split kernels.
+// DG_VOCAB_PATH=split forces the split kernels (used by the tests to cover both).
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+bool use_fused(int d, int* n_wg) {
+  const char* e = getenv("DG_VOCAB_PATH");
+  if (e != nullptr && strcmp(e, "split") == 0) return false;
+  if (!dg::fused_supported(d)) return false;
+  int n = device_cu_count();
+  if (n <= 0) n = 256;  // sizing without a device: MI355X
+  *n_wg = n;
+  return (n / 8) >= 16;
+}
+
+size_t plan_bytes(int n_canvas, int V, int d) {
+  int n_wg = 0;
+  if (use_fused(d, &n_wg)) return dg::fused_plan(n_canvas, V, d, n_wg).bytes;
+  return dg::vocab_plan(n_canvas, V, d).bytes;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -69,7 +96,7 @@ size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d) {
   const dg_status s = check_vocab_shape(n_canvas, C, V, d);
   memcpy(g_err, keep, sizeof(g_err));
   if (s != DG_OK) return 0;
-  return dg::vocab_plan(n_canvas, V, d).bytes;
+  return plan_bytes(n_canvas, V, d);
 }
 
 dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
@@ -86,10 +113,10 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
     return fail(DG_ERR_INVALID_ARG, "E and h must be 16-byte aligned");
   if (selfcond && !aligned16(selfcond))
     return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
-  const dg::VocabPlan plan = dg::vocab_plan(n_canvas, V, d);
-  if (!workspace || workspace_bytes < plan.bytes)
+  const size_t need = plan_bytes(n_canvas, V, d);
+  if (!workspace || workspace_bytes < need)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
-                plan.bytes);
+                need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   dg::VocabArgs a{};
@@ -107,7 +134,11 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
   a.argmax_tok = argmax_tok;
   a.gumbel_tok = gumbel_tok;
   a.selfcond = selfcond;
-  const hipError_t e = dg::vocab_pass_launch(a, plan, workspace, (hipStream_t)stream);
+  int n_wg = 0;
+  const hipError_t e =
+      use_fused(d, &n_wg)
+          ? dg::fused_launch(a, dg::fused_plan(n_canvas, V, d, n_wg), workspace, (hipStream_t)stream)
+          : dg::vocab_pass_launch(a, dg::vocab_plan(n_canvas, V, d), workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
 }

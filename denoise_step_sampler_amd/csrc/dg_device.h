@@ -26,7 +26,7 @@ constexpr uint32_t kTagQSample = 0x51534D50u;
 // with the round key; the key advances by the Weyl constants between rounds.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll 2
+#pragma unroll 1
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
@@ -101,10 +101,9 @@ __device__ __forceinline__ int xor_i(int v, int m) { return __shfl_xor(v, m, 64)
 
 // (value, index) pair: larger value wins, ties go to the smaller index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
+  const bool take = (v2 > v) | ((v2 == v) & (i2 < i));  // branch-free: selects, no exec masks
+  v = take ? v2 : v;
+  i = take ? i2 : i;
 }
 
 // Online-softmax partial in base-2 units: max m, l = sum 2^(z-m), a = sum 2^(z-m) (z-m).

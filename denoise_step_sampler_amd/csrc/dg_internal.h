@@ -55,6 +55,22 @@ struct VocabPlan {
 };
 
 VocabPlan vocab_plan(int n_canvas, int V, int d);
+
+// Fused cooperative path (vocab_fused.hip).
+struct FusedPlan {
+  int n_wg;       // workgroups launched (one per CU)
+  int per_xcd;    // workgroups per XCD
+  int n_groups;   // groups of 16 workgroups
+  size_t R;
+  int n_tiles;
+  int s_v;        // vocabulary ranges per canvas
+  size_t off_sync, off_ring, off_ring_ref, off_st, off_accp, off_accM;
+  size_t bytes;
+};
+bool fused_supported(int d);
+FusedPlan fused_plan(int n_canvas, int V, int d, int n_wg);
+hipError_t fused_launch(const VocabArgs& a, const FusedPlan& p, void* workspace,
+                        hipStream_t stream);
 hipError_t vocab_pass_launch(const VocabArgs& a, const VocabPlan& p, void* workspace,
                              hipStream_t stream);
 

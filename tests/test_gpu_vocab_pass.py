@@ -1,5 +1,6 @@
 """Parity of dg_vocab_pass (through the C ABI) with the fp64 oracle."""
 import math
+import os
 import sys
 
 import numpy as np
@@ -26,6 +27,21 @@ def _gpu():
     from denoise_step_sampler_amd import binding
     binding.load()
     yield
+
+
+@pytest.fixture(params=["fused", "split"])
+def path(request):
+    """Runs the test through the fused cooperative kernel and through the split kernels."""
+    old = os.environ.get("DG_VOCAB_PATH")
+    if request.param == "split":
+        os.environ["DG_VOCAB_PATH"] = "split"
+    else:
+        os.environ.pop("DG_VOCAB_PATH", None)
+    yield request.param
+    if old is None:
+        os.environ.pop("DG_VOCAB_PATH", None)
+    else:
+        os.environ["DG_VOCAB_PATH"] = old
 
 
 def _run(wl, seed, want_sc=True, E_t=None):
@@ -61,23 +77,24 @@ def _check(wl, seed, rows=None, want_sc=True, E64=None, E_t=None, label=""):
     return b, rep
 
 
-def test_tiny_workload_full():
+def test_tiny_workload_full(path):
     wl = synth.workload("tiny")
-    _check(wl, seed=0, label="tiny")
+    _check(wl, seed=0, label=f"tiny/{path}")
 
 
-@pytest.mark.parametrize("V,d,n", [(1000, 128, 2), (50, 64, 1), (129, 192, 1), (1, 64, 1)])
+@pytest.mark.parametrize("V,d,n", [(1000, 128, 2), (50, 64, 1), (129, 192, 1), (1, 64, 1),
+                                   (1000, 256, 2), (1, 256, 1), (300, 512, 3), (5000, 1024, 2)])
 def test_ragged_vocab_and_widths(V, d, n):
     """Vocabulary tails (V % 128 != 0, V < one tile, V = 1), d not a multiple of 128."""
     wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=3)
     wl.temperature = np.linspace(0.7, 1.3, n).astype(np.float32)
     wl.step = np.arange(n, dtype=np.int32) + 5
     if n > 1:
-        wl.commit = np.array([0, 1] * (n // 2), np.uint8)
+        wl.commit = (np.arange(n) % 2).astype(np.uint8)
     _check(wl, seed=0xDEADBEEF12345, label="ragged")
 
 
-def test_uniform_and_peaked_rows():
+def test_uniform_and_peaked_rows(path):
     """h = 0 rows: entropy = lse = ln V, argmax 0, selfcond = mean E.  Peaked rows: argmax =
     Gumbel = target, entropy ~ 0."""
     wl = synth.workload("tiny", V=3000, d=256, seed=4)
@@ -111,10 +128,36 @@ def test_no_selfcond_and_determinism():
     assert not np.array_equal(b1.gumbel_tok.cpu().numpy(), b4.gumbel_tok.cpu().numpy())
 
 
-def test_lite_workload_sampled_rows():
+def test_lite_workload_sampled_rows(path):
     wl = synth.workload("lite")
     rows = np.random.default_rng(0).choice(wl.R, size=96, replace=False)
-    _check(wl, seed=0, rows=np.sort(rows), label="lite")
+    _check(wl, seed=0, rows=np.sort(rows), label=f"lite/{path}")
+
+
+def test_fused_determinism_and_agreement_with_split():
+    """The fused kernel is bit-reproducible and agrees with the split kernels."""
+    wl = synth.workload("lite", V=20000, d=1024, n_canvas=3, seed=8)
+    wl.commit = np.array([0, 1, 0], np.uint8)
+    os.environ.pop("DG_VOCAB_PATH", None)
+    a = _run(wl, 5)
+    b = _run(wl, 5)
+    for k in ("entropy", "argmax_tok", "gumbel_tok", "selfcond"):
+        x, y = getattr(a, k).cpu().numpy(), getattr(b, k).cpu().numpy()
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), k
+    os.environ["DG_VOCAB_PATH"] = "split"
+    try:
+        c = _run(wl, 5)
+    finally:
+        os.environ.pop("DG_VOCAB_PATH", None)
+    nc = np.repeat(wl.commit == 0, 256)
+    assert np.array_equal(a.argmax_tok.cpu().numpy(), c.argmax_tok.cpu().numpy())
+    ha, hc = a.entropy.cpu().numpy()[nc], c.entropy.cpu().numpy()[nc]
+    assert np.allclose(ha, hc, rtol=1e-4, atol=1e-6)
+    sa, sc = a.selfcond.cpu().numpy()[nc], c.selfcond.cpu().numpy()[nc]
+    rel = np.linalg.norm(sa - sc, axis=1) / np.linalg.norm(sc, axis=1)
+    assert rel.max() < 2e-3
+    same = (a.gumbel_tok.cpu().numpy() == c.gumbel_tok.cpu().numpy())[nc]
+    assert same.mean() > 0.99
 
 
 @pytest.fixture(scope="module")
@@ -127,20 +170,20 @@ def large():
     yield E, E_t, E64
 
 
-def test_large_vocab_single_canvas_sampled(large):
+def test_large_vocab_single_canvas_sampled(large, path):
     E, E_t, E64 = large
     wl = synth.workload("large_v", E=E)
     rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
-    _check(wl, seed=0, rows=rows, E64=E64, E_t=E_t, label="large_v")
+    _check(wl, seed=0, rows=rows, E64=E64, E_t=E_t, label=f"large_v/{path}")
 
 
-def test_batched_serving_step_sampled(large):
+def test_batched_serving_step_sampled(large, path):
     E, E_t, E64 = large
     wl = synth.workload("batched", E=E)
     rng = np.random.default_rng(1)
     canv = [0, 3, 5, 7, 22, 31]   # 3, 7, 31 commit
     rows = np.sort(np.concatenate([c * 256 + rng.choice(256, 3, replace=False) for c in canv]))
-    b, rep = _check(wl, seed=0, rows=rows, E64=E64, E_t=E_t, label="batched")
+    b, rep = _check(wl, seed=0, rows=rows, E64=E64, E_t=E_t, label=f"batched/{path}")
     assert rep["commit_rows"] == 9
     # every commit row of every commit canvas untouched except argmax
     cm = np.repeat(wl.commit.astype(bool), 256)
