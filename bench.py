@@ -59,7 +59,7 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": rows_done / spent, "unit": "canvas-positions/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows_done} non-commit positions of the {wl.name} workload, full vocabulary "
+            "sample": f"{rows_done} non-commit positions (rows) of the {wl.name} workload, full vocabulary "
                       f"(logits, softmax, entropy, argmax, Gumbel, selfcond), fp64 numpy, "
                       f"{spent:.1f}s; bf16->fp64 widening of E ({widen_s:.1f}s) excluded"}
 
@@ -145,7 +145,9 @@ def main() -> int:
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "roofline": {
-            "kernel": "dg_vocab_pass",
+            "kernel": "k_vp_fused (dg_vocab_pass: init + fused kernel + combine)"
+                      if wl.d % 256 == 0 and os.environ.get("DG_VOCAB_PATH") != "split"
+                      else "dg_vocab_pass (split kernels)",
             "bound": "mfma", "achieved": ach_tflops, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": ach_tflops / PEAK_BF16_TFLOPS, "traffic": None,
             "algorithmic_flops_per_launch": flops, "avg_launch_ms": vp_avg},

@@ -41,6 +41,9 @@
 //
 // Jobs: (canvas, vocabulary range) pairs, non-commit canvases first, dealt round-robin to
 // groups.  Commit canvases need only the argmax: no probabilities, no exchange.
+#include <stdlib.h>
+#include <string.h>
+
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -800,8 +803,16 @@ __global__ __launch_bounds__(256) void k_vp_fused_combine(Fused f) {
   }
 }
 
+// Cooperative launch guarantees that the whole grid is resident.  DG_COOPERATIVE=0 uses an
+// ordinary launch instead (one workgroup per CU still fits; waits stay bounded either way),
+// for tools that do not follow cooperative dispatches.
 template <int NCB>
 hipError_t launch_fused(const Fused& f, int n_wg, hipStream_t stream) {
+  const char* e = getenv("DG_COOPERATIVE");
+  if (e != nullptr && strcmp(e, "0") == 0) {
+    hipLaunchKernelGGL(k_vp_fused<NCB>, dim3(n_wg), dim3(512), 0, stream, f);
+    return hipGetLastError();
+  }
   void* args[] = {const_cast<Fused*>(&f)};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_vp_fused<NCB>), dim3(n_wg),
                                     dim3(512), args, 0, stream);
