@@ -64,7 +64,7 @@ struct FusedPlan {
   size_t R;
   int n_tiles;
   int s_v;        // vocabulary ranges per canvas
-  size_t off_sync, off_ring, off_ring_ref, off_st, off_accp, off_accM;
+  size_t off_sync, off_order, off_ring, off_ring_ref, off_st, off_accp, off_accM;
   size_t bytes;
 };
 bool fused_supported(int d);

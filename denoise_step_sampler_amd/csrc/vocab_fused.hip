@@ -13,11 +13,16 @@
 //                        B: acc[256, d/16 slice g] += P_t E_t[:, slice] for the 16 tiles of
 //                           the previous round (bf16 MFMA 16x16x32)
 //
-// Staging: global_load_lds_dwordx4 moves E and h chunks straight into LDS (no staging
-// registers).  The logits operands sit in XOR-swizzled 128-byte rows (conflict-free
+// Staging: every operand moves global -> LDS by LDS DMA (global_load_lds_dwordx4), through
+// three-stage rings, one per role.  The copies are issued in inline assembly and awaited with
+// counted s_waitcnt vmcnt(N): the compiler cannot tell the stages apart and would otherwise
+// hold every LDS read back until all copies in flight (the next stages too) had landed.  Both
+// roles issue their copies in the order they consume them, so an in-order wait never stalls
+// on a later stage.  The logits operands sit in XOR-swizzled 64-byte rows (conflict-free
 // ds_read_b128); the E slice of the expectation sits row-major and is read with the LDS
 // transpose read ds_read_b64_tr_b16, which delivers vocabulary-contiguous operand fragments
-// from d-contiguous rows.
+// from d-contiguous rows; the probability fragments are copied whole (1 KB per wave and row
+// block) and read back contiguously.
 //
 // Probability reference: the A step writes 2^(z2 - ref) with ref = max(M, m_tile), M the
 // group's running row maximum known to this workgroup (B step, same job) and m_tile the tile
@@ -25,19 +30,21 @@
 // maximum stores its largest probability as exactly 1.  The B step rescales a tile only when
 // its ref differs from the group maximum after the round (rare once the maximum has settled);
 // the accumulators are rescaled in fp32 when the maximum grows.
-
+//
 // Roles: each workgroup has 8 waves; waves 0-3 run the A step (logits + epilogue), waves 4-7
 // the B step, so the epilogue's VALU work and the B MFMAs issue side by side on every SIMD.
 // Within a role, waves synchronise through an LDS counter (never the workgroup barrier).
 //
-// Synchronisation across the group: two monotonically increasing counters per group, waves
-// that published a round (A) and waves that consumed one (B); A of round q waits until every B
-// wave finished round q - 2 (two ring slots), B of round q waits until every A wave published
-// round q.  Group members are formed from the hardware XCC id so that all ring traffic stays
-// in one L2; the data is written with plain stores, completed (s_waitcnt) before the counter
-// increment, and read after an L1 invalidate.  Every wait is bounded; on time-out the kernel
-// raises an error flag, every wave leaves, and the combine kernel poisons the outputs (token
-// -1, NaN statistics).
+// Synchronisation across the group: per round parity, a counter of waves that published a
+// round (A) and one of waves that consumed one (B).  A of round q waits until every B wave
+// finished round q - 2 (two ring slots), B of round q waits until every A wave published
+// round q.  Keeping the parities apart makes each count exact: no wave can reach round q + 2
+// of the same parity before the round q it would be confused with has been consumed.  Group
+// members are formed from the hardware XCC id so that all ring traffic stays in one L2; the
+// data is written with plain stores, completed (s_waitcnt) before the counter increment, and
+// read after an L1 invalidate.  Every wait is bounded; on time-out the kernel raises an error
+// flag, every wave leaves, and the combine kernel poisons the outputs (token -1, NaN
+// statistics).
 //
 // Jobs: (canvas, vocabulary range) pairs, non-commit canvases first, dealt round-robin to
 // groups.  Commit canvases need only the argmax: no probabilities, no exchange.
@@ -54,18 +61,29 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kG = 16;          // workgroups per group (one d slice each)
-constexpr int kThreads = 256;   // 4 waves
 constexpr int kBV = 128;        // vocabulary tile
-constexpr int kKC = 64;         // d chunk of the logits contraction (128 bytes per row)
-constexpr int kStageA = (kBV + DG_CANVAS) * 128;  // one A stage: 48 KB
-constexpr int kSmem = 2 * kStageA;                 // 96 KB
+constexpr int kKC = 32;         // d chunk of the logits contraction: 64 bytes per row
+constexpr int kRowA = 2 * kKC;  // bytes of one staged row
+constexpr int kStageA = (kBV + DG_CANVAS) * kRowA;  // one A stage: E chunk + h chunk, 24 KB
+constexpr int kNStage = 3;                           // stages per role ring
+constexpr int kSmemA = kNStage * kStageA;            // 72 KB
+constexpr int kBQ = 32;         // vocabulary rows per B stage (a quarter tile)
 constexpr unsigned kSpinLimit = 1u << 22;
-constexpr int kTileElems = kBV * DG_CANVAS;        // bf16 probability tile: 64 KB
+constexpr int kTileElems = kBV * DG_CANVAS;          // bf16 probability tile: 64 KB
+
+// B stage: E slice [32 rows][32 NCB bytes] (NCB KB), then the probability fragments of the
+// four B waves (4 row blocks x 1 KB each).
+template <int NCB>
+constexpr int b_stage_bytes() {
+  return NCB * 1024 + 16 * 1024;
+}
 
 struct Fused {
   VocabArgs a;
-  unsigned* sync;     // [0, 8) per-XCC slot counters, [8] error flag, [16 + gid] produced,
-                      // [16 + n_groups + gid] consumed
+  unsigned* sync;     // [0, 8) per-XCC slot counters, [8] error flag, [9] non-commit
+                      // canvases, [16 + 4 gid + p] produced and [16 + 4 gid + 2 + p] consumed
+                      // counters of round parity p
+  const int* order;   // [n_canvas] non-commit canvases first, each part in index order
   uint16_t* ring;     // [n_groups][2][kG][kBV * 256]
   float* ring_ref;    // [n_groups][2][kG][256]
   float* st_m;        // [S_v][kG][R] partial statistics
@@ -87,39 +105,253 @@ __device__ __forceinline__ unsigned poll(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void g2l16(const void* g, lds_char* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
 __device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
 // ---------------------------------------------------------------------------------------
-// A step: S^T tile (128 vocab x 256 rows) over all of d.  Wave w owns rows [64w, 64w + 64):
-// acc[mb][nb] is the 32x32 block (vocabulary block mb, row block nb).  LDS stage: E chunk
-// [128 rows][8 x 16 B] then h chunk [256 rows][8 x 16 B]; chunk s of row r sits at slot
-// s ^ (r & 7).
+// LDS DMA.  One instruction: lane l copies the 16 bytes at base + off (off per lane, base
+// wave-uniform) to LDS byte address dst + 16 l (dst wave-uniform, through M0).  The
+// non-temporal form is used for the E stream, which no workgroup of this XCD re-reads soon,
+// so that it does not push the hidden states and the probability ring out of L2.  M0 is free
+// between instructions on gfx9 and later (LDS instructions no longer read it); the one-cycle
+// nop covers the M0 -> LDS DMA hazard.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void stage_a(const uint16_t* E, const uint16_t* h, int V, int d,
-                                        int v0, int row0, int k0, lds_char* st) {
-  // Instruction q of wave w covers rows 32w + 8q + lane/8 (E) and 64w + 8q + lane/8 (h);
-  // the swizzled chunk index depends on lane only, so every address is a per-lane offset plus
-  // a wave-uniform stride.
-  const int lane = threadIdx.x & 63, w = (threadIdx.x >> 6) & 3;
-  const int lr = lane >> 3;
-  const int seg = (lane & 7) ^ (lr & 7);
-  const uint16_t* eb = E + k0 + 8 * seg;
-  const uint16_t* hb = h + (size_t)(row0 + 64 * w + lr) * d + k0 + 8 * seg;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(dst)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(off), "s"(base), "s"(dst)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are outstanding.  Operations
+// complete in issue order, so this waits for everything but the N most recent.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------------------
+// Role barriers: the four A waves (and the four B waves) of a workgroup synchronise through
+// an LDS counter, so that one role never waits for the other.  A wave arrives after its own
+// copies into the stage it is about to read have landed (vm_wait before the call) and after
+// its reads of the stage being refilled were issued; LDS executes a wave's operations in
+// order, so those reads are done before the arrival is counted.  Bounded like the group
+// waits: on time-out the flag `bad` is raised, later barriers stop waiting, and the caller
+// leaves at its next check (the loops keep one exit, which keeps the accumulators in place).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void role_bar(int* ctr, int& gen, unsigned* err, bool& bad) {
+  gen += 4;
+  asm volatile("" ::: "memory");
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  unsigned it = 0;
+  while (!bad && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < gen) {
+    if (++it > kSpinLimit) {
+      atomicOr(err, 4u);
+      bad = true;
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+
+// Bounded wait of one wave until *p >= target.
+__device__ __forceinline__ bool wave_wait(unsigned* p, unsigned target, unsigned* err) {
+  unsigned it = 0;
+  while (poll(p) < target) {
+    if (poll(err) != 0u) return false;
+    if (++it > kSpinLimit) {
+      atomicOr(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
+}
+
+// Publish: every store of this wave completes before the counter moves.
+__device__ __forceinline__ void wave_signal(unsigned* p) {
+  vm_wait<0>();
+  if ((threadIdx.x & 63) == 0) atomicAdd(p, 1u);
+}
+
+// ---------------------------------------------------------------------------------------
+// Jobs.
+// ---------------------------------------------------------------------------------------
+struct Sched {
+  const int* order;
+  int s_v, n_nc, n_tiles, n_jobs, n_heavy, n_groups, member;
+};
+
+struct Job {
+  int c, vr, tb, te, nr;
+  bool commit;
+};
+
+__device__ __forceinline__ Job job_at(const Sched& s, int job) {
+  Job J;
+  const bool nc = job < s.n_heavy;
+  const int k = nc ? job : job - s.n_heavy;
+  const int idx = k / s.s_v;
+  J.vr = k - idx * s.s_v;
+  J.c = s.order[nc ? idx : s.n_nc + idx];
+  J.commit = !nc;
+  J.tb = (int)(((long long)s.n_tiles * J.vr) / s.s_v);
+  J.te = (int)(((long long)s.n_tiles * (J.vr + 1)) / s.s_v);
+  J.nr = (J.te - J.tb + kG - 1) / kG;
+  return J;
+}
+
+// The A role's next logits tile after round r of `job`: the same job's next round, else the
+// first tile of a later job of this group.
+__device__ __forceinline__ bool next_tile(const Sched& s, int job, int tb, int te, int row0,
+                                          int r, int& v0n, int& row0n) {
+  const int t = tb + kG * (r + 1) + s.member;
+  if (t < te) {
+    v0n = t * kBV;
+    row0n = row0;
+    return true;
+  }
+  for (int j = job + s.n_groups; j < s.n_jobs; j += s.n_groups) {
+    const Job J = job_at(s, j);
+    if (J.tb + s.member < J.te) {
+      v0n = (J.tb + s.member) * kBV;
+      row0n = J.c * DG_CANVAS;
+      return true;
+    }
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------------------
+// A step: S^T tile (128 vocab x 256 rows) over all of d, in 32-wide chunks.  Wave w owns
+// rows [64w, 64w + 64): acc[mb][nb] is the 32x32 block (vocabulary block mb, row block nb).
+// LDS stage: E chunk [128 rows][4 x 16 B] then h chunk [256 rows][4 x 16 B]; 16-byte segment
+// s of row r sits at slot s ^ ((r >> 1) & 3), so that eight consecutive rows read at one
+// segment hit eight distinct bank groups.
+// ---------------------------------------------------------------------------------------
+struct ALanes {
+  uint32_t rdE0, rdE1;  // LDS read offsets of this lane's E fragment rows, k steps 0 and 1
+  uint32_t rdH0, rdH1;  // same for the h rows of this wave
+  uint32_t offH;        // DMA: per-lane source offset (bytes) of an h copy
+  uint32_t seg16;       // DMA: swizzled 16-byte segment of this lane
+  int dlrow;            // DMA: row of this lane within a 16-row copy
+};
+
+__device__ __forceinline__ ALanes a_lanes(int w, int d) {
+  ALanes k;
+  const int lane = threadIdx.x & 63, fr = lane & 31, fh = lane >> 5;
+  const int swz = (fr >> 1) & 3;
+  k.rdE0 = fr * kRowA + 16 * ((0 + fh) ^ swz);
+  k.rdE1 = fr * kRowA + 16 * ((2 + fh) ^ swz);
+  k.rdH0 = kBV * kRowA + (64 * w + fr) * kRowA + 16 * ((0 + fh) ^ swz);
+  k.rdH1 = kBV * kRowA + (64 * w + fr) * kRowA + 16 * ((2 + fh) ^ swz);
+  k.dlrow = lane >> 2;
+  k.seg16 = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+  k.offH = (uint32_t)k.dlrow * (2u * (uint32_t)d) + k.seg16;
+  return k;
+}
+
+// Copies of chunk kc of tile (v0, row0) into the stage at LDS address dst: wave w moves E
+// rows [32w, 32w + 32) (clamped to V - 1 past the vocabulary) and its own h rows.
+// Six DMA instructions per wave.
+__device__ __forceinline__ void a_issue(const uint16_t* E, const uint16_t* h, int V, int d,
+                                        int v0, int row0, int kc, uint32_t dst, int w,
+                                        const ALanes& k) {
+  const uint32_t pitch = 2u * (uint32_t)d;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {  // E: 1024 chunks, 16 instructions
-    int v = v0 + 32 * w + 8 * q + lr;
-    v = v < V ? v : V - 1;
-    g2l16(eb + (size_t)v * d, st + 1024 * (4 * w + q));
+  for (int j = 0; j < 2; ++j) {
+    const int rb = v0 + 32 * w + 16 * j;
+    const int br = min(rb, V - 1);
+    const int rv = min(rb + k.dlrow, V - 1);
+    dma16_nt(E + (size_t)br * d + kc * kKC, (uint32_t)(rv - br) * pitch + k.seg16,
+             dst + 1024u * (uint32_t)(2 * w + j));
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q)  // h: 2048 chunks, 32 instructions
-    g2l16(hb + (size_t)(8 * q) * d, st + kBV * 128 + 1024 * (8 * w + q));
+  for (int j = 0; j < 4; ++j)
+    dma16(h + (size_t)(row0 + 64 * w + 16 * j) * d + kc * kKC, k.offH,
+          dst + (uint32_t)(kBV * kRowA) + 1024u * (uint32_t)(4 * w + j));
+}
+constexpr int kADma = 6;
+
+__device__ __forceinline__ void a_compute(const lds_char* st, const ALanes& k,
+                                          f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const lds_char* pe = st + (ks ? k.rdE1 : k.rdE0);
+    const lds_char* ph = st + (ks ? k.rdH1 : k.rdH0);
+    u32x4 fa[4], fb[2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa[mb] = lds_read16(pe + 32 * kRowA * mb);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) fb[nb] = lds_read16(ph + 32 * kRowA * nb);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[mb], fb[nb], acc[mb][nb]);
+  }
+}
+
+__device__ __forceinline__ int stage_add2(int s) { return s == 0 ? 2 : s - 1; }
+__device__ __forceinline__ int stage_add1(int s) { return s == kNStage - 1 ? 0 : s + 1; }
+
+// The A role's copy stream runs across tiles: the last two chunks of a tile issue the first
+// two chunks of the next one (pre = they are in flight), so a tile starts without a bubble.
+struct APipe {
+  int st;    // stage of the next chunk to compute
+  bool pre;  // chunks 0 and 1 of the next tile are in flight (after the first tile: always)
+};
+
+__device__ __forceinline__ bool a_logits(const uint16_t* E, const uint16_t* h, int V, int d,
+                                         int v0, int row0, bool has_next, int v0n, int row0n,
+                                         APipe& p, lds_char* smem, int w, const ALanes& k,
+                                         f32x16 (&acc)[4][2], int* bar, int& gen,
+                                         unsigned* err) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{0};
+  const int nk = d / kKC;
+  const uint32_t base = lds_addr(smem);
+  int s = p.st;
+  bool bad = false;
+  if (!p.pre) {
+    a_issue(E, h, V, d, v0, row0, 0, base + s * kStageA, w, k);
+    a_issue(E, h, V, d, v0, row0, 1, base + stage_add1(s) * kStageA, w, k);
+  }
+  // Chunk kc: its copies have landed (chunk kc + 1 may still be in flight) and every wave is
+  // past chunk kc - 1, whose stage receives chunk kc + 2 of the stream.  Past the end of the
+  // tile that is the next tile, or, when there is none, the first chunks of this one again:
+  // the body stays free of branches (which keeps the accumulators in place) and every
+  // iteration has the same number of copies in flight.
+  const int vx = has_next ? v0n : v0;
+  const int rx = has_next ? row0n : row0;
+  for (int kc = 0; kc < nk; ++kc) {
+    vm_wait<kADma>();
+    role_bar(bar, gen, err, bad);
+    const bool in = kc + 2 < nk;
+    a_issue(E, h, V, d, in ? v0 : vx, in ? row0 : rx, in ? kc + 2 : kc + 2 - nk,
+            base + stage_add2(s) * kStageA, w, k);
+    a_compute(smem + s * kStageA, k, acc);
+    s = stage_add1(s);
+  }
+  p.st = s;
+  p.pre = true;
+  if (bad) vm_wait<0>();
+  return !bad;
 }
 
 // Tile maximum (base-2 units) and argmax of one row: 64 logits in this lane, 64 in lane ^ 32.
@@ -247,13 +479,11 @@ __device__ __forceinline__ void piece_end(const Piece& p, int piece, EpiState& e
   }
 }
 
-// Whole pieces, not interleaved (first round of a job, tiles that reach past V).
-__device__ __forceinline__ void epi_pieces(int first, const f32x16 (&acc)[4][2], EpiState& e,
-                                           bool full, int vt0, int V, float c2, int row0,
-                                           uint32_t step, uint32_t k0, uint32_t k1,
-                                           char* ring_tile) {
+__device__ __forceinline__ void epi_pieces(const f32x16 (&acc)[4][2], EpiState& e, bool full,
+                                           int vt0, int V, float c2, int row0, uint32_t step,
+                                           uint32_t k0, uint32_t k1, char* ring_tile) {
 #pragma unroll 1
-  for (int piece = first; piece < 8; ++piece) {
+  for (int piece = 0; piece < 8; ++piece) {
     Piece p;
     piece_begin(p, piece, acc, e, vt0, row0, ring_tile);
     if (full) {
@@ -274,18 +504,19 @@ __device__ __forceinline__ void epi_pieces(int first, const f32x16 (&acc)[4][2],
 }
 
 // ---------------------------------------------------------------------------------------
-// B step helpers.  E slice of one tile in LDS, row-major [128 vocab][DS columns].
+// B step.  A stage holds one 32-row quarter of a tile: the E slice row-major [32][DS] and
+// the probability fragments of the four B waves.
 // ---------------------------------------------------------------------------------------
-// B operand of v_mfma_f32_16x16x32_bf16 for columns [16 cb, 16 cb + 16) and vocabulary
-// [32 ks, 32 ks + 32): lane (g = lane / 16, i = lane % 16) needs E[32 ks + 8 g + 0..7][16 cb + i].
-// Two transpose reads: lane j of a 16-lane group addresses row 32 ks + 8 g + 4 half + j / 4,
-// columns 16 cb + 4 (j % 4) .. + 3; lane i then holds rows + 0..3 of column 16 cb + i.
+// B operand of v_mfma_f32_16x16x32_bf16 for columns [16 cb, 16 cb + 16) and the stage's 32
+// vocabulary rows: lane (g = lane / 16, i = lane % 16) needs E[8 g + 0..7][16 cb + i].  Two
+// transpose reads: lane j of a 16-lane group addresses row 8 g + 4 half + j / 4, columns
+// 16 cb + 4 (j % 4) .. + 3; lane i then holds rows + 0..3 of column 16 cb + i.
 template <int NCB>
-__device__ __forceinline__ u32x4 et_frag(const lds_char* et, int cb, int ks) {
+__device__ __forceinline__ u32x4 et_frag(const lds_char* et, int cb) {
   constexpr int pitch = 32 * NCB;  // bytes per row
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
-  const int row = 32 * ks + 8 * g + (j >> 2);
+  const int row = 8 * g + (j >> 2);
   const int col = 16 * cb + 4 * (j & 3);
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -301,7 +532,7 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f3
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Multiply 8 bf16 by an exact power of two (the re-rounding is exact).
+// Multiply 8 bf16 by a power of two (the re-rounding is exact for normal results).
 __device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float s) {
   u32x4 o;
 #pragma unroll
@@ -323,117 +554,119 @@ __device__ __forceinline__ void stats_reset(RowStats& s) {
   s.gi = 0x7FFFFFFF;
 }
 
-// ---------------------------------------------------------------------------------------
-// Role barriers: the four A waves (and the four B waves) of a workgroup synchronise through
-// an LDS counter, so that one role never waits for the other.  Bounded like the group waits.
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ bool role_sync(int* ctr, int& gen, unsigned* err) {
-  gen += 4;
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  if ((threadIdx.x & 63) == 0)
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  unsigned it = 0;
-  while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < gen) {
-    if (++it > kSpinLimit) {
-      atomicOr(err, 4u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
+// Position of the B role in its stream of stages: (heavy job, round, stage of the round).
+struct BCur {
+  int job, r, s, nst, ptb, tb, te, nr, c, vr;
+  unsigned q;  // group round counter; ring slot and counter parity = q & 1
+  bool valid;
+};
+
+__device__ __forceinline__ void b_load_job(BCur& u, const Sched& sc) {
+  u.valid = u.job < sc.n_heavy;
+  if (!u.valid) return;
+  const Job J = job_at(sc, u.job);
+  u.c = J.c;
+  u.vr = J.vr;
+  u.tb = J.tb;
+  u.te = J.te;
+  u.nr = J.nr;
+  u.r = 0;
+  u.s = 0;
+  u.ptb = J.tb;
+  u.nst = 4 * min(kG, J.te - J.tb);
+}
+
+__device__ __forceinline__ void b_advance(BCur& u, const Sched& sc) {
+  if (++u.s < u.nst) return;
+  u.s = 0;
+  ++u.q;
+  if (++u.r < u.nr) {
+    u.ptb += kG;
+    u.nst = 4 * min(kG, u.te - u.ptb);
+    return;
   }
-  return true;
+  u.job += sc.n_groups;
+  b_load_job(u, sc);
 }
 
-// Bounded wait of one wave until *p >= target.
-__device__ __forceinline__ bool wave_wait(unsigned* p, unsigned target, unsigned* err) {
-  unsigned it = 0;
-  while (poll(p) < target) {
-    if (poll(err) != 0u) return false;
-    if (++it > kSpinLimit) {
-      atomicOr(err, 1u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return true;
+__device__ __forceinline__ bool b_is_last(const BCur& u, const Sched& sc) {
+  return u.s == u.nst - 1 && u.r == u.nr - 1 && u.job + sc.n_groups >= sc.n_heavy;
 }
 
-__device__ __forceinline__ void wave_signal(unsigned* p) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if ((threadIdx.x & 63) == 0) atomicAdd(p, 1u);
-}
-
-// Logits tile with the A role's own barrier.
-__device__ __forceinline__ bool logits_tile_a(const uint16_t* E, const uint16_t* h, int V, int d,
-                                              int v0, int row0, lds_char* smem,
-                                              f32x16 (&acc)[4][2], int* bar, int& gen,
-                                              unsigned* err) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{0};
-  const int nk = d / kKC;
-  const int fr = lane & 31, fh = lane >> 5;
-  stage_a(E, h, V, d, v0, row0, 0, smem);
-  if (!role_sync(bar, gen, err)) return false;
-  for (int kc = 0; kc < nk; ++kc) {
-    lds_char* cur = smem + (kc & 1) * kStageA;
-    if (kc + 1 < nk) stage_a(E, h, V, d, v0, row0, (kc + 1) * kKC, smem + ((kc + 1) & 1) * kStageA);
-#pragma unroll
-    for (int ks = 0; ks < kKC / 16; ++ks) {
-      u32x4 fa[4], fb[2];
-      const int seg = 2 * ks + fh;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = 32 * mb + fr;
-        fa[mb] = lds_read16(cur + row * 128 + 16 * (seg ^ (row & 7)));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int row = 64 * w + 32 * nb + fr;
-        fb[nb] = lds_read16(cur + kBV * 128 + row * 128 + 16 * (seg ^ (row & 7)));
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[mb], fb[nb], acc[mb][nb]);
-    }
-    if (!role_sync(bar, gen, err)) return false;
-  }
-  return true;
-}
-
-// E slice of half a tile (64 vocabulary rows x DS columns, row-major) for the B role.  Each
-// 64-lane instruction loads whole rows (kRpi rows of kRowChunks 16-byte chunks), so a lane's
-// source offset is the same in every instruction up to a wave-uniform stride.
+// Copies of one B stage: E rows [v0, v0 + 32) x columns [col0, col0 + 16 NCB) as NCB 1-KB
+// instructions (chunk c = 64 i + lane is row c / (2 NCB), 16-byte column chunk c % (2 NCB)),
+// dealt round-robin to the four B waves; then this wave's four probability fragments.
 template <int NCB>
-__device__ __forceinline__ void stage_b_half(const uint16_t* E, int V, int d, int v0, int col0,
-                                             lds_char* st) {
-  constexpr int DS = 16 * NCB;
-  constexpr int kRowChunks = DS / 8;
-  constexpr int kRpi = 64 / kRowChunks;               // rows per instruction
-  constexpr int kInstr = (64 + kRpi - 1) / kRpi;      // instructions per half tile
-  const int lane = threadIdx.x & 63, bw = (threadIdx.x >> 6) - 4;
-  const int lr = lane / kRowChunks, cc = lane % kRowChunks;
-  const bool active = lr < kRpi;
-  const uint16_t* src = E + col0 + 8 * cc;
+__device__ __forceinline__ void b_issue(const uint16_t* E, const uint16_t* ring, int V, int d,
+                                        int col0, const BCur& u, uint32_t dst, int bw) {
+  const int lane = threadIdx.x & 63;
+  const int g = u.s >> 2, kq = u.s & 3;
+  const int v0 = (u.ptb + g) * kBV + kBQ * kq;
+  const int br = min(v0, V - 1);
+  const uint16_t* eb = E + (size_t)br * d + col0;
 #pragma unroll
-  for (int k = 0; k < (kInstr + 3) / 4; ++k) {
-    const int i = bw + 4 * k;
-    if (i < kInstr) {
-      int v = v0 + i * kRpi + lr;
-      v = v < V ? v : V - 1;
-      if (active && i * kRpi + lr < 64) g2l16(src + (size_t)v * d, st + i * kRpi * (2 * DS));
+  for (int j = 0; j < (NCB + 3) / 4; ++j) {
+    const int i = bw + 4 * j;
+    if (i < NCB) {
+      const int c = 64 * i + lane;
+      const int row = c / (2 * NCB), cc = c - row * (2 * NCB);
+      const int rv = min(v0 + row, V - 1);
+      dma16_nt(eb, (uint32_t)(rv - br) * (2u * (uint32_t)d) + 16u * (uint32_t)cc,
+               dst + 1024u * (uint32_t)i);
     }
+  }
+  const uint16_t* pb = ring + ((size_t)(u.q & 1) * kG + g) * kTileElems;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    dma16(pb + ((4 * bw + rb) * 4 + kq) * 512, 16u * (uint32_t)lane,
+          dst + (uint32_t)(NCB * 1024 + 4096 * bw + 1024 * rb));
+}
+
+template <int NCB>
+__device__ __forceinline__ void b_compute(const lds_char* st, int bw, bool scaled,
+                                          const float* refg, const float* Mn,
+                                          f32x4 (&bacc)[4][NCB]) {
+  const int lane = threadIdx.x & 63;
+  u32x4 fa[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    fa[rb] = lds_read16(st + NCB * 1024 + 4096 * bw + 1024 * rb + 16 * lane);
+  if (scaled) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int row = 64 * bw + 16 * rb + (lane & 15);
+      const float rf = refg[row];
+      fa[rb] = scale_bf16x8(fa[rb], rf == -INFINITY ? 0.0f : hw_exp2(rf - Mn[row]));
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const u32x4 fb = et_frag<NCB>(st, cb);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) bacc[rb][cb] = mfma16x16x32(fa[rb], fb, bacc[rb][cb]);
+  }
+}
+
+// vm_wait with a wave-uniform count n in [4, 7]: a uniform branch to the immediate form.
+__device__ __forceinline__ void vm_wait_n(int n) {
+  if (n >= 7) {
+    vm_wait<7>();
+  } else if (n == 6) {
+    vm_wait<6>();
+  } else if (n == 5) {
+    vm_wait<5>();
+  } else {
+    vm_wait<4>();
   }
 }
 
 struct SharedState {
-  float sM[DG_CANVAS];        // group running row maximum (base 2, integer), this job
-  float sMold[DG_CANVAS];
-  int sMjob;                  // job the maxima belong to
+  float sM[DG_CANVAS];        // group running row maximum (base 2) of job sMjob, for the A role
+  float sMn[2][DG_CANVAS];    // per round parity: row maximum after the round
+  float sRs[2][DG_CANVAS];    // per round parity: accumulator rescale factor of the round
+  int sMjob;                  // job the maxima in sM belong to (-1: none)
   int sMask[2];               // per round parity: tiles whose probabilities need scaling
-  int sRescale[2];            // per round parity: some row maximum grew
+  int sResc[2];               // per round parity: some row maximum grew
   int barA, barB;
   int sInfo[4];
 };
@@ -444,16 +677,16 @@ struct SharedState {
 template <int NCB>
 __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
   constexpr int DS = 16 * NCB;
-  constexpr int kStageB = 64 * DS * 2;  // half tile of the E slice
-  __shared__ __attribute__((aligned(16))) char smem_a[kSmem];
-  __shared__ __attribute__((aligned(16))) char smem_b[2 * kStageB];
+  constexpr int kStageB = b_stage_bytes<NCB>();
+  __shared__ __attribute__((aligned(1024))) char smem_a[kSmemA];
+  __shared__ __attribute__((aligned(1024))) char smem_b[kNStage * kStageB];
   __shared__ SharedState ss;
 
   const uint16_t* E = f.a.E;
   const uint16_t* h = f.a.h;
   const int V = f.a.V, d = f.a.d, n_canvas = f.a.n_canvas;
-  const uint8_t* commit = f.a.commit;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, fr = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, fr = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const size_t R = (size_t)n_canvas * DG_CANVAS;
   unsigned* err = f.sync + 8;
   const int n_tiles = f.n_tiles, s_v = f.s_v, n_groups = f.n_groups;
@@ -470,77 +703,70 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
       ok = 0;
       atomicOr(err, 2u);
     }
-    int n_nc = n_canvas;
-    if (commit != nullptr) {
-      n_nc = 0;
-      for (int c = 0; c < n_canvas; ++c) n_nc += commit[c] == 0;
-    }
     ss.sInfo[0] = ok;
     ss.sInfo[1] = gid;
     ss.sInfo[2] = (int)(slot % kG);
-    ss.sInfo[3] = n_nc;
+    ss.sInfo[3] = (int)f.sync[9];
     ss.barA = 0;
     ss.barB = 0;
     ss.sMjob = -1;
     ss.sMask[0] = ss.sMask[1] = 0;
-    ss.sRescale[0] = ss.sRescale[1] = 0;
+    ss.sResc[0] = ss.sResc[1] = 0;
   }
   __syncthreads();  // the only whole-workgroup barrier
   if (!ss.sInfo[0]) return;
-  const int gid = ss.sInfo[1], member = ss.sInfo[2], n_nc = ss.sInfo[3];
-  unsigned* produced = f.sync + 16 + gid;
-  unsigned* consumed = f.sync + 16 + n_groups + gid;
+  const int gid = __builtin_amdgcn_readfirstlane(ss.sInfo[1]);
+  const int member = __builtin_amdgcn_readfirstlane(ss.sInfo[2]);
+  Sched sc;
+  sc.order = f.order;
+  sc.s_v = s_v;
+  sc.n_nc = __builtin_amdgcn_readfirstlane(ss.sInfo[3]);
+  sc.n_tiles = n_tiles;
+  sc.n_jobs = n_canvas * s_v;
+  sc.n_heavy = sc.n_nc * s_v;
+  sc.n_groups = n_groups;
+  sc.member = member;
+  unsigned* produced = f.sync + 16 + 4 * gid;
+  unsigned* consumed = produced + 2;
   uint16_t* ring = f.ring + (size_t)gid * 2 * kG * kTileElems;
   float* ring_ref = f.ring_ref + (size_t)gid * 2 * kG * DG_CANVAS;
-  const int col0 = member * DS;
-  const int n_jobs = n_canvas * s_v;
-  const bool role_a = w < 4;
-  int gen = 0;       // this wave's role-barrier generation
-  unsigned rr = 0;   // heavy rounds of this group so far (identical in every wave)
+  int gen = 0;  // this wave's role-barrier generation
 
-  if (role_a) {
-    for (int job = gid; job < n_jobs; job += n_groups) {
-    int c = 0, vr;
-    {
-      const int heavy = n_nc * s_v;
-      const bool want_nc = job < heavy;
-      const int idx = want_nc ? job / s_v : (job - heavy) / s_v;
-      vr = want_nc ? job % s_v : (job - heavy) % s_v;
-      int seen = 0;
-      for (int cc = 0; cc < n_canvas; ++cc) {
-        const bool nc = commit == nullptr || commit[cc] == 0;
-        if (nc == want_nc) {
-          if (seen == idx) {
-            c = cc;
-            break;
-          }
-          ++seen;
-        }
-      }
-    }
-    const bool is_commit = commit != nullptr && commit[c] != 0;
-    const int tb = (int)(((long long)n_tiles * vr) / s_v);
-    const int te = (int)(((long long)n_tiles * (vr + 1)) / s_v);
-    const int nr = (te - tb + kG - 1) / kG;
-    const int row0 = c * DG_CANVAS;
-
-
-      // ================================ A role ================================
-      const float c2 = kLog2e / f.a.temperature[c];
-      const uint32_t step = (uint32_t)f.a.step[c];
-      const uint32_t k0 = f.a.k0, k1 = f.a.k1;
+  if (w < 4) {
+    // ================================ A role ================================
+    const float* temperature = f.a.temperature;
+    const int32_t* steps = f.a.step;
+    const uint32_t k0 = f.a.k0, k1 = f.a.k1;
+    float* st_m = f.st_m;
+    float* st_l = f.st_l;
+    float* st_a = f.st_a;
+    float* st_amv = f.st_amv;
+    int* st_ami = f.st_ami;
+    float* st_gv = f.st_gv;
+    int* st_gi = f.st_gi;
+    const ALanes k = a_lanes(w, d);
+    APipe pipe{0, false};
+    unsigned rr = 0;  // heavy rounds of this group so far
+    f32x16 acc[4][2];
+    for (int job = gid; job < sc.n_jobs; job += n_groups) {
+      const Job J = job_at(sc, job);
+      const int row0 = J.c * DG_CANVAS;
+      const float c2 = kLog2e / temperature[J.c];
+      const uint32_t step = (uint32_t)steps[J.c];
       RowStats st0, st1;
       stats_reset(st0);
       stats_reset(st1);
-      f32x16 acc[4][2];
-      for (int r = 0; r < nr; ++r) {
-        const int tile = tb + r * kG + member;
-        const bool a_valid = tile < te;
+      for (int r = 0; r < J.nr; ++r) {
+        const int tile = J.tb + r * kG + member;
+        const bool valid = tile < J.te;
         const int vt0 = tile * kBV;
         const bool full = vt0 + kBV <= V;
-        if (is_commit) {
-          if (!a_valid) break;
-          if (!logits_tile_a(E, h, V, d, vt0, row0, (lds_char*)smem_a, acc, &ss.barA, gen, err))
+        if (J.commit) {
+          if (!valid) break;
+          int v0n = 0, row0n = 0;
+          const bool hn = next_tile(sc, job, J.tb, J.te, row0, r, v0n, row0n);
+          if (!a_logits(E, h, V, d, vt0, row0, hn, v0n, row0n, pipe, (lds_char*)smem_a, w, k,
+                        acc, &ss.barA, gen, err))
             return;
           float m[2], amv[2];
           int ami[2];
@@ -549,10 +775,17 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
           argmax_merge(st1.amv, st1.ami, amv[1], ami[1]);
           continue;
         }
-        // ring slot reuse: every B wave of the group has finished round rr - 2
-        if (rr >= 2 && !wave_wait(consumed, 64u * (rr - 1), err)) return;
-        if (a_valid) {
-          if (!logits_tile_a(E, h, V, d, vt0, row0, (lds_char*)smem_a, acc, &ss.barA, gen, err))
+        const unsigned par = rr & 1;
+        // ring slot par is free once every B wave of the group has consumed round rr - 2
+        if (rr >= 2 && !wave_wait(consumed + par, 64u * (rr >> 1), err)) {
+          vm_wait<0>();
+          return;
+        }
+        if (valid) {
+          int v0n = 0, row0n = 0;
+          const bool hn = next_tile(sc, job, J.tb, J.te, row0, r, v0n, row0n);
+          if (!a_logits(E, h, V, d, vt0, row0, hn, v0n, row0n, pipe, (lds_char*)smem_a, w, k,
+                        acc, &ss.barA, gen, err))
             return;
           float mt[2], tamv[2];
           int tami[2];
@@ -571,15 +804,15 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
           e.ref0 = fmaxf(M0, mt[0]);
           e.ref1 = fmaxf(M1, mt[1]);
           char* ring_out =
-              reinterpret_cast<char*>(ring + ((size_t)(rr & 1) * kG + member) * kTileElems);
-          epi_pieces(0, acc, e, full, vt0, V, c2, row0, step, k0, k1, ring_out);
+              reinterpret_cast<char*>(ring + ((size_t)par * kG + member) * kTileElems);
+          epi_pieces(acc, e, full, vt0, V, c2, row0, step, k0, k1, ring_out);
           e.ls0 += xor_f(e.ls0, 32);
           e.as0 += xor_f(e.as0, 32);
           argmax_merge(e.gv0, e.gi0, xor_f(e.gv0, 32), xor_i(e.gi0, 32));
           e.ls1 += xor_f(e.ls1, 32);
           e.as1 += xor_f(e.as1, 32);
           argmax_merge(e.gv1, e.gi1, xor_f(e.gv1, 32), xor_i(e.gi1, 32));
-          float* rout = ring_ref + ((size_t)(rr & 1) * kG + member) * DG_CANVAS;
+          float* rout = ring_ref + ((size_t)par * kG + member) * DG_CANVAS;
           if (lane < 32) {
             rout[64 * w + fr] = e.ref0;
             rout[64 * w + 32 + fr] = e.ref1;
@@ -591,166 +824,187 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
           argmax_merge(st1.amv, st1.ami, tamv[1], tami[1]);
           argmax_merge(st1.gv, st1.gi, e.gv1, e.gi1);
         }
-        wave_signal(produced);
+        wave_signal(produced + par);
         ++rr;
       }
       if (lane < 32) {
-        const size_t o0 = ((size_t)vr * kG + member) * R + row0 + 64 * w + fr;
+        const size_t o0 = ((size_t)J.vr * kG + member) * R + row0 + 64 * w + fr;
         const size_t o1 = o0 + 32;
-        f.st_amv[o0] = st0.amv;
-        f.st_ami[o0] = st0.ami;
-        f.st_m[o0] = st0.m;
-        f.st_l[o0] = st0.l;
-        f.st_a[o0] = st0.a;
-        f.st_gv[o0] = st0.gv;
-        f.st_gi[o0] = st0.gi;
-        f.st_amv[o1] = st1.amv;
-        f.st_ami[o1] = st1.ami;
-        f.st_m[o1] = st1.m;
-        f.st_l[o1] = st1.l;
-        f.st_a[o1] = st1.a;
-        f.st_gv[o1] = st1.gv;
-        f.st_gi[o1] = st1.gi;
+        st_amv[o0] = st0.amv;
+        st_ami[o0] = st0.ami;
+        st_m[o0] = st0.m;
+        st_l[o0] = st0.l;
+        st_a[o0] = st0.a;
+        st_gv[o0] = st0.gv;
+        st_gi[o0] = st0.gi;
+        st_amv[o1] = st1.amv;
+        st_ami[o1] = st1.ami;
+        st_m[o1] = st1.m;
+        st_l[o1] = st1.l;
+        st_a[o1] = st1.a;
+        st_gv[o1] = st1.gv;
+        st_gi[o1] = st1.gi;
       }
     }
-  } else {
-    for (int job = gid; job < n_jobs; job += n_groups) {
-    int c = 0, vr;
-    {
-      const int heavy = n_nc * s_v;
-      const bool want_nc = job < heavy;
-      const int idx = want_nc ? job / s_v : (job - heavy) / s_v;
-      vr = want_nc ? job % s_v : (job - heavy) % s_v;
-      int seen = 0;
-      for (int cc = 0; cc < n_canvas; ++cc) {
-        const bool nc = commit == nullptr || commit[cc] == 0;
-        if (nc == want_nc) {
-          if (seen == idx) {
-            c = cc;
-            break;
-          }
-          ++seen;
-        }
-      }
-    }
-    const bool is_commit = commit != nullptr && commit[c] != 0;
-    const int tb = (int)(((long long)n_tiles * vr) / s_v);
-    const int te = (int)(((long long)n_tiles * (vr + 1)) / s_v);
-    const int nr = (te - tb + kG - 1) / kG;
-    const int row0 = c * DG_CANVAS;
-
-      if (is_commit) continue;
-
-      // ================================ B role ================================
-      const int bw = w - 4;
-      const int tbt = t - 256;  // 0..255: the row this thread maintains
-      // start of the job: reset the maxima (after the previous job's last use of them)
-      if (!role_sync(&ss.barB, gen, err)) return;
-      ss.sM[tbt] = -INFINITY;
-      if (!role_sync(&ss.barB, gen, err)) return;
-      if (tbt == 0) __hip_atomic_store(&ss.sMjob, job, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      f32x4 bacc[4][NCB];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb] = f32x4{0, 0, 0, 0};
-      for (int r = 0; r < nr; ++r) {
-        if (!wave_wait(produced, 64u * (rr + 1), err)) return;
-        asm volatile("buffer_inv sc0" ::: "memory");
-        const uint16_t* ring_in = ring + (size_t)(rr & 1) * kG * kTileElems;
-        const float* ref_in = ring_ref + (size_t)(rr & 1) * kG * DG_CANVAS;
-        const int ptb = tb + r * kG;
-        const int n_in = (te - ptb) < kG ? (te - ptb) : kG;
-        const int par = rr & 1;
-        // new running maxima and per-tile exponents (thread: row tbt)
-        {
-          const float mo = ss.sM[tbt];
-          float mn = mo;
-          for (int g = 0; g < n_in; ++g) mn = fmaxf(mn, ref_in[g * DG_CANVAS + tbt]);
-          int mask = 0;
-          for (int g = 0; g < n_in; ++g)
-            if (ref_in[g * DG_CANVAS + tbt] != mn) mask |= 1 << g;
-          ss.sMold[tbt] = mo;
-          ss.sM[tbt] = mn;
-          if (mask) atomicOr(&ss.sMask[par], mask);
-          if (mn != mo && mo != -INFINITY) atomicOr(&ss.sRescale[par], 1);
-        }
-        if (!role_sync(&ss.barB, gen, err)) return;
-        const int mask = ss.sMask[par];
-        const int rescale = ss.sRescale[par];
-        if (tbt == 0) {  // the other parity is next used two role barriers from now
-          ss.sMask[par ^ 1] = 0;
-          ss.sRescale[par ^ 1] = 0;
-        }
-        if (rescale) {
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = 64 * bw + 16 * rb + 4 * (lane >> 4) + i;
-              const float mo = ss.sMold[row];
-              const float sc = (mo == -INFINITY) ? 0.0f : hw_exp2(mo - ss.sM[row]);
-#pragma unroll
-              for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb][i] *= sc;
-            }
-        }
-        // stages: (tile g, half) pairs, E half tiles double-buffered
-        const int n_st = 2 * n_in;
-        stage_b_half<NCB>(E, V, d, ptb * kBV, col0, (lds_char*)smem_b);
-        if (!role_sync(&ss.barB, gen, err)) return;
-        for (int k = 0; k < n_st; ++k) {
-          const int g = k >> 1, half = k & 1;
-          const lds_char* et = (lds_char*)smem_b + (k & 1) * kStageB;
-          const char* ptile = reinterpret_cast<const char*>(ring_in + (size_t)g * kTileElems);
-          if (k + 1 < n_st)
-            stage_b_half<NCB>(E, V, d, (ptb + ((k + 1) >> 1)) * kBV + 64 * ((k + 1) & 1), col0,
-                              (lds_char*)smem_b + ((k + 1) & 1) * kStageB);
-          const bool scaled = (mask >> g) & 1;
-#pragma unroll
-          for (int kl = 0; kl < 2; ++kl) {
-            u32x4 fa[4];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-              fa[rb] = *reinterpret_cast<const u32x4*>(
-                  ptile + (((4 * bw + rb) * 4 + 2 * half + kl) * 64 + lane) * 16);
-            if (scaled) {
-#pragma unroll
-              for (int rb = 0; rb < 4; ++rb) {
-                const int row = 64 * bw + 16 * rb + (lane & 15);
-                const float rf = ref_in[g * DG_CANVAS + row];
-                fa[rb] = scale_bf16x8(fa[rb], rf == -INFINITY ? 0.0f : hw_exp2(rf - ss.sM[row]));
-              }
-            }
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-              const u32x4 fb = et_frag<NCB>(et, cb, kl);
-#pragma unroll
-              for (int rb = 0; rb < 4; ++rb) bacc[rb][cb] = mfma16x16x32(fa[rb], fb, bacc[rb][cb]);
-            }
-          }
-          if (!role_sync(&ss.barB, gen, err)) return;
-        }
-        wave_signal(consumed);
-        ++rr;
-      }
-      // expectation partial of this (range, slice) and the final maxima
-      float* out = f.accp + (size_t)vr * R * d;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 64 * bw + 16 * rb + 4 * (lane >> 4) + i;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            out[(size_t)(row0 + row) * d + col0 + 16 * cb + (lane & 15)] = bacc[rb][cb][i];
-        }
-      if (member == 0) f.accM[(size_t)vr * R + row0 + tbt] = ss.sM[tbt];
-    }
+    vm_wait<0>();
+    return;
   }
+
+  // ================================ B role ================================
+  const int bw = w - 4;
+  const int tbt = t - 256;  // 0..255: the row this thread maintains
+  const int col0 = member * DS;
+  const int nB = (NCB - bw + 3) / 4 + 4;  // copies per stage of this wave
+  float* accp = f.accp;
+  float* accM = f.accM;
+  const uint32_t bbase = lds_addr((lds_char*)smem_b);
+  BCur cu;
+  cu.job = gid;
+  cu.q = 0;
+  b_load_job(cu, sc);
+  if (!cu.valid) return;
+  BCur iu = cu;
+  int s_issue = 0, s_comp = 0;
+  f32x4 bacc[4][NCB];
+  int mask = 0;
+  bool bad = false;
+
+  // Start of round iu (at issue time, two stages before it is computed): wait for its data,
+  // then fold its tile references into the row maxima of this thread's row.
+  auto round_prep = [&](const BCur& u) -> bool {
+    const unsigned par = u.q & 1;
+    if (!wave_wait(produced + par, 64u * ((u.q >> 1) + 1), err)) return false;
+    asm volatile("buffer_inv sc0" ::: "memory");
+    const float* ref = ring_ref + (size_t)par * kG * DG_CANVAS + tbt;
+    const int n_in = u.nst >> 2;
+    float rv[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) rv[g] = g < n_in ? ref[g * DG_CANVAS] : -INFINITY;
+    const float mo = (u.r == 0) ? -INFINITY : ss.sMn[par ^ 1][tbt];
+    float mn = mo;
+#pragma unroll
+    for (int g = 0; g < kG; ++g) mn = fmaxf(mn, rv[g]);
+    int m = 0;
+#pragma unroll
+    for (int g = 0; g < kG; ++g) m |= (g < n_in && rv[g] != mn) ? (1 << g) : 0;
+    ss.sMn[par][tbt] = mn;
+    ss.sRs[par][tbt] = (mo == -INFINITY) ? 0.0f : hw_exp2(mo - mn);
+    if (m) atomicOr(&ss.sMask[par], m);
+    if (mo != -INFINITY && mn != mo) atomicOr(&ss.sResc[par], 1);
+    return true;
+  };
+  auto issue_next = [&]() -> bool {
+    if (!iu.valid) return true;
+    if (iu.s == 0 && !round_prep(iu)) return false;
+    b_issue<NCB>(E, ring, V, d, col0, iu, bbase + s_issue * kStageB, bw);
+    s_issue = stage_add1(s_issue);
+    b_advance(iu, sc);
+    return true;
+  };
+
+  bool ok = issue_next() && issue_next();
+  while (ok && cu.valid) {
+    const bool last = b_is_last(cu, sc);
+    if (last)
+      vm_wait<0>();
+    else
+      vm_wait_n(nB);
+    role_bar(&ss.barB, gen, err, bad);
+    if (bad || !issue_next()) break;
+    const unsigned par = cu.q & 1;
+    if (cu.s == 0) {
+      if (cu.r == 0) {
+        // new job: zero the accumulators, publish the maxima under the new job id
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb] = f32x4{0, 0, 0, 0};
+        if (tbt == 0) __hip_atomic_store(&ss.sMjob, -1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        role_bar(&ss.barB, gen, err, bad);
+        ss.sM[tbt] = ss.sMn[par][tbt];
+        role_bar(&ss.barB, gen, err, bad);
+        if (tbt == 0)
+          __hip_atomic_store(&ss.sMjob, cu.job, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        ss.sM[tbt] = ss.sMn[par][tbt];
+      }
+      mask = ss.sMask[par];
+      if (ss.sResc[par]) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sf = ss.sRs[par][64 * bw + 16 * rb + 4 * (lane >> 4) + i];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb][i] *= sf;
+          }
+      }
+    } else if (cu.s == 1 && tbt == 0) {
+      // every B wave read this round's flags at stage 0; the next writer is two rounds ahead
+      ss.sMask[par] = 0;
+      ss.sResc[par] = 0;
+    }
+    const int g = cu.s >> 2;
+    b_compute<NCB>((lds_char*)smem_b + s_comp * kStageB, bw, (mask >> g) & 1,
+                   ring_ref + ((size_t)par * kG + g) * DG_CANVAS, ss.sMn[par], bacc);
+    if (cu.s == cu.nst - 1) {
+      // this wave's reads of the round's ring slot are complete
+      if (lane == 0) atomicAdd(consumed + par, 1u);
+      if (cu.r == cu.nr - 1) {
+        // expectation partial of this (range, slice) and the final maxima
+        float* out = accp + (size_t)cu.vr * R * d;
+        const int row0 = cu.c * DG_CANVAS;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 64 * bw + 16 * rb + 4 * (lane >> 4) + i;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              out[(size_t)(row0 + row) * d + col0 + 16 * cb + (lane & 15)] = bacc[rb][cb][i];
+          }
+        if (member == 0) accM[(size_t)cu.vr * R + row0 + tbt] = ss.sMn[par][tbt];
+      }
+    }
+    s_comp = stage_add1(s_comp);
+    b_advance(cu, sc);
+  }
+  vm_wait<0>();
 }
 
-__global__ void k_vp_fused_init(unsigned* sync, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0u;
+// Zero the counters; order the canvases (non-commit first, each part ascending) and count
+// the non-commit ones.
+__global__ __launch_bounds__(256) void k_vp_fused_init(unsigned* sync, int n_sync, int* order,
+                                                       const uint8_t* commit, int n) {
+  __shared__ int cnt[256];
+  __shared__ int total;
+  const int t = threadIdx.x;
+  for (int i = t; i < n_sync; i += 256) sync[i] = 0u;
+  const int per = (n + 255) / 256;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int k = 0;
+  for (int c = lo; c < hi; ++c) k += (commit == nullptr || commit[c] == 0) ? 1 : 0;
+  cnt[t] = k;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = cnt[i];
+      cnt[i] = run;
+      run += v;
+    }
+    total = run;
+    sync[9] = (unsigned)run;
+  }
+  __syncthreads();
+  int a = cnt[t];                   // non-commit canvases before lo
+  int b = total + (lo - cnt[t]);    // commit canvases before lo, after all non-commit ones
+  for (int c = lo; c < hi; ++c) {
+    if (commit == nullptr || commit[c] == 0)
+      order[a++] = c;
+    else
+      order[b++] = c;
+  }
 }
 
 // Merge the partials of each row; sc = sum_range 2^(accM - m) accp / l.
@@ -845,7 +1099,9 @@ FusedPlan fused_plan(int n_canvas, int V, int d, int n_wg) {
   p.s_v = sv;
   size_t off = 0;
   p.off_sync = off;
-  off += al256((16 + 2 * (size_t)p.n_groups) * 4);
+  off += al256((16 + 4 * (size_t)p.n_groups) * 4);
+  p.off_order = off;
+  off += al256((size_t)n_canvas * 4);
   p.off_ring = off;
   off += al256((size_t)p.n_groups * 2 * kG * kTileElems * 2);
   p.off_ring_ref = off;
@@ -866,6 +1122,7 @@ hipError_t fused_launch(const VocabArgs& a, const FusedPlan& p, void* workspace,
   Fused f{};
   f.a = a;
   f.sync = reinterpret_cast<unsigned*>(b + p.off_sync);
+  f.order = reinterpret_cast<const int*>(b + p.off_order);
   f.ring = reinterpret_cast<uint16_t*>(b + p.off_ring);
   f.ring_ref = reinterpret_cast<float*>(b + p.off_ring_ref);
   const size_t st = al256((size_t)p.s_v * kG * p.R * 4);
@@ -882,7 +1139,9 @@ hipError_t fused_launch(const VocabArgs& a, const FusedPlan& p, void* workspace,
   f.s_v = p.s_v;
   f.n_groups = p.n_groups;
   f.per_xcd = p.per_xcd;
-  hipLaunchKernelGGL(k_vp_fused_init, dim3(1), dim3(256), 0, stream, f.sync, 16 + 2 * p.n_groups);
+  hipLaunchKernelGGL(k_vp_fused_init, dim3(1), dim3(256), 0, stream, f.sync,
+                     16 + 4 * p.n_groups, reinterpret_cast<int*>(b + p.off_order), a.commit,
+                     a.n_canvas);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (a.d / (16 * kG)) {
