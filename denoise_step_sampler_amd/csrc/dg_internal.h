@@ -60,7 +60,8 @@ VocabPlan vocab_plan(int n_canvas, int V, int d);
 struct FusedPlan {
   int n_wg;       // workgroups launched (one per CU)
   int per_xcd;    // workgroups per XCD
-  int n_groups;   // groups of 16 workgroups
+  int n_groups;   // groups of 16 x halves workgroups (one or two per XCD)
+  int halves;     // halves per group: 2 when an XCD holds 32 workgroups
   size_t R;
   int n_tiles;
   int s_v;        // vocabulary ranges per canvas

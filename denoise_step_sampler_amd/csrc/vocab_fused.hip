@@ -3,8 +3,8 @@
 // Why cooperative: the self-conditioning expectation acc[256, d] += P_t E_t needs, for one
 // canvas, 256 x d fp32 accumulators (2.9 MB at d = 2816), far more than one CU holds, while
 // the logits S_t = E_t h^T need all of d for every vocabulary tile.  So the accumulator is
-// split by columns over a group of 16 workgroups sharing one XCD (one L2), and each member
-// produces the probability tile of one vocabulary tile per round for the whole group:
+// split by columns over a half-group of 16 workgroups sharing one XCD (one L2), and each
+// member produces the probability tile of one vocabulary tile per round for its half:
 //
 //   round r, member g:   A: S^T tile t = tb + 16 r + g  (128 vocab x 256 rows, all of d,
 //                           bf16 MFMA 32x32x16) -> epilogue (softmax partial, entropy moment,
@@ -36,9 +36,9 @@
 // Within a role, waves synchronise through an LDS counter (never the workgroup barrier).
 //
 // Synchronisation across the group: per round parity, a counter of waves that published a
-// round (A) and one of waves that consumed one (B).  A of round q waits until every B wave
-// finished round q - 2 (two ring slots), B of round q waits until every A wave published
-// round q.  Keeping the parities apart makes each count exact: no wave can reach round q + 2
+// round (A) and one of waves that consumed one (B), over both halves.  A of round q waits until
+// every B wave finished round q - 2 (two ring slots), B of round q waits until every A wave
+// published round q.  Keeping the parities apart makes each count exact: no wave can reach round q + 2
 // of the same parity before the round q it would be confused with has been consumed.  Group
 // members are formed from the hardware XCC id so that all ring traffic stays in one L2; the
 // data is written with plain stores, completed (s_waitcnt) before the counter increment, and
@@ -46,8 +46,15 @@
 // flag, every wave leaves, and the combine kernel poisons the outputs (token -1, NaN
 // statistics).
 //
-// Jobs: (canvas, vocabulary range) pairs, non-commit canvases first, dealt round-robin to
-// groups.  Commit canvases need only the argmax: no probabilities, no exchange.
+// Groups and halves: a group is the 32 workgroups of one XCD, in two halves of 16.  The halves
+// run two jobs side by side (two canvases over the same vocabulary range), in one round count,
+// so every E line one half streams is read by the other half from L2 within the same round:
+// the E stream from beyond L2 is paid once per two canvases.  With fewer than 32 workgroups per
+// XCD a group is one half.
+//
+// Jobs: (canvas, vocabulary range) pairs, non-commit canvases first, range-major, taken two
+// at a time by the groups.  Commit canvases need only the argmax: no probabilities, no
+// exchange.
 #include <stdlib.h>
 #include <string.h>
 
@@ -60,7 +67,7 @@ namespace {
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kG = 16;          // workgroups per group (one d slice each)
+constexpr int kG = 16;          // workgroups per half-group (one d slice each)
 constexpr int kBV = 128;        // vocabulary tile
 constexpr int kKC = 32;         // d chunk of the logits contraction: 64 bytes per row
 constexpr int kRowA = 2 * kKC;  // bytes of one staged row
@@ -71,11 +78,11 @@ constexpr int kBQ = 32;         // vocabulary rows per B stage (a quarter tile)
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kTileElems = kBV * DG_CANVAS;          // bf16 probability tile: 64 KB
 
-// B stage: E slice [32 rows][32 NCB bytes] (NCB KB), then the probability fragments of the
-// four B waves (4 row blocks x 1 KB each).
+// B stage: E slice [32 rows][32 NCB bytes] (NCB KB), the probability fragments of the four
+// B waves (4 row blocks x 1 KB each), and the references of the stage's tile (256 floats).
 template <int NCB>
 constexpr int b_stage_bytes() {
-  return NCB * 1024 + 16 * 1024;
+  return NCB * 1024 + 16 * 1024 + 1024;
 }
 
 struct Fused {
@@ -84,8 +91,8 @@ struct Fused {
                       // canvases, [16 + 4 gid + p] produced and [16 + 4 gid + 2 + p] consumed
                       // counters of round parity p
   const int* order;   // [n_canvas] non-commit canvases first, each part in index order
-  uint16_t* ring;     // [n_groups][2][kG][kBV * 256]
-  float* ring_ref;    // [n_groups][2][kG][256]
+  uint16_t* ring;     // [n_groups][2][halves * kG][kBV * 256]
+  float* ring_ref;    // [n_groups][2][halves * kG][256]
   float* st_m;        // [S_v][kG][R] partial statistics
   float* st_l;
   float* st_a;
@@ -99,10 +106,14 @@ struct Fused {
   int s_v;
   int n_groups;
   int per_xcd;
+  int halves;         // halves per group (1 or 2)
 };
 
+// Polls read one wave-uniform word; readfirstlane tells the compiler so, which keeps the
+// control flow after every wait scalar (and the loop state out of vector registers).
 __device__ __forceinline__ unsigned poll(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
@@ -159,7 +170,8 @@ __device__ __forceinline__ void role_bar(int* ctr, int& gen, unsigned* err, bool
   if ((threadIdx.x & 63) == 0)
     __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   unsigned it = 0;
-  while (!bad && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < gen) {
+  while (!bad && __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                     ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < gen) {
     if (++it > kSpinLimit) {
       atomicOr(err, 4u);
       bad = true;
@@ -193,7 +205,9 @@ __device__ __forceinline__ void wave_signal(unsigned* p) {
 // ---------------------------------------------------------------------------------------
 struct Sched {
   const int* order;
-  int s_v, n_nc, n_tiles, n_jobs, n_heavy, n_groups, member;
+  int s_v, n_nc, n_tiles, n_jobs, n_heavy, n_groups;
+  int halves, half, sub;  // halves per group; this workgroup's half and member within it
+  int n_hpairs, n_pairs;  // job pairs of the group schedule: non-commit ones first
 };
 
 struct Job {
@@ -201,13 +215,17 @@ struct Job {
   bool commit;
 };
 
+// Jobs are numbered range-major within each part (non-commit, then commit), so that the two
+// groups of one XCD, which take consecutive jobs, stream the same vocabulary tiles for two
+// canvases at the same time and share every E line through their L2.
 __device__ __forceinline__ Job job_at(const Sched& s, int job) {
   Job J;
   const bool nc = job < s.n_heavy;
   const int k = nc ? job : job - s.n_heavy;
-  const int idx = k / s.s_v;
-  J.vr = k - idx * s.s_v;
-  J.c = s.order[nc ? idx : s.n_nc + idx];
+  const int n_part = nc ? s.n_nc : s.n_jobs / s.s_v - s.n_nc;
+  J.vr = k / n_part;
+  const int idx = k - J.vr * n_part;
+  J.c = __builtin_amdgcn_readfirstlane(s.order[nc ? idx : s.n_nc + idx]);  // wave-uniform
   J.commit = !nc;
   J.tb = (int)(((long long)s.n_tiles * J.vr) / s.s_v);
   J.te = (int)(((long long)s.n_tiles * (J.vr + 1)) / s.s_v);
@@ -215,20 +233,57 @@ __device__ __forceinline__ Job job_at(const Sched& s, int job) {
   return J;
 }
 
-// The A role's next logits tile after round r of `job`: the same job's next round, else the
-// first tile of a later job of this group.
-__device__ __forceinline__ bool next_tile(const Sched& s, int job, int tb, int te, int row0,
+// Job of half `half` in pair p (the halves of a group run the two jobs of a pair side by
+// side), or -1 when the pair has no job for that half.
+__device__ __forceinline__ int pair_job(const Sched& s, int p, int half) {
+  if (p < s.n_hpairs) {
+    const int j = s.halves * p + half;
+    return j < s.n_heavy ? j : -1;
+  }
+  const int j = s.n_heavy + s.halves * (p - s.n_hpairs) + half;
+  return j < s.n_jobs ? j : -1;
+}
+
+// Rounds of a non-commit pair: the longer of its jobs (the halves share one round count; the
+// shorter job's half runs empty rounds).
+__device__ __forceinline__ int pair_rounds(const Sched& s, int p) {
+  int nr = 0;
+  for (int hh = 0; hh < s.halves; ++hh) {
+    const int j = pair_job(s, p, hh);
+    if (j >= 0) nr = max(nr, job_at(s, j).nr);
+  }
+  return nr;
+}
+
+__device__ __forceinline__ Job half_job(const Sched& s, int p, int& job) {
+  job = pair_job(s, p, s.half);
+  if (job >= 0) return job_at(s, job);
+  Job J;
+  J.c = 0;
+  J.vr = 0;
+  J.tb = 0;
+  J.te = 0;
+  J.nr = 0;
+  J.commit = p >= s.n_hpairs;
+  return J;
+}
+
+// The A role's next logits tile after round r of pair p: this half's next round of the same
+// job, else the first tile of this half in a later pair of the group.
+__device__ __forceinline__ bool next_tile(const Sched& s, int p, int tb, int te, int row0,
                                           int r, int& v0n, int& row0n) {
-  const int t = tb + kG * (r + 1) + s.member;
+  const int t = tb + kG * (r + 1) + s.sub;
   if (t < te) {
     v0n = t * kBV;
     row0n = row0;
     return true;
   }
-  for (int j = job + s.n_groups; j < s.n_jobs; j += s.n_groups) {
+  for (int p2 = p + s.n_groups; p2 < s.n_pairs; p2 += s.n_groups) {
+    const int j = pair_job(s, p2, s.half);
+    if (j < 0) continue;
     const Job J = job_at(s, j);
-    if (J.tb + s.member < J.te) {
-      v0n = (J.tb + s.member) * kBV;
+    if (J.tb + s.sub < J.te) {
+      v0n = (J.tb + s.sub) * kBV;
       row0n = J.c * DG_CANVAS;
       return true;
     }
@@ -240,8 +295,8 @@ __device__ __forceinline__ bool next_tile(const Sched& s, int job, int tb, int t
 // A step: S^T tile (128 vocab x 256 rows) over all of d, in 32-wide chunks.  Wave w owns
 // rows [64w, 64w + 64): acc[mb][nb] is the 32x32 block (vocabulary block mb, row block nb).
 // LDS stage: E chunk [128 rows][4 x 16 B] then h chunk [256 rows][4 x 16 B]; 16-byte segment
-// s of row r sits at slot s ^ ((r >> 1) & 3), so that eight consecutive rows read at one
-// segment hit eight distinct bank groups.
+// s of row r sits at slot s ^ ((r >> 2) & 3), so that the sixteen consecutive rows one
+// ds_read_b128 cycle serves (256 bytes) hit sixteen distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------------------
 struct ALanes {
   uint32_t rdE0, rdE1;  // LDS read offsets of this lane's E fragment rows, k steps 0 and 1
@@ -254,13 +309,13 @@ struct ALanes {
 __device__ __forceinline__ ALanes a_lanes(int w, int d) {
   ALanes k;
   const int lane = threadIdx.x & 63, fr = lane & 31, fh = lane >> 5;
-  const int swz = (fr >> 1) & 3;
+  const int swz = (fr >> 2) & 3;
   k.rdE0 = fr * kRowA + 16 * ((0 + fh) ^ swz);
   k.rdE1 = fr * kRowA + 16 * ((2 + fh) ^ swz);
   k.rdH0 = kBV * kRowA + (64 * w + fr) * kRowA + 16 * ((0 + fh) ^ swz);
   k.rdH1 = kBV * kRowA + (64 * w + fr) * kRowA + 16 * ((2 + fh) ^ swz);
   k.dlrow = lane >> 2;
-  k.seg16 = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+  k.seg16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   k.offH = (uint32_t)k.dlrow * (2u * (uint32_t)d) + k.seg16;
   return k;
 }
@@ -554,51 +609,61 @@ __device__ __forceinline__ void stats_reset(RowStats& s) {
   s.gi = 0x7FFFFFFF;
 }
 
-// Position of the B role in its stream of stages: (heavy job, round, stage of the round).
+// Position of the B role in its stream of stages: (non-commit pair, round, stage of the
+// round).  A round of this half has 4 stages per tile it holds, none in the empty rounds at the
+// end of the shorter job of a pair (or all rounds of a pair without a job for this half).
 struct BCur {
-  int job, r, s, nst, ptb, tb, te, nr, c, vr;
+  int p, job, r, s, nst, ptb, tb, te, nr, c, vr;
   unsigned q;  // group round counter; ring slot and counter parity = q & 1
   bool valid;
 };
 
-__device__ __forceinline__ void b_load_job(BCur& u, const Sched& sc) {
-  u.valid = u.job < sc.n_heavy;
+__device__ __forceinline__ void b_round_set(BCur& u) {
+  const int n_in = (u.job >= 0 && u.ptb < u.te) ? min(kG, u.te - u.ptb) : 0;
+  u.nst = 4 * n_in;
+}
+
+__device__ __forceinline__ void b_load_pair(BCur& u, const Sched& sc) {
+  u.valid = u.p < sc.n_hpairs;
   if (!u.valid) return;
-  const Job J = job_at(sc, u.job);
+  const Job J = half_job(sc, u.p, u.job);
+  u.nr = pair_rounds(sc, u.p);
   u.c = J.c;
   u.vr = J.vr;
   u.tb = J.tb;
   u.te = J.te;
-  u.nr = J.nr;
   u.r = 0;
   u.s = 0;
   u.ptb = J.tb;
-  u.nst = 4 * min(kG, J.te - J.tb);
+  b_round_set(u);
 }
 
-__device__ __forceinline__ void b_advance(BCur& u, const Sched& sc) {
-  if (++u.s < u.nst) return;
+__device__ __forceinline__ void b_next_round(BCur& u, const Sched& sc) {
   u.s = 0;
   ++u.q;
   if (++u.r < u.nr) {
     u.ptb += kG;
-    u.nst = 4 * min(kG, u.te - u.ptb);
+    b_round_set(u);
     return;
   }
-  u.job += sc.n_groups;
-  b_load_job(u, sc);
+  u.p += sc.n_groups;
+  b_load_pair(u, sc);
 }
 
-__device__ __forceinline__ bool b_is_last(const BCur& u, const Sched& sc) {
-  return u.s == u.nst - 1 && u.r == u.nr - 1 && u.job + sc.n_groups >= sc.n_heavy;
+__device__ __forceinline__ void b_advance(BCur& u, const Sched& sc) {
+  if (++u.s < u.nst) return;
+  b_next_round(u, sc);
 }
 
 // Copies of one B stage: E rows [v0, v0 + 32) x columns [col0, col0 + 16 NCB) as NCB 1-KB
 // instructions (chunk c = 64 i + lane is row c / (2 NCB), 16-byte column chunk c % (2 NCB)),
-// dealt round-robin to the four B waves; then this wave's four probability fragments.
+// dealt round-robin to the four B waves; this wave's four probability fragments; and, by the
+// last wave (which has the fewest E copies), the 256 references of the tile.
 template <int NCB>
-__device__ __forceinline__ void b_issue(const uint16_t* E, const uint16_t* ring, int V, int d,
-                                        int col0, const BCur& u, uint32_t dst, int bw) {
+__device__ __forceinline__ void b_issue(const uint16_t* E, const uint16_t* ring,
+                                        const float* ring_ref, int V, int d, int col0,
+                                        int slot_tiles, int hoff, const BCur& u, uint32_t dst,
+                                        int bw) {
   const int lane = threadIdx.x & 63;
   const int g = u.s >> 2, kq = u.s & 3;
   const int v0 = (u.ptb + g) * kBV + kBQ * kq;
@@ -615,23 +680,31 @@ __device__ __forceinline__ void b_issue(const uint16_t* E, const uint16_t* ring,
                dst + 1024u * (uint32_t)i);
     }
   }
-  const uint16_t* pb = ring + ((size_t)(u.q & 1) * kG + g) * kTileElems;
+  const uint16_t* pb = ring + ((size_t)(u.q & 1) * slot_tiles + hoff + g) * kTileElems;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
     dma16(pb + ((4 * bw + rb) * 4 + kq) * 512, 16u * (uint32_t)lane,
           dst + (uint32_t)(NCB * 1024 + 4096 * bw + 1024 * rb));
+  if (bw == 3)
+    dma16(ring_ref + ((size_t)(u.q & 1) * slot_tiles + hoff + g) * DG_CANVAS, 16u * (uint32_t)lane,
+          dst + (uint32_t)(NCB * 1024 + 16384));
 }
 
+// One B stage.  A tile whose reference differs from the row maximum after the round (for
+// some row) has its fragments scaled by 2^(ref - M) per row, from the stage's copy of the
+// references.
 template <int NCB>
 __device__ __forceinline__ void b_compute(const lds_char* st, int bw, bool scaled,
-                                          const float* refg, const float* Mn,
-                                          f32x4 (&bacc)[4][NCB]) {
+                                          const float* Mn, f32x4 (&bacc)[4][NCB]) {
   const int lane = threadIdx.x & 63;
   u32x4 fa[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
     fa[rb] = lds_read16(st + NCB * 1024 + 4096 * bw + 1024 * rb + 16 * lane);
   if (scaled) {
+    const __attribute__((address_space(3))) float* refg =
+        reinterpret_cast<const __attribute__((address_space(3))) float*>(st + NCB * 1024 +
+                                                                          16384);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int row = 64 * bw + 16 * rb + (lane & 15);
@@ -663,7 +736,6 @@ __device__ __forceinline__ void vm_wait_n(int n) {
 struct SharedState {
   float sM[DG_CANVAS];        // group running row maximum (base 2) of job sMjob, for the A role
   float sMn[2][DG_CANVAS];    // per round parity: row maximum after the round
-  float sRs[2][DG_CANVAS];    // per round parity: accumulator rescale factor of the round
   int sMjob;                  // job the maxima in sM belong to (-1: none)
   int sMask[2];               // per round parity: tiles whose probabilities need scaling
   int sResc[2];               // per round parity: some row maximum grew
@@ -697,15 +769,16 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
     int ok = xcc < 8;
     unsigned slot = 0;
     if (ok) slot = atomicAdd(&f.sync[xcc], 1u);
-    ok = ok && slot < (unsigned)f.per_xcd;
-    const int gid = xcc * (f.per_xcd / kG) + (int)slot / kG;
+    const int gs = kG * f.halves;
+    ok = ok && slot < (unsigned)((f.per_xcd / gs) * gs);
+    const int gid = xcc * (f.per_xcd / gs) + (int)slot / gs;
     if (!ok || gid >= n_groups) {
       ok = 0;
       atomicOr(err, 2u);
     }
     ss.sInfo[0] = ok;
     ss.sInfo[1] = gid;
-    ss.sInfo[2] = (int)(slot % kG);
+    ss.sInfo[2] = (int)(slot % gs);
     ss.sInfo[3] = (int)f.sync[9];
     ss.barA = 0;
     ss.barB = 0;
@@ -717,6 +790,8 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
   if (!ss.sInfo[0]) return;
   const int gid = __builtin_amdgcn_readfirstlane(ss.sInfo[1]);
   const int member = __builtin_amdgcn_readfirstlane(ss.sInfo[2]);
+  const int halves = f.halves;
+  const int slot_tiles = kG * halves;  // tiles per ring slot
   Sched sc;
   sc.order = f.order;
   sc.s_v = s_v;
@@ -725,11 +800,17 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
   sc.n_jobs = n_canvas * s_v;
   sc.n_heavy = sc.n_nc * s_v;
   sc.n_groups = n_groups;
-  sc.member = member;
+  sc.halves = halves;
+  sc.half = member / kG;
+  sc.sub = member % kG;
+  sc.n_hpairs = (sc.n_heavy + halves - 1) / halves;
+  sc.n_pairs = sc.n_hpairs + (sc.n_jobs - sc.n_heavy + halves - 1) / halves;
+  const int sub = sc.sub, hoff = sc.half * kG;
+  const unsigned per_round = 64u * (unsigned)halves;  // counter increments per round
   unsigned* produced = f.sync + 16 + 4 * gid;
   unsigned* consumed = produced + 2;
-  uint16_t* ring = f.ring + (size_t)gid * 2 * kG * kTileElems;
-  float* ring_ref = f.ring_ref + (size_t)gid * 2 * kG * DG_CANVAS;
+  uint16_t* ring = f.ring + (size_t)gid * 2 * slot_tiles * kTileElems;
+  float* ring_ref = f.ring_ref + (size_t)gid * 2 * slot_tiles * DG_CANVAS;
   int gen = 0;  // this wave's role-barrier generation
 
   if (w < 4) {
@@ -748,23 +829,26 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
     APipe pipe{0, false};
     unsigned rr = 0;  // heavy rounds of this group so far
     f32x16 acc[4][2];
-    for (int job = gid; job < sc.n_jobs; job += n_groups) {
-      const Job J = job_at(sc, job);
+    for (int pr = gid; pr < sc.n_pairs; pr += n_groups) {
+      int job;
+      const Job J = half_job(sc, pr, job);
+      const bool heavy = pr < sc.n_hpairs;
+      const int nr = heavy ? pair_rounds(sc, pr) : J.nr;
       const int row0 = J.c * DG_CANVAS;
       const float c2 = kLog2e / temperature[J.c];
       const uint32_t step = (uint32_t)steps[J.c];
       RowStats st0, st1;
       stats_reset(st0);
       stats_reset(st1);
-      for (int r = 0; r < J.nr; ++r) {
-        const int tile = J.tb + r * kG + member;
+      for (int r = 0; r < nr; ++r) {
+        const int tile = J.tb + r * kG + sub;
         const bool valid = tile < J.te;
         const int vt0 = tile * kBV;
         const bool full = vt0 + kBV <= V;
-        if (J.commit) {
+        if (!heavy) {
           if (!valid) break;
           int v0n = 0, row0n = 0;
-          const bool hn = next_tile(sc, job, J.tb, J.te, row0, r, v0n, row0n);
+          const bool hn = next_tile(sc, pr, J.tb, J.te, row0, r, v0n, row0n);
           if (!a_logits(E, h, V, d, vt0, row0, hn, v0n, row0n, pipe, (lds_char*)smem_a, w, k,
                         acc, &ss.barA, gen, err))
             return;
@@ -777,13 +861,13 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
         }
         const unsigned par = rr & 1;
         // ring slot par is free once every B wave of the group has consumed round rr - 2
-        if (rr >= 2 && !wave_wait(consumed + par, 64u * (rr >> 1), err)) {
+        if (rr >= 2 && !wave_wait(consumed + par, per_round * (rr >> 1), err)) {
           vm_wait<0>();
           return;
         }
         if (valid) {
           int v0n = 0, row0n = 0;
-          const bool hn = next_tile(sc, job, J.tb, J.te, row0, r, v0n, row0n);
+          const bool hn = next_tile(sc, pr, J.tb, J.te, row0, r, v0n, row0n);
           if (!a_logits(E, h, V, d, vt0, row0, hn, v0n, row0n, pipe, (lds_char*)smem_a, w, k,
                         acc, &ss.barA, gen, err))
             return;
@@ -803,8 +887,8 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
           const float M1 = mine ? ss.sM[64 * w + 32 + fr] : -INFINITY;
           e.ref0 = fmaxf(M0, mt[0]);
           e.ref1 = fmaxf(M1, mt[1]);
-          char* ring_out =
-              reinterpret_cast<char*>(ring + ((size_t)par * kG + member) * kTileElems);
+          char* ring_out = reinterpret_cast<char*>(
+              ring + ((size_t)par * slot_tiles + hoff + sub) * kTileElems);
           epi_pieces(acc, e, full, vt0, V, c2, row0, step, k0, k1, ring_out);
           e.ls0 += xor_f(e.ls0, 32);
           e.as0 += xor_f(e.as0, 32);
@@ -812,7 +896,7 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
           e.ls1 += xor_f(e.ls1, 32);
           e.as1 += xor_f(e.as1, 32);
           argmax_merge(e.gv1, e.gi1, xor_f(e.gv1, 32), xor_i(e.gi1, 32));
-          float* rout = ring_ref + ((size_t)par * kG + member) * DG_CANVAS;
+          float* rout = ring_ref + ((size_t)par * slot_tiles + hoff + sub) * DG_CANVAS;
           if (lane < 32) {
             rout[64 * w + fr] = e.ref0;
             rout[64 * w + 32 + fr] = e.ref1;
@@ -827,8 +911,8 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
         wave_signal(produced + par);
         ++rr;
       }
-      if (lane < 32) {
-        const size_t o0 = ((size_t)J.vr * kG + member) * R + row0 + 64 * w + fr;
+      if (job >= 0 && lane < 32) {
+        const size_t o0 = ((size_t)J.vr * kG + sub) * R + row0 + 64 * w + fr;
         const size_t o1 = o0 + 32;
         st_amv[o0] = st0.amv;
         st_ami[o0] = st0.ami;
@@ -853,29 +937,30 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
   // ================================ B role ================================
   const int bw = w - 4;
   const int tbt = t - 256;  // 0..255: the row this thread maintains
-  const int col0 = member * DS;
-  const int nB = (NCB - bw + 3) / 4 + 4;  // copies per stage of this wave
+  const int col0 = sub * DS;
+  const int nB = (NCB - bw + 3) / 4 + 4 + (bw == 3);  // copies per stage of this wave
   float* accp = f.accp;
   float* accM = f.accM;
   const uint32_t bbase = lds_addr((lds_char*)smem_b);
   BCur cu;
-  cu.job = gid;
+  cu.p = gid;
   cu.q = 0;
-  b_load_job(cu, sc);
+  b_load_pair(cu, sc);
   if (!cu.valid) return;
   BCur iu = cu;
   int s_issue = 0, s_comp = 0;
+  int inflight = 0;  // stages issued and not yet computed
   f32x4 bacc[4][NCB];
   int mask = 0;
   bool bad = false;
 
-  // Start of round iu (at issue time, two stages before it is computed): wait for its data,
+  // Start of a round (at issue time, two stages before it is computed): wait for its data,
   // then fold its tile references into the row maxima of this thread's row.
   auto round_prep = [&](const BCur& u) -> bool {
     const unsigned par = u.q & 1;
-    if (!wave_wait(produced + par, 64u * ((u.q >> 1) + 1), err)) return false;
+    if (!wave_wait(produced + par, per_round * ((u.q >> 1) + 1), err)) return false;
     asm volatile("buffer_inv sc0" ::: "memory");
-    const float* ref = ring_ref + (size_t)par * kG * DG_CANVAS + tbt;
+    const float* ref = ring_ref + ((size_t)par * slot_tiles + hoff) * DG_CANVAS + tbt;
     const int n_in = u.nst >> 2;
     float rv[kG];
 #pragma unroll
@@ -888,37 +973,53 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
 #pragma unroll
     for (int g = 0; g < kG; ++g) m |= (g < n_in && rv[g] != mn) ? (1 << g) : 0;
     ss.sMn[par][tbt] = mn;
-    ss.sRs[par][tbt] = (mo == -INFINITY) ? 0.0f : hw_exp2(mo - mn);
     if (m) atomicOr(&ss.sMask[par], m);
     if (mo != -INFINITY && mn != mo) atomicOr(&ss.sResc[par], 1);
     return true;
   };
+  // Issue the next stage of the stream (empty rounds carry none).
   auto issue_next = [&]() -> bool {
+    while (iu.valid && iu.nst == 0) b_next_round(iu, sc);
     if (!iu.valid) return true;
     if (iu.s == 0 && !round_prep(iu)) return false;
-    b_issue<NCB>(E, ring, V, d, col0, iu, bbase + s_issue * kStageB, bw);
+    b_issue<NCB>(E, ring, ring_ref, V, d, col0, slot_tiles, hoff, iu,
+                 bbase + s_issue * kStageB, bw);
     s_issue = stage_add1(s_issue);
+    ++inflight;
     b_advance(iu, sc);
     return true;
   };
 
-  bool ok = issue_next() && issue_next();
+  // Empty rounds of this half: nothing to read, but the counts stay exact (a round is counted
+  // as consumed only once it has been published).  Run where the compute cursor enters them,
+  // outside the stage body, which keeps the accumulators on one path.
+  auto skip_empty = [&]() -> bool {
+    while (cu.valid && cu.nst == 0) {
+      const unsigned par = cu.q & 1;
+      if (!wave_wait(produced + par, per_round * ((cu.q >> 1) + 1), err)) return false;
+      if (lane == 0) atomicAdd(consumed + par, 1u);
+      b_next_round(cu, sc);
+    }
+    return true;
+  };
+
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb] = f32x4{0, 0, 0, 0};
+  bool ok = issue_next() && issue_next() && skip_empty();
   while (ok && cu.valid) {
-    const bool last = b_is_last(cu, sc);
-    if (last)
-      vm_wait<0>();
-    else
+    const unsigned par = cu.q & 1;
+    // this wave's copies of the stage have landed (the next stage may still be in flight)
+    if (inflight >= 2)
       vm_wait_n(nB);
+    else
+      vm_wait<0>();
     role_bar(&ss.barB, gen, err, bad);
     if (bad || !issue_next()) break;
-    const unsigned par = cu.q & 1;
     if (cu.s == 0) {
       if (cu.r == 0) {
-        // new job: zero the accumulators, publish the maxima under the new job id
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb] = f32x4{0, 0, 0, 0};
+        // new job: publish the maxima under the new job id (the accumulators start at zero)
         if (tbt == 0) __hip_atomic_store(&ss.sMjob, -1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         role_bar(&ss.barB, gen, err, bad);
         ss.sM[tbt] = ss.sMn[par][tbt];
@@ -929,12 +1030,14 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
         ss.sM[tbt] = ss.sMn[par][tbt];
       }
       mask = ss.sMask[par];
-      if (ss.sResc[par]) {
+      if (cu.r != 0 && ss.sResc[par]) {
+        // the previous round of this job left its maxima in the other parity
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float sf = ss.sRs[par][64 * bw + 16 * rb + 4 * (lane >> 4) + i];
+            const int row = 64 * bw + 16 * rb + 4 * (lane >> 4) + i;
+            const float sf = hw_exp2(ss.sMn[par ^ 1][row] - ss.sMn[par][row]);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb][i] *= sf;
           }
@@ -945,13 +1048,14 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
       ss.sResc[par] = 0;
     }
     const int g = cu.s >> 2;
-    b_compute<NCB>((lds_char*)smem_b + s_comp * kStageB, bw, (mask >> g) & 1,
-                   ring_ref + ((size_t)par * kG + g) * DG_CANVAS, ss.sMn[par], bacc);
+    b_compute<NCB>((lds_char*)smem_b + s_comp * kStageB, bw, (mask >> g) & 1, ss.sMn[par],
+                   bacc);
+    --inflight;
     if (cu.s == cu.nst - 1) {
       // this wave's reads of the round's ring slot are complete
       if (lane == 0) atomicAdd(consumed + par, 1u);
-      if (cu.r == cu.nr - 1) {
-        // expectation partial of this (range, slice) and the final maxima
+      if (cu.r == cu.nr - 1 || cu.ptb + kG >= cu.te) {
+        // last round of the job: expectation partial of this (range, slice), final maxima
         float* out = accp + (size_t)cu.vr * R * d;
         const int row0 = cu.c * DG_CANVAS;
 #pragma unroll
@@ -963,11 +1067,16 @@ __global__ __launch_bounds__(512, 1) void k_vp_fused(Fused f) {
             for (int cb = 0; cb < NCB; ++cb)
               out[(size_t)(row0 + row) * d + col0 + 16 * cb + (lane & 15)] = bacc[rb][cb][i];
           }
-        if (member == 0) accM[(size_t)cu.vr * R + row0 + tbt] = ss.sMn[par][tbt];
+        if (sub == 0) accM[(size_t)cu.vr * R + row0 + tbt] = ss.sMn[par][tbt];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) bacc[rb][cb] = f32x4{0, 0, 0, 0};
       }
     }
     s_comp = stage_add1(s_comp);
     b_advance(cu, sc);
+    ok = skip_empty();
   }
   vm_wait<0>();
 }
@@ -1089,10 +1198,11 @@ FusedPlan fused_plan(int n_canvas, int V, int d, int n_wg) {
   FusedPlan p{};
   p.n_wg = n_wg;
   p.per_xcd = n_wg / 8;
-  p.n_groups = 8 * (p.per_xcd / kG);
+  p.halves = p.per_xcd >= 2 * kG ? 2 : 1;
+  p.n_groups = 8 * (p.per_xcd / (kG * p.halves));
   p.R = (size_t)n_canvas * DG_CANVAS;
   p.n_tiles = (V + kBV - 1) / kBV;
-  int sv = (p.n_groups + n_canvas - 1) / n_canvas;
+  int sv = (p.n_groups * p.halves + n_canvas - 1) / n_canvas;
   if (sv < 2) sv = 2;
   if (sv > p.n_tiles) sv = p.n_tiles;
   if (sv > 64) sv = 64;
@@ -1103,9 +1213,9 @@ FusedPlan fused_plan(int n_canvas, int V, int d, int n_wg) {
   p.off_order = off;
   off += al256((size_t)n_canvas * 4);
   p.off_ring = off;
-  off += al256((size_t)p.n_groups * 2 * kG * kTileElems * 2);
+  off += al256((size_t)p.n_groups * 2 * kG * p.halves * kTileElems * 2);
   p.off_ring_ref = off;
-  off += al256((size_t)p.n_groups * 2 * kG * DG_CANVAS * 4);
+  off += al256((size_t)p.n_groups * 2 * kG * p.halves * DG_CANVAS * 4);
   p.off_st = off;
   off += 7 * al256((size_t)p.s_v * kG * p.R * 4);
   p.off_accp = off;
@@ -1139,6 +1249,7 @@ hipError_t fused_launch(const VocabArgs& a, const FusedPlan& p, void* workspace,
   f.s_v = p.s_v;
   f.n_groups = p.n_groups;
   f.per_xcd = p.per_xcd;
+  f.halves = p.halves;
   hipLaunchKernelGGL(k_vp_fused_init, dim3(1), dim3(256), 0, stream, f.sync,
                      16 + 4 * p.n_groups, reinterpret_cast<int*>(b + p.off_order), a.commit,
                      a.n_canvas);
