@@ -24,9 +24,12 @@ dg_status hip_fail(hipError_t e, const char* what) {
   return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Path of the vocabulary pass: the fused cooperative kernel when its tiling covers d and the
-// device holds at least one 16-workgroup group per XCD; otherwise the split kernels.
-// DG_VOCAB_PATH=split forces the split kernels (used by the tests to cover both).
+// Path of the vocabulary pass.  Default: the two-GEMM path (every d % 64 == 0).
+// DG_VOCAB_PATH=fused selects the cooperative single-kernel path (when its tiling covers d
+// and the device holds a 16-workgroup group per XCD), DG_VOCAB_PATH=split the four-kernel
+// path with fp32 tile weights.  The tests run all three.
+enum Path { kGemm, kFused, kSplit };
+
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -34,20 +37,25 @@ int device_cu_count() {
   return n;
 }
 
-bool use_fused(int d, int* n_wg) {
+Path pick_path(int d, int* n_wg) {
   const char* e = getenv("DG_VOCAB_PATH");
-  if (e != nullptr && strcmp(e, "split") == 0) return false;
-  if (!dg::fused_supported(d)) return false;
-  int n = device_cu_count();
-  if (n <= 0) n = 256;  // sizing without a device: MI355X
-  *n_wg = n;
-  return (n / 8) >= 16;
+  if (e != nullptr && strcmp(e, "split") == 0) return kSplit;
+  if (e != nullptr && strcmp(e, "fused") == 0 && dg::fused_supported(d)) {
+    int n = device_cu_count();
+    if (n <= 0) n = 256;  // sizing without a device: MI355X
+    *n_wg = n;
+    if ((n / 8) >= 16) return kFused;
+  }
+  return dg::gemm_supported(d) ? kGemm : kSplit;
 }
 
 size_t plan_bytes(int n_canvas, int V, int d) {
   int n_wg = 0;
-  if (use_fused(d, &n_wg)) return dg::fused_plan(n_canvas, V, d, n_wg).bytes;
-  return dg::vocab_plan(n_canvas, V, d).bytes;
+  switch (pick_path(d, &n_wg)) {
+    case kGemm: return dg::gemm_plan(n_canvas, V, d).bytes;
+    case kFused: return dg::fused_plan(n_canvas, V, d, n_wg).bytes;
+    default: return dg::vocab_plan(n_canvas, V, d).bytes;
+  }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -135,10 +143,20 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
   a.gumbel_tok = gumbel_tok;
   a.selfcond = selfcond;
   int n_wg = 0;
-  const hipError_t e =
-      use_fused(d, &n_wg)
-          ? dg::fused_launch(a, dg::fused_plan(n_canvas, V, d, n_wg), workspace, (hipStream_t)stream)
-          : dg::vocab_pass_launch(a, dg::vocab_plan(n_canvas, V, d), workspace, (hipStream_t)stream);
+  hipError_t e;
+  switch (pick_path(d, &n_wg)) {
+    case kGemm:
+      e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, (hipStream_t)stream);
+      break;
+    case kFused:
+      e = dg::fused_launch(a, dg::fused_plan(n_canvas, V, d, n_wg), workspace,
+                           (hipStream_t)stream);
+      break;
+    default:
+      e = dg::vocab_pass_launch(a, dg::vocab_plan(n_canvas, V, d), workspace,
+                                (hipStream_t)stream);
+      break;
+  }
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
 }

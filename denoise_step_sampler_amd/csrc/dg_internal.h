@@ -56,6 +56,24 @@ struct VocabPlan {
 
 VocabPlan vocab_plan(int n_canvas, int V, int d);
 
+// Two-GEMM path (vocab_gemm.hip), the default.
+struct GemmPlan {
+  size_t R;
+  int n_tiles;    // vocabulary tiles of 256
+  size_t vpad;    // n_tiles * 256
+  int ncb;        // 16-column blocks per wave of the expectation pass
+  int n_range;    // vocabulary ranges of the expectation pass
+  int n_colblk;   // column blocks of the expectation pass
+  int n_rounds;   // canvas rounds of the logits pass (256 workgroups each)
+  int n_units_xcd;  // expectation units per XCD at most
+  size_t off_small, off_P, off_ref, off_st, off_accp, off_accM;
+  size_t bytes;
+};
+bool gemm_supported(int d);
+GemmPlan gemm_plan(int n_canvas, int V, int d);
+hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
+                       hipStream_t stream);
+
 // Fused cooperative path (vocab_fused.hip).
 struct FusedPlan {
   int n_wg;       // workgroups launched (one per CU)

@@ -126,22 +126,16 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
 
 // ---------------------------------------------------------------------------------------
 // LDS DMA.  One instruction: lane l copies the 16 bytes at base + off (off per lane, base
-// wave-uniform) to LDS byte address dst + 16 l (dst wave-uniform, through M0).  The
-// non-temporal form is used for the E stream, which no workgroup of this XCD re-reads soon,
-// so that it does not push the hidden states and the probability ring out of L2.  M0 is free
-// between instructions on gfx9 and later (LDS instructions no longer read it); the one-cycle
-// nop covers the M0 -> LDS DMA hazard.
+// wave-uniform) to LDS byte address dst + 16 l (dst wave-uniform, through M0).  Every stream,
+// E included, uses the ordinary cached form: an E line is read by several workgroups of the
+// same XCD (the two halves, and the B role after the A role), and the non-temporal form was
+// measured to lose those L2 hits.  M0 is free between instructions on gfx9 and later (LDS
+// instructions no longer read it); the one-cycle nop covers the M0 -> LDS DMA hazard.
 // ---------------------------------------------------------------------------------------
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(dst)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(off), "s"(base), "s"(dst)
                : "memory", "m0");
@@ -332,7 +326,7 @@ __device__ __forceinline__ void a_issue(const uint16_t* E, const uint16_t* h, in
     const int rb = v0 + 32 * w + 16 * j;
     const int br = min(rb, V - 1);
     const int rv = min(rb + k.dlrow, V - 1);
-    dma16_nt(E + (size_t)br * d + kc * kKC, (uint32_t)(rv - br) * pitch + k.seg16,
+    dma16(E + (size_t)br * d + kc * kKC, (uint32_t)(rv - br) * pitch + k.seg16,
              dst + 1024u * (uint32_t)(2 * w + j));
   }
 #pragma unroll
@@ -676,7 +670,7 @@ __device__ __forceinline__ void b_issue(const uint16_t* E, const uint16_t* ring,
       const int c = 64 * i + lane;
       const int row = c / (2 * NCB), cc = c - row * (2 * NCB);
       const int rv = min(v0 + row, V - 1);
-      dma16_nt(eb, (uint32_t)(rv - br) * (2u * (uint32_t)d) + 16u * (uint32_t)cc,
+      dma16(eb, (uint32_t)(rv - br) * (2u * (uint32_t)d) + 16u * (uint32_t)cc,
                dst + 1024u * (uint32_t)i);
     }
   }

@@ -1,0 +1,966 @@
+// Vocabulary pass as two streamed GEMMs for gfx950 (the default path).
+//
+// The pass computes, per row r of h and temperature T_c of its canvas c, the logits
+// S = h E^T (tied unembedding, "DiffusionGemma Technical Report" sec. 3.2 eq. (5)), the
+// tempered softmax p = softmax(S / T_c) with its log-partition and entropy ("DiffusionGemma
+// Explained", Sampling), the argmax of S and the Gumbel-max sample argmax(S / T_c + g) (the
+// vLLM sampler step), and the self-conditioning expectation sum_v p_v E_v (eq. (6) of the
+// report, the argument of FFW).  d = 2816 makes the expectation's accumulator of one
+// canvas 256 x 2816 fp32 (2.9 MB): it cannot live beside the logits tile in one CU, so the
+// pass runs as two contractions over the same E:
+//
+//   k_gemm_logits   S^T tile = E_t h_c^T (256 vocabulary x 256 rows of one canvas, bf16
+//                   MFMA 32x32x16, fp32 accumulate over all of d) and its epilogue: per row
+//                   and 128-entry half tile the integer reference ref = ceil(max z2)
+//                   (z2 = S log2(e) / T), the online-softmax partial (sum 2^(z2 - ref),
+//                   entropy moment), argmax and Philox Gumbel key; the weights 2^(z2 - ref)
+//                   in (0, 1] go to HBM as bf16 (one rounding), with the reference beside
+//                   them.  The fp32 logits never leave the registers.
+//   k_gemm_selfcond acc[256 rows, BN columns] += P~ E over one vocabulary range (bf16 MFMA
+//                   16x16x32).  Each weight fragment is brought to the range's reference
+//                   M = max ref by subtracting (M - ref) from its bf16 exponent field with
+//                   unsigned saturation (v_pk_sub_u16 clamp): an exact power-of-two scaling
+//                   (flush to zero below 2^-126), so every weight is rounded to bf16 once.
+//   k_gemm_combine  per row: merges the statistic partials (max/sum/moment merge of the
+//                   chunked logsumexp in "DiffusionGemma-Lite", (value, -index) max for the
+//                   tokens) and sums the expectation partials with weights 2^(M_s - m) / l.
+//
+// Both GEMMs are persistent (one 512-thread workgroup per CU), stage operands through LDS
+// by LDS DMA (global_load_lds_dwordx4, 1 KB per instruction) into two 64-element K stages,
+// and interleave the DMA issue and the fragment reads with the MFMAs.  Work is mapped to
+// the eight XCDs so that the CUs of one XCD share operands through their L2: the logits
+// pass runs up to two canvases per XCD over the same vocabulary tiles (h of both canvases
+// stays in L2, each E line is read by both), the expectation pass runs the column blocks
+// of one (range, canvas) pair on one XCD (the weights are read once from HBM, E of the
+// range by every canvas of the XCD).
+#include <stdlib.h>
+#include <string.h>
+
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 256;      // vocabulary tile of the logits pass (and rows per canvas)
+constexpr int kHalf = 128;      // granularity of the weight references
+constexpr int kKC = 64;         // K chunk (elements) per LDS stage
+constexpr int kRow = 2 * kKC;   // bytes of one staged row: one 128-byte line
+constexpr int kLanesMax = 256;  // vocabulary lanes per canvas at most (one canvas per GPU)
+constexpr int kWG = 256;        // persistent workgroups
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_dst, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// 16-byte slot of segment s in staged row r: XOR swizzle over the eight segments of the
+// 128-byte row, so that the rows one ds_read_b128 pass serves fall on distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// ---------------------------------------------------------------------------------------
+// Schedule of the logits pass.  Canvases are taken in `order` (non-commit first) in rounds
+// of g = a power of two <= 16; a round gives each canvas L = 256 / g vocabulary lanes, and
+// lane l of a canvas processes tiles l, l + L, l + 2L, ...  Workgroup b runs on XCD b % 8
+// (the dispatcher deals workgroups to the XCDs round-robin), slot b / 8:
+//   g >= 8: canvas k = 8 (slot % (g/8)) + xcd, lane = slot / (g/8)   (g/8 canvases per XCD)
+//   g <  8: canvas k = xcd % g,                lane = 32 (xcd / g) + slot
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int round_size(int remaining) {
+  int g = 16;
+  while (g > remaining) g >>= 1;
+  return g;
+}
+
+struct Lane {
+  int k;     // canvas within the round
+  int lane;  // vocabulary lane
+  int L;     // lanes per canvas
+};
+
+__device__ __forceinline__ Lane lane_of(int b, int g) {
+  const int x = b & 7, s = b >> 3;
+  Lane r;
+  r.L = kWG / g;
+  if (g >= 8) {
+    const int per = g / 8;
+    r.k = 8 * (s % per) + x;
+    r.lane = s / per;
+  } else {
+    r.k = x % g;
+    r.lane = 32 * (x / g) + s;
+  }
+  return r;
+}
+
+// Lanes per canvas of the canvas at position pos of the order (same rounds as above).
+__device__ __forceinline__ int lanes_at(int pos, int n_canvas) {
+  int start = 0;
+  for (;;) {
+    const int g = round_size(n_canvas - start);
+    if (pos < start + g) return kWG / g;
+    start += g;
+  }
+}
+
+// Running statistics of one row over the tiles of a lane (base-2 units): reference m, sum
+// l = sum 2^(z2 - m), moment a = sum 2^(z2 - m) (z2 - m), and lb = the same sum over the
+// bf16-rounded weights the expectation pass multiplies (its normaliser).
+struct RowAcc {
+  float m, l, a, lb, amv, gv;
+  int ami, gi;
+  float tm[4];  // the four largest half-tile maxima of z2 (descending) ...
+  int tv[4];    // ... and their vocabulary entries
+};
+// Keeps the four largest (z2, -v) pairs in descending order (bubble insertion, no branches).
+__device__ __forceinline__ void top4_insert(float (&tm)[4], int (&tv)[4], float m, int v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool take = (m > tm[k]) | ((m == tm[k]) & (v < tv[k]));
+    const float om = tm[k];
+    const int ov = tv[k];
+    tm[k] = take ? m : om;
+    tv[k] = take ? v : ov;
+    m = take ? om : m;
+    v = take ? ov : v;
+  }
+}
+__device__ __forceinline__ void row_acc_reset(RowAcc& s) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    s.tm[k] = -INFINITY;
+    s.tv[k] = 0x7FFFFFFF;
+  }
+  s.m = -INFINITY;
+  s.l = 0.0f;
+  s.lb = 0.0f;
+  s.a = 0.0f;
+  s.amv = -INFINITY;
+  s.gv = -INFINITY;
+  s.ami = 0x7FFFFFFF;
+  s.gi = 0x7FFFFFFF;
+}
+
+// Online-softmax merge (base 2) carrying the rounded-weight sum along with the exact one.
+__device__ __forceinline__ void lse_merge_b(float& m, float& l, float& a, float& lb, float m2,
+                                            float l2, float a2, float lb2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  const float d1 = m - M, d2 = m2 - M;
+  const float s1 = (m == -INFINITY) ? 0.0f : hw_exp2(d1);
+  const float s2 = (m2 == -INFINITY) ? 0.0f : hw_exp2(d2);
+  const float t1 = (m == -INFINITY) ? 0.0f : s1 * (a + d1 * l);
+  const float t2 = (m2 == -INFINITY) ? 0.0f : s2 * (a2 + d2 * l2);
+  l = s1 * l + s2 * l2;
+  lb = s1 * lb + s2 * lb2;
+  a = t1 + t2;
+  m = M;
+}
+
+// ---------------------------------------------------------------------------------------
+// Logits pass.
+// ---------------------------------------------------------------------------------------
+struct GemmK {
+  VocabArgs a;
+  const int* order;   // [n_canvas] canvases, non-commit first
+  const int* pos;     // [n_canvas] position of each canvas in order
+  const int* n_nc_p;  // number of non-commit canvases
+  uint16_t* P;        // bf16 weights 2^(z2 - ref) in MFMA-fragment order: 1 KB blocks
+                      // [row / 16][v / 32], entry (row, v) at 8 (row % 16 + 16 ((v % 32) / 8))
+                      // + v % 8 of its block; row = 256 pos + i
+  int* ref;           // [n_half][R] integer references (base-2 units), row = 256 pos + i
+  float* st_m;        // [2 * kLanesMax][R] statistic partials (slot = 2 lane + half)
+  float* st_l;
+  float* st_lb;
+  float* st_tm;       // [4][2 * kLanesMax][R] top-4 half-tile maxima (z2) and their entries
+  int* st_tv;
+  float* st_a;
+  float* st_amv;
+  int* st_ami;
+  float* st_gv;
+  int* st_gi;
+  float* accp;        // [n_range][R][d] expectation partials, row = 256 pos + i
+  float* accM;        // [n_range][R] their references
+  int n_tiles;        // vocabulary tiles of 256
+  size_t vpad;        // n_tiles * 256
+  int n_range;        // vocabulary ranges of the expectation pass
+  int ncb;            // 16-column blocks per wave in the expectation pass
+  int n_colblk;       // d / (32 ncb)
+};
+
+// Per-lane epilogue of one row (32-row block of this wave) over the wave's 128 entries: the
+// lane holds 64 of them in s0..s3 (entry vt0 + 32 mb + 8 (i / 4) + 4 (lane / 32) + i % 4),
+// lane ^ 32 the other 64.  kHeavy: the full epilogue; otherwise only the argmax.
+// z2 = S c2 and dz = z2 - ref are rounded separately (no contraction), so that the
+// combine can recompute the weight of a half tile's maximum bit for bit.
+// pt: this lane's 8-byte group in the weight block of the half tile's first 32 entries.
+template <bool kHeavy>
+__device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, const f32x16& s2,
+                                        const f32x16& s3, int vt0, int V, float c2,
+                                        uint32_t row, uint32_t step, uint32_t k0, uint32_t k1,
+                                        uint16_t* pt, int* ref_out, RowAcc& st) {
+  const int lane = threadIdx.x & 63;
+  const int vb0 = vt0 + 4 * (lane >> 5);
+  float m = -INFINITY, amv = -INFINITY;
+  int ami = 0x7FFFFFFF;
+  auto scan = [&](const f32x16& sb, int vb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int v = vb + 8 * (i >> 2) + (i & 3);
+      const float x = v < V ? sb[i] : -INFINITY;
+      argmax_merge(amv, ami, x, v);
+      m = fmaxf(m, __fmul_rn(x, c2));
+    }
+  };
+  scan(s0, vb0);
+  scan(s1, vb0 + 32);
+  scan(s2, vb0 + 64);
+  scan(s3, vb0 + 96);
+  m = fmaxf(m, xor_f(m, 32));
+  argmax_merge(amv, ami, xor_f(amv, 32), xor_i(ami, 32));
+  argmax_merge(st.amv, st.ami, amv, ami);
+  if (!kHeavy) return;
+  // integer reference >= every z2 of the half tile (clamped to +-2^24 so that differences
+  // of references stay exact integers)
+  const bool empty = (m == -INFINITY);
+  const float ref = empty ? 0.0f : fminf(fmaxf(ceilf(m), -16777216.0f), 16777216.0f);
+  // the half tile's maximum (its entry is the argmax of S: c2 > 0) joins the row's top four
+  if (!empty) top4_insert(st.tm, st.tv, m, ami);
+  float ls = 0.0f, as = 0.0f, lsb = 0.0f, gv = -INFINITY;
+  int gi = 0x7FFFFFFF;
+  auto block = [&](const f32x16& sb, int vbb, uint16_t* pbk) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int vb = vbb + 8 * q;
+      const u32x4 wd = philox4x32_10(u32x4{(uint32_t)vb >> 2, row, step, kTagGumbel}, k0, k1);
+      float pv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = vb + j < V;
+        const float z2 = __fmul_rn(sb[4 * q + j], c2);
+        const float dz = __fsub_rn(z2, ref);
+        const float pe = ok ? hw_exp2(dz) : 0.0f;
+        ls += pe;
+        as += ok ? pe * dz : 0.0f;
+        argmax_merge(gv, gi, ok ? z2 + gumbel2_from_word(wd[j]) : -INFINITY, vb + j);
+        pv[j] = pe;
+      }
+      const uint32_t w01 = pack_bf16x2(pv[0], pv[1]), w23 = pack_bf16x2(pv[2], pv[3]);
+      lsb += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+      *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
+    }
+  };
+  // one 32-entry block at a time (a run-time loop: the Philox streams of the blocks would
+  // otherwise be interleaved by the scheduler at a high register cost)
+#pragma unroll 1
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x16 sb;
+    switch (mb) {
+      case 0: sb = s0; break;
+      case 1: sb = s1; break;
+      case 2: sb = s2; break;
+      default: sb = s3; break;
+    }
+    block(sb, vb0 + 32 * mb, pt + 512 * mb);
+  }
+  ls += xor_f(ls, 32);
+  as += xor_f(as, 32);
+  lsb += xor_f(lsb, 32);
+  argmax_merge(gv, gi, xor_f(gv, 32), xor_i(gi, 32));
+  if (lane < 32) *ref_out = empty ? INT32_MIN : (int)ref;
+  lse_merge_b(st.m, st.l, st.a, st.lb, empty ? -INFINITY : ref, ls, as, lsb);
+  argmax_merge(st.gv, st.gi, gv, gi);
+}
+
+// Round r of the canvas order: canvases [start, start + g).  Rounds of 16 while 16 or more
+// remain, then the binary decomposition of the rest (8, 4, 2, 1).
+__device__ __forceinline__ void round_info(int r, int n_canvas, int& start, int& gsz) {
+  const int full = n_canvas / 16;
+  if (r < full) {
+    start = 16 * r;
+    gsz = 16;
+    return;
+  }
+  start = 16 * full;
+  int rem = n_canvas - start, k = r - full;
+  for (int gg = 8; gg >= 1; gg >>= 1) {
+    if (rem & gg) {
+      if (k == 0) {
+        gsz = gg;
+        return;
+      }
+      --k;
+      start += gg;
+    }
+  }
+  gsz = 0;
+}
+
+// One workgroup per (round, slot): the tiles t = lane, lane + L, ... of one canvas.
+__global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
+  constexpr int kStage = 512 * kRow;  // 256 E rows + 256 h rows
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  const uint16_t* E = g.a.E;
+  const uint16_t* h = g.a.h;
+  const int V = g.a.V, d = g.a.d, n_canvas = g.a.n_canvas;
+  const int t = threadIdx.x, lane = t & 63, fr = lane & 31, fh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int vh = w & 1, rq = w >> 1;  // wave tile: vocabulary half vh x rows [64 rq, 64 rq + 64)
+  const int T = g.n_tiles;
+  const int nk = d / kKC;
+  const size_t R = (size_t)n_canvas * kTile;
+
+  int start, gsz;
+  round_info(blockIdx.x >> 8, n_canvas, start, gsz);
+  const Lane ln = lane_of(blockIdx.x & 255, gsz);
+  if (gsz == 0 || ln.lane >= T) return;
+  const int c = __builtin_amdgcn_readfirstlane(g.order[start + ln.k]);
+  const int p = __builtin_amdgcn_readfirstlane(g.pos[c]);
+  const bool heavy = p < *g.n_nc_p;
+
+  // LDS fragment offsets (stage-relative) of this lane for the four 16-wide K steps
+  const int sw = swz(fr);
+  uint32_t rdE[4], rdH[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    rdE[ks] = (uint32_t)((128 * vh + fr) * kRow + 16 * ((2 * ks + fh) ^ sw));
+    rdH[ks] = (uint32_t)(kTile * kRow + (64 * rq + fr) * kRow + 16 * ((2 * ks + fh) ^ sw));
+  }
+  // DMA: wave w copies E rows and h rows [32 w, 32 w + 32) of the tile, 8 rows per
+  // instruction; lane -> row 8 j + lane / 8, slot lane % 8, global segment slot ^ swz(row).
+  // Sources: a wave-uniform base plus a 32-bit lane offset.
+  const int dlrow = lane >> 3;
+  const uint32_t pitch = 2u * (uint32_t)d;
+  uint32_t offJ[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    offJ[j] = (uint32_t)(8 * j + dlrow) * pitch + 16u * (uint32_t)((lane & 7) ^ swz(8 * j + dlrow));
+  const char* hb = reinterpret_cast<const char*>(h) + ((size_t)c * kTile + 32 * w) * pitch;
+  // E rows of the wave's block of tile tt, clamped to V - 1: base row and lane offsets
+  auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[4]) {
+    const int r0 = tt * kTile + 32 * w;
+    const int rb = min(r0, V - 1);
+    eb = reinterpret_cast<const char*>(E) + (size_t)rb * pitch;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rv = min(r0 + 8 * j + dlrow, V - 1);
+      oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz(8 * j + dlrow));
+    }
+  };
+  // copies of chunk kc of a tile whose E source is (eb, oe)
+  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[4], char* stg) {
+    const uint32_t kb = (uint32_t)kc * (2u * kKC);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(eb + kb + oe[j], stg + 1024 * (4 * w + j));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(hb + kb + offJ[j], stg + kTile * kRow + 1024 * (4 * w + j));
+  };
+
+  f32x16 acc[4][2];
+  RowAcc sa[2];
+  row_acc_reset(sa[0]);
+  row_acc_reset(sa[1]);
+
+  // compute the chunk in stage sc; meanwhile copy chunk kn of the tile (eb, oe) into sn
+  auto chunk = [&](const char* sc, char* sn, int kn, const char* eb, const uint32_t (&oe)[4]) {
+    vm_wait<0>();
+    __syncthreads();
+    const lds_char* s = (const lds_char*)sc;
+    u32x4 fa[2][4], fb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa[0][mb] = lds_read16(s + rdE[0] + 32 * kRow * mb);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow * nb);
+    issue(kn, eb, oe, sn);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cb = ks & 1;
+      if (ks < 3) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          fa[cb ^ 1][mb] = lds_read16(s + rdE[ks + 1] + 32 * kRow * mb);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          fb[cb ^ 1][nb] = lds_read16(s + rdH[ks + 1] + 32 * kRow * nb);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[cb][mb], fb[cb][nb], acc[mb][nb]);
+    }
+    // order: the stage's first reads, then per 16-wide step its MFMAs interleaved with the
+    // next step's reads (and, in the first step, this wave's eight copies of the next chunk)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  const float c2 = kLog2e / g.a.temperature[c];
+  const uint32_t step = (uint32_t)g.a.step[c];
+  const uint32_t k0 = g.a.k0, k1 = g.a.k1;
+  const int rloc0 = 64 * rq + fr, rloc1 = rloc0 + 32;  // rows (in the canvas) of blocks 0, 1
+  const uint32_t row0 = (uint32_t)(c * kTile + rloc0), row1 = row0 + 32;
+  // weight blocks of rows rloc0 (row16 = 16 p + 4 rq + fr / 16) and rloc0 + 32 (row16 + 2);
+  // lane group (fr % 16, fh) at element 8 (fr % 16) + 4 fh of a block
+  const size_t nvb = g.vpad / 32;
+  uint16_t* prow0 = g.P + ((size_t)(16 * p + 4 * rq + (fr >> 4)) * nvb) * 512 + 8 * (fr & 15) + 4 * fh;
+  uint16_t* prow1 = prow0 + 2 * nvb * 512;
+
+  const char* eb;
+  uint32_t oe[4];
+  e_src(ln.lane, eb, oe);
+  issue(0, eb, oe, st0);
+  // nk is even: every tile starts on stage 0, and its last chunk copies the next tile's
+  // first chunk (or, after the last tile, repeats this tile's; never read)
+  for (int tt = ln.lane; tt < T; tt += ln.L) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{0};
+    const char* ebn;
+    uint32_t oen[4];
+    e_src(tt + ln.L < T ? tt + ln.L : tt, ebn, oen);
+    for (int kc = 0; kc < nk - 2; kc += 2) {
+      chunk(st0, st1, kc + 1, eb, oe);
+      chunk(st1, st0, kc + 2, eb, oe);
+    }
+    chunk(st0, st1, nk - 1, eb, oe);
+    chunk(st1, st0, 0, ebn, oen);
+    eb = ebn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) oe[j] = oen[j];
+    // ---- epilogue of tile tt
+    const int vt0 = tt * kTile + kHalf * vh;
+    int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
+    const size_t vblk = (size_t)(vt0 >> 5) * 512;  // first 32-entry block of the half tile
+    if (heavy) {
+      epi_row<true>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, row0, step, k0, k1,
+                    prow0 + vblk, rout0, sa[0]);
+      epi_row<true>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, row1, step, k0, k1,
+                    prow1 + vblk, rout0 + 32, sa[1]);
+    } else {
+      epi_row<false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, row0, step, 0, 0,
+                     prow0, rout0, sa[0]);
+      epi_row<false>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, row1, step, 0, 0,
+                     prow1, rout0 + 32, sa[1]);
+    }
+  }
+  vm_wait<0>();
+  // statistic partials of this (canvas, lane, half)
+  if (lane < 32) {
+    const int slot = 2 * ln.lane + vh;
+    const size_t o0 = (size_t)slot * R + (size_t)c * kTile + rloc0;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const size_t o = o0 + 32 * nb;
+      g.st_amv[o] = sa[nb].amv;
+      g.st_ami[o] = sa[nb].ami;
+      if (heavy) {
+        g.st_m[o] = sa[nb].m;
+        g.st_l[o] = sa[nb].l;
+        g.st_lb[o] = sa[nb].lb;
+        const size_t plane = (size_t)2 * kLanesMax * R;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          g.st_tm[k * plane + o] = sa[nb].tm[k];
+          g.st_tv[k * plane + o] = sa[nb].tv[k];
+        }
+        g.st_a[o] = sa[nb].a;
+        g.st_gv[o] = sa[nb].gv;
+        g.st_gi[o] = sa[nb].gi;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Expectation pass.  Units (non-commit position pc, column block j, range s); the pairs
+// (s, pc) are numbered range-major, pair q runs on XCD q % 8, and the XCD's units
+// (its pairs in order, each with its column blocks) go round-robin to its 32 slots.
+// Wave w: rows [64 (w >> 1), +64) x columns [16 NCB (w & 1), +16 NCB) of the unit's BN.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// B operand of v_mfma_f32_16x16x32_bf16 for 16 columns at byte offset cbyte of the staged
+// E rows [k0, k0 + 32) (row pitch `pitch` bytes): lane (g = lane / 16, i = lane % 16) needs
+// E[k0 + 8 g + 0..7][col i].  Two transpose reads: lane j of a 16-lane group addresses row
+// k0 + 8 g + 4 half + j / 4, columns 4 (j % 4) .. + 3; lane i then holds rows + 0..3 of
+// column i.
+__device__ __forceinline__ u32x4 e_frag(const lds_char* e, int pitch, int k0, int cbyte) {
+  const int lane = threadIdx.x & 63;
+  const int gq = lane >> 4, j = lane & 15;
+  const int row = k0 + 8 * gq + (j >> 2);
+  const int off = row * pitch + cbyte + 8 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(const_cast<lds_char*>(e) + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(const_cast<lds_char*>(e) + off + 4 * pitch));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Scales 8 bf16 weights by 2^-sh (sh in [0, 255]) by lowering their exponent fields with
+// unsigned saturation: exact while the result stays normal, zero below.
+// (Written component by component: the same operation as a loop over v[q] was compiled to a
+// single 32-bit load whose result was copied to all four words.)
+__device__ __forceinline__ uint32_t sub_sat_u16x2(uint32_t x, u16x2 k) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, x), k));
+}
+__device__ __forceinline__ u32x4 shift_down(u32x4 v, uint32_t sh7) {
+  const u16x2 k = {(unsigned short)sh7, (unsigned short)sh7};
+  return u32x4{sub_sat_u16x2(v.x, k), sub_sat_u16x2(v.y, k), sub_sat_u16x2(v.z, k),
+               sub_sat_u16x2(v.w, k)};
+}
+
+struct Unit {
+  int pc, j, s, t0, t1;
+  bool valid;
+};
+
+// Local unit lu of XCD x: its pair q = x + 8 (lu / n_colblk), column block lu % n_colblk.
+__device__ __forceinline__ Unit unit_at(int x, int lu, int n_nc, int n_range, int n_colblk, int T) {
+  Unit u;
+  const int i = lu / n_colblk;
+  u.j = lu - i * n_colblk;
+  const int q = x + 8 * i;
+  u.valid = q < n_nc * n_range;
+  const int qq = u.valid ? q : 0;
+  u.s = qq / n_nc;
+  u.pc = qq - u.s * n_nc;
+  u.t0 = (int)(((long long)T * u.s) / n_range);
+  u.t1 = (int)(((long long)T * (u.s + 1)) / n_range);
+  return u;
+}
+
+// One workgroup per unit: workgroup b runs unit b / 8 of XCD b % 8.
+template <int NCB>
+__global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
+  constexpr int BN = 32 * NCB;            // columns of a unit
+  constexpr int kPitchE = 2 * BN;         // bytes of one staged E row
+  constexpr int kPB = kTile * kRow;       // weights: 256 rows x 64 entries (32 KB)
+  constexpr int kEB = kKC * kPitchE;      // E: 64 rows x BN columns
+  constexpr int kStage = kPB + kEB;
+  constexpr int kNE = kEB / 1024;         // E copies per stage (4 NCB)
+  constexpr int kNEw = (kNE + 7) / 8;     // E copies per wave, at most
+  constexpr int kC16 = BN / 8;            // 16-byte chunks per staged E row
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  const int V = g.a.V, d = g.a.d;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int rw = w >> 1, cw = w & 1;
+  const int T = g.n_tiles;
+  const int n_nc = *g.n_nc_p;
+  const size_t R = (size_t)g.a.n_canvas * kTile;
+  const Unit u = unit_at(blockIdx.x & 7, blockIdx.x >> 3, n_nc, g.n_range, g.n_colblk, T);
+  if (!u.valid || u.t1 <= u.t0) return;
+
+  // A operand (weights): the stage holds the 32 fragment blocks of the chunk, block
+  // (row16, ks) at 1 KB (2 row16 + ks); lane L reads its 16 bytes at 16 L.  A rows of this
+  // lane: ra(rb) = 64 rw + 16 rb + lane % 16.
+  const int ar = lane & 15;
+  // wave w copies the blocks of row16 in {2w, 2w + 1}, ks in {0, 1}: instruction j covers
+  // row16 2w + j / 2, ks j % 2 (LDS 1 KB (4 w + j)); chunk kc starts 2 kc blocks further
+  const size_t nvb = g.vpad / 32;
+  const char* pb = reinterpret_cast<const char*>(g.P) +
+                   (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024 +
+                   16 * lane;
+  const uint32_t epitch = 2u * (uint32_t)d;
+  const char* ebase = reinterpret_cast<const char*>(g.a.E) + (size_t)u.j * BN * 2;
+  const int v00 = u.t0 * kTile;
+  const int nkc = (u.t1 - u.t0) * (kTile / kKC);
+
+  auto issue = [&](int kc, char* stg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(pb + ((size_t)(j >> 1) * nvb + (j & 1) + 2 * kc) * 1024, stg + 1024 * (4 * w + j));
+    // rows past V - 1 (the tail of the last tile, whose weights are zero) read row V - 1
+    const int vb = min(v00 + kc * kKC, V - 1);
+    const char* eb = ebase + (size_t)vb * epitch;
+    const int lim = V - 1 - vb;  // >= 0: last valid row of the chunk, relative to vb
+#pragma unroll
+    for (int m = 0; m < kNEw; ++m) {
+      if (w + 8 * m < kNE) {
+        const int c16 = 64 * (w + 8 * m) + lane;
+        const int row = c16 / kC16, col = c16 - row * kC16;
+        dma16(eb + (uint32_t)min(row, lim) * epitch + 16u * (uint32_t)col,
+              stg + kPB + 1024 * (w + 8 * m));
+      }
+    }
+  };
+
+  // reference of the unit's range for the four A rows of this lane
+  int M[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) M[rb] = INT32_MIN;
+  const int* rbase = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + 64 * rw + ar;
+  for (int ht = 0; ht < 2 * (u.t1 - u.t0); ++ht) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) M[rb] = max(M[rb], rbase[(size_t)ht * R + 16 * rb]);
+  }
+  f32x4 acc[4][NCB];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
+
+  // one chunk from stage sc (shift words sh7 per A row block); copy chunk kn into sn
+  auto chunk = [&](const char* sc, char* sn, int kn, bool copy, const uint32_t (&sh7)[4]) {
+    vm_wait<0>();
+    __syncthreads();
+    if (copy) issue(kn, sn);
+    const lds_char* sp = (const lds_char*)sc;
+    const lds_char* se = (const lds_char*)(sc + kPB);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 fa[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        fa[rb] = shift_down(lds_read16(sp + ((4 * rw + rb) * 2 + ks) * 1024 + 16 * lane), sh7[rb]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const u32x4 fb = e_frag(se, kPitchE, 32 * ks, 2 * (16 * NCB * cw + 16 * cb));
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
+      }
+    }
+  };
+
+  issue(0, st0);
+  for (int kc = 0; kc < nkc; kc += 2) {
+    // shifts of the half tile these two chunks cover
+    uint32_t sh7[4];
+    const int* rp = rbase + (size_t)(kc >> 1) * R;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int rf = rp[16 * rb];
+      const int sh = (rf == INT32_MIN) ? 0 : min(M[rb] - rf, 255);
+      sh7[rb] = (uint32_t)sh << 7;
+    }
+    chunk(st0, st1, kc + 1, true, sh7);
+    chunk(st1, st0, kc + 2, kc + 2 < nkc, sh7);
+  }
+  vm_wait<0>();
+  // expectation partial of this unit; the column-block-0 unit also records the references
+  float* out = g.accp + ((size_t)u.s * R + (size_t)u.pc * kTile) * d + (size_t)u.j * BN +
+               16 * NCB * cw + (lane & 15);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * rw + 16 * rb + 4 * (lane >> 4) + i;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) out[(size_t)row * d + 16 * cb] = acc[rb][cb][i];
+    }
+  if (u.j == 0 && cw == 0 && lane < 16) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      g.accM[(size_t)u.s * R + (size_t)u.pc * kTile + 64 * rw + 16 * rb + ar] =
+          M[rb] == INT32_MIN ? -INFINITY : (float)M[rb];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Canvas order: non-commit canvases first, each part in index order; position of each
+// canvas; number of non-commit canvases.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gemm_init(const uint8_t* commit, int n, int* order,
+                                                   int* pos, int* n_nc) {
+  __shared__ int cnt[256];
+  __shared__ int total;
+  const int t = threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int k = 0;
+  for (int c = lo; c < hi; ++c) k += (commit == nullptr || commit[c] == 0) ? 1 : 0;
+  cnt[t] = k;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = cnt[i];
+      cnt[i] = run;
+      run += v;
+    }
+    total = run;
+    *n_nc = run;
+  }
+  __syncthreads();
+  int a = cnt[t];
+  int bb = total + (lo - cnt[t]);
+  for (int c = lo; c < hi; ++c) {
+    const int p = (commit == nullptr || commit[c] == 0) ? a++ : bb++;
+    order[p] = c;
+    pos[c] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Combine: one 256-thread workgroup per row.  Wave 0 merges the statistic partials of the
+// row's lanes (and their top-4 half-tile maxima); then every thread sums the expectation
+// partials of its columns.
+//
+// Expectation normaliser and top-4 correction.  The expectation pass multiplies bf16 weights
+// w~ = bf16(2^(z2 - ref)); dividing by the sum of the same rounded weights (lb) cancels a
+// common rounding, and the four largest half-tile maxima of the row, whose rounding would
+// otherwise dominate the error, are restored exactly: their residual w - w~ (w recomputed
+// here bit for bit as the logits pass computed it) is added, scaled, to numerator and lb.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gemm_combine(GemmK g) {
+  const int n_canvas = g.a.n_canvas;
+  const size_t R = (size_t)n_canvas * kTile;
+  const int d = g.a.d;
+  const int r = blockIdx.x;
+  const int c = r / kTile, i = r - c * kTile;
+  const int p = g.pos[c];
+  const bool heavy = p < *g.n_nc_p;
+  __shared__ float sm, sl, sbase[64], scoef[4];
+  __shared__ int sidx[4];
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const int L = lanes_at(p, n_canvas);
+    const int n_slot = 2 * min(L, g.n_tiles);
+    const size_t plane = (size_t)2 * kLanesMax * R;
+    float m = -INFINITY, l = 0.0f, a = 0.0f, lb = 0.0f, amv = -INFINITY, gv = -INFINITY;
+    int ami = 0x7FFFFFFF, gi = 0x7FFFFFFF;
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int tv[4] = {0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
+    for (int s = t; s < n_slot; s += 64) {
+      const size_t o = (size_t)s * R + r;
+      argmax_merge(amv, ami, g.st_amv[o], g.st_ami[o]);
+      if (heavy) {
+        lse_merge_b(m, l, a, lb, g.st_m[o], g.st_l[o], g.st_a[o], g.st_lb[o]);
+        argmax_merge(gv, gi, g.st_gv[o], g.st_gi[o]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) top4_insert(tm, tv, g.st_tm[k * plane + o], g.st_tv[k * plane + o]);
+      }
+    }
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) {
+      argmax_merge(amv, ami, xor_f(amv, msk), xor_i(ami, msk));
+      if (heavy) {
+        const float m2 = xor_f(m, msk), l2 = xor_f(l, msk), a2 = xor_f(a, msk);
+        const float lb2 = xor_f(lb, msk);
+        lse_merge_b(m, l, a, lb, m2, l2, a2, lb2);
+        argmax_merge(gv, gi, xor_f(gv, msk), xor_i(gi, msk));
+        float om[4];
+        int ov[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          om[k] = xor_f(tm[k], msk);
+          ov[k] = xor_i(tv[k], msk);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) top4_insert(tm, tv, om[k], ov[k]);
+      }
+    }
+    if (t == 0) {
+      g.a.argmax_tok[r] = ami;
+      if (heavy) {
+        const float lg = hw_log2(l);
+        if (g.a.lse) g.a.lse[r] = kLn2 * (m + lg);
+        g.a.entropy[r] = fmaxf(0.0f, kLn2 * (lg - a / l));
+        g.a.gumbel_tok[r] = gi;
+        float lbc = lb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float cf = 0.0f;
+          if (tm[k] != -INFINITY) {
+            const float ref = fminf(fmaxf(ceilf(tm[k]), -16777216.0f), 16777216.0f);
+            const float w = hw_exp2(__fsub_rn(tm[k], ref));
+            const float wr = __uint_as_float(f32_to_bf16_bits(w) << 16);
+            cf = (w - wr) * hw_exp2(ref - m);
+          }
+          scoef[k] = cf;
+          sidx[k] = cf != 0.0f ? tv[k] : 0;
+          lbc += cf;
+        }
+        sm = m;
+        sl = lbc;
+      }
+    }
+    if (heavy && g.a.selfcond != nullptr)
+      for (int s = t; s < g.n_range; s += 64)
+        sbase[s] = g.accM[(size_t)s * R + (size_t)p * kTile + i];
+  }
+  __syncthreads();
+  if (!heavy || g.a.selfcond == nullptr) return;
+  const float m = sm;
+  const float linv = 1.0f / sl;
+  const uint16_t* E = g.a.E;
+  for (int k = t; k < d; k += 256) {
+    float acc = 0.0f;
+    for (int s = 0; s < g.n_range; ++s) {
+      const float base = sbase[s];
+      if (base == -INFINITY) continue;
+      acc += hw_exp2(base - m) * g.accp[((size_t)s * R + (size_t)p * kTile + i) * d + k];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc += scoef[q] * __uint_as_float((uint32_t)E[(size_t)sidx[q] * d + k] << 16);
+    g.a.selfcond[(size_t)r * d + k] = acc * linv;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------
+static size_t al256g(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static const int kNcbChoices[3] = {8, 4, 2};
+
+bool gemm_supported(int d) { return d % 128 == 0; }
+
+// Column blocking and vocabulary ranges of the expectation pass, from a cost model of the
+// persistent schedule: rounds of the busiest XCD x unit time (scaled by the MFMA-to-byte
+// intensity of the unit's tile), plus the HBM time of writing and reading the partials.
+static void pick_selfcond_tiling(int n_canvas, int n_tiles, int d, int* ncb_out, int* nr_out) {
+  double best = 1e300;
+  int bn = 2, br = 1;
+  for (int qi = 0; qi < 3; ++qi) {
+    const int ncb = kNcbChoices[qi];
+    if (d % (32 * ncb) != 0) continue;
+    const int n_col = d / (32 * ncb);
+    const double inten = 2.0 * 256 * 32 * ncb * 64 / (32768.0 + 64.0 * 64 * ncb);
+    const double eff = inten >= 140.0 ? 1.0 : inten / 140.0;
+    const int rmax = n_tiles < 64 ? n_tiles : 64;
+    for (int nr = 1; nr <= rmax; ++nr) {
+      const int pairs = n_canvas * nr;
+      const int pairs_x = (pairs + 7) / 8;
+      const int rounds = (pairs_x * n_col + 31) / 32;
+      const int tiles = (n_tiles + nr - 1) / nr;
+      const double unit = (double)tiles * 256.0 * 256.0 * 32.0 * ncb * 2.0 / (9.77e12 * 0.5 * eff);
+      const double part = (double)n_canvas * 256.0 * d * 4.0 * nr * 2.0 / 5.0e12;
+      const double cost = rounds * unit + part;
+      if (cost < best * 0.999) {
+        best = cost;
+        bn = ncb;
+        br = nr;
+      }
+    }
+  }
+  *ncb_out = bn;
+  *nr_out = br;
+}
+
+GemmPlan gemm_plan(int n_canvas, int V, int d) {
+  GemmPlan p{};
+  p.R = (size_t)n_canvas * kTile;
+  p.n_tiles = (V + kTile - 1) / kTile;
+  p.vpad = (size_t)p.n_tiles * kTile;
+  pick_selfcond_tiling(n_canvas, p.n_tiles, d, &p.ncb, &p.n_range);
+  p.n_colblk = d / (32 * p.ncb);
+  p.n_rounds = n_canvas / 16 + __builtin_popcount((unsigned)(n_canvas % 16));
+  p.n_units_xcd = ((n_canvas * p.n_range + 7) / 8) * p.n_colblk;
+  size_t off = 0;
+  p.off_small = off;
+  off += al256g((size_t)(2 * n_canvas + 64) * 4);
+  p.off_P = off;
+  off += al256g(p.R * p.vpad * 2);
+  p.off_ref = off;
+  off += al256g((size_t)2 * p.n_tiles * p.R * 4);
+  p.off_st = off;
+  off += 16 * al256g((size_t)2 * kLanesMax * p.R * 4);  // 8 statistics + 4 x (top z2, entry)
+  p.off_accp = off;
+  off += al256g((size_t)p.n_range * p.R * d * 4);
+  p.off_accM = off;
+  off += al256g((size_t)p.n_range * p.R * 4);
+  p.bytes = off;
+  return p;
+}
+
+hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
+                       hipStream_t stream) {
+  char* b = static_cast<char*>(workspace);
+  GemmK g{};
+  g.a = a;
+  int* small = reinterpret_cast<int*>(b + p.off_small);
+  int* order = small;
+  int* pos = small + a.n_canvas;
+  int* n_nc = small + 2 * a.n_canvas;
+  g.order = order;
+  g.pos = pos;
+  g.n_nc_p = n_nc;
+  g.P = reinterpret_cast<uint16_t*>(b + p.off_P);
+  g.ref = reinterpret_cast<int*>(b + p.off_ref);
+  const size_t st = al256g((size_t)2 * kLanesMax * p.R * 4);
+  g.st_m = reinterpret_cast<float*>(b + p.off_st + 0 * st);
+  g.st_l = reinterpret_cast<float*>(b + p.off_st + 1 * st);
+  g.st_a = reinterpret_cast<float*>(b + p.off_st + 2 * st);
+  g.st_amv = reinterpret_cast<float*>(b + p.off_st + 3 * st);
+  g.st_ami = reinterpret_cast<int*>(b + p.off_st + 4 * st);
+  g.st_gv = reinterpret_cast<float*>(b + p.off_st + 5 * st);
+  g.st_gi = reinterpret_cast<int*>(b + p.off_st + 6 * st);
+  g.st_lb = reinterpret_cast<float*>(b + p.off_st + 7 * st);
+  g.st_tm = reinterpret_cast<float*>(b + p.off_st + 8 * st);   // 4 planes of st bytes
+  g.st_tv = reinterpret_cast<int*>(b + p.off_st + 12 * st);
+  g.accp = reinterpret_cast<float*>(b + p.off_accp);
+  g.accM = reinterpret_cast<float*>(b + p.off_accM);
+  g.n_tiles = p.n_tiles;
+  g.vpad = p.vpad;
+  g.n_range = p.n_range;
+  g.ncb = p.ncb;
+  g.n_colblk = p.n_colblk;
+  hipLaunchKernelGGL(k_gemm_init, dim3(1), dim3(256), 0, stream, a.commit, a.n_canvas, order,
+                     pos, n_nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gemm_logits, dim3((unsigned)(kWG * p.n_rounds)), dim3(512), 0, stream, g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.selfcond != nullptr) {
+    const dim3 grid((unsigned)(8 * p.n_units_xcd));
+    switch (p.ncb) {
+      case 8: hipLaunchKernelGGL(k_gemm_selfcond<8>, grid, dim3(512), 0, stream, g); break;
+      case 4: hipLaunchKernelGGL(k_gemm_selfcond<4>, grid, dim3(512), 0, stream, g); break;
+      default: hipLaunchKernelGGL(k_gemm_selfcond<2>, grid, dim3(512), 0, stream, g); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_gemm_combine, dim3((unsigned)p.R), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace dg

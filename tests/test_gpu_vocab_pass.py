@@ -29,14 +29,15 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["fused", "split"])
+@pytest.fixture(params=["gemm", "fused", "split"])
 def path(request):
-    """Runs the test through the fused cooperative kernel and through the split kernels."""
+    """Runs the test through the default two-GEMM path, the cooperative single-kernel path and
+    the split kernels."""
     old = os.environ.get("DG_VOCAB_PATH")
-    if request.param == "split":
-        os.environ["DG_VOCAB_PATH"] = "split"
-    else:
+    if request.param == "gemm":
         os.environ.pop("DG_VOCAB_PATH", None)
+    else:
+        os.environ["DG_VOCAB_PATH"] = request.param
     yield request.param
     if old is None:
         os.environ.pop("DG_VOCAB_PATH", None)
@@ -134,13 +135,21 @@ def test_lite_workload_sampled_rows(path):
     _check(wl, seed=0, rows=np.sort(rows), label=f"lite/{path}")
 
 
-def test_fused_determinism_and_agreement_with_split():
-    """The fused kernel is bit-reproducible and agrees with the split kernels."""
+@pytest.mark.parametrize("which", ["gemm", "fused"])
+def test_determinism_and_agreement_with_split(which):
+    """The default and the cooperative paths are bit-reproducible and agree with the split
+    kernels."""
     wl = synth.workload("lite", V=20000, d=1024, n_canvas=3, seed=8)
     wl.commit = np.array([0, 1, 0], np.uint8)
-    os.environ.pop("DG_VOCAB_PATH", None)
-    a = _run(wl, 5)
-    b = _run(wl, 5)
+    if which == "gemm":
+        os.environ.pop("DG_VOCAB_PATH", None)
+    else:
+        os.environ["DG_VOCAB_PATH"] = which
+    try:
+        a = _run(wl, 5)
+        b = _run(wl, 5)
+    finally:
+        os.environ.pop("DG_VOCAB_PATH", None)
     for k in ("entropy", "argmax_tok", "gumbel_tok", "selfcond"):
         x, y = getattr(a, k).cpu().numpy(), getattr(b, k).cpu().numpy()
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), k
