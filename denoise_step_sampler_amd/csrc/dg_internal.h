@@ -66,7 +66,7 @@ struct GemmPlan {
   int n_colblk;   // column blocks of the expectation pass
   int n_rounds;   // canvas rounds of the logits pass (256 workgroups each)
   int n_units_xcd;  // expectation units per XCD at most
-  size_t off_small, off_P, off_ref, off_st, off_accp, off_accM;
+  size_t off_small, off_P, off_ref, off_st, off_accp, off_accM, off_fac;
   size_t bytes;
 };
 bool gemm_supported(int d);

@@ -53,7 +53,8 @@ constexpr int kHalf = 128;      // granularity of the weight references
 constexpr int kKC = 64;         // K chunk (elements) per LDS stage
 constexpr int kRow = 2 * kKC;   // bytes of one staged row: one 128-byte line
 constexpr int kLanesMax = 256;  // vocabulary lanes per canvas at most (one canvas per GPU)
-constexpr int kWG = 256;        // persistent workgroups
+constexpr int kWG = 256;        // workgroups per round of the logits pass
+constexpr int kFacStride = 72;  // floats per row of the combine's weights
 
 __device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
@@ -195,6 +196,8 @@ struct GemmK {
   int* st_gi;
   float* accp;        // [n_range][R][d] expectation partials, row = 256 pos + i
   float* accM;        // [n_range][R] their references
+  float* fac;         // [R][kFacStride]: range weights [0, 64), correction weights [64, 68),
+                      // correction entries (int) [68, 72)
   int n_tiles;        // vocabulary tiles of 256
   size_t vpad;        // n_tiles * 256
   int n_range;        // vocabulary ranges of the expectation pass
@@ -571,7 +574,29 @@ __device__ __forceinline__ Unit unit_at(int x, int lu, int n_nc, int n_range, in
   return u;
 }
 
-// One workgroup per unit: workgroup b runs unit b / 8 of XCD b % 8.
+// LDS DMA issued as inline assembly: the compiler does not see these copies, so it neither
+// waits for them before unrelated LDS reads (it cannot tell the two stages apart for the
+// transpose reads) nor counts them; the kernel waits for them explicitly (vm_wait) before the
+// barrier that publishes a stage.  base is wave-uniform, off per lane, dst the wave-uniform
+// LDS address of the 1 KB destination; the one-cycle nop covers the M0 -> LDS DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_asm(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(dst)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
+}
+
+// One workgroup per unit: workgroup b runs unit b / 8 of XCD b % 8.  A unit spans at most
+// kMaxUnitTiles vocabulary tiles (its exponent shifts fit in LDS).
+constexpr int kMaxUnitTiles = 64;
+
 template <int NCB>
 __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int BN = 32 * NCB;            // columns of a unit
@@ -580,10 +605,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int kEB = kKC * kPitchE;      // E: 64 rows x BN columns
   constexpr int kStage = kPB + kEB;
   constexpr int kNE = kEB / 1024;         // E copies per stage (4 NCB)
-  constexpr int kNEw = (kNE + 7) / 8;     // E copies per wave, at most
+  constexpr int kNEw = kNE / 8;           // E copies per wave
+  static_assert(kNE % 8 == 0, "E copies must divide among the eight waves");
   constexpr int kC16 = BN / 8;            // 16-byte chunks per staged E row
+  constexpr int kRowsPerCopy = 1024 / kPitchE;  // E rows per 1 KB copy
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  // exponent shifts: byte (ht, row) at 256 ht + 64 rw + 4 (row % 16) + rb for
+  // row = 64 rw + 16 rb + row % 16, so one 32-bit read gives a lane its four A rows
+  __shared__ __attribute__((aligned(16))) uint8_t shb[2 * kMaxUnitTiles * kTile];
+  // the prologue's two partial maxima per row live in stage 1 (no copy has been issued yet)
+  int (*sM)[kTile] = reinterpret_cast<int (*)[kTile]>(st1);
   const int V = g.a.V, d = g.a.d;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -593,61 +625,78 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   const size_t R = (size_t)g.a.n_canvas * kTile;
   const Unit u = unit_at(blockIdx.x & 7, blockIdx.x >> 3, n_nc, g.n_range, g.n_colblk, T);
   if (!u.valid || u.t1 <= u.t0) return;
+  const int nh = 2 * (u.t1 - u.t0);  // half tiles of the unit (<= 2 kMaxUnitTiles)
 
-  // A operand (weights): the stage holds the 32 fragment blocks of the chunk, block
-  // (row16, ks) at 1 KB (2 row16 + ks); lane L reads its 16 bytes at 16 L.  A rows of this
-  // lane: ra(rb) = 64 rw + 16 rb + lane % 16.
+  // ---- prologue: reference M of every row over the unit's half tiles, then the shifts
+  {
+    const int row = t & (kTile - 1), hh = t >> 8;
+    const int* rp = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + row;
+    int mx = INT32_MIN;
+#pragma unroll 8
+    for (int ht = hh; ht < nh; ht += 2) mx = max(mx, rp[(size_t)ht * R]);
+    sM[hh][row] = mx;
+    __syncthreads();
+    const int M = max(sM[0][row], sM[1][row]);
+    const int pos = 64 * (row >> 6) + 4 * (row & 15) + ((row >> 4) & 3);
+#pragma unroll 8
+    for (int ht = hh; ht < nh; ht += 2) {
+      const int rf = rp[(size_t)ht * R];
+      shb[ht * kTile + pos] = (uint8_t)((rf == INT32_MIN) ? 0 : min(M - rf, 255));
+    }
+    if (hh == 0) sM[0][row] = M;
+    __syncthreads();
+  }
   const int ar = lane & 15;
-  // wave w copies the blocks of row16 in {2w, 2w + 1}, ks in {0, 1}: instruction j covers
-  // row16 2w + j / 2, ks j % 2 (LDS 1 KB (4 w + j)); chunk kc starts 2 kc blocks further
+  int M[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) M[rb] = sM[0][64 * rw + 16 * rb + ar];
+
+  // ---- copies.  Weights: instruction j of wave w covers fragment block (row16 2w + j / 2,
+  // ks j % 2) of the chunk (LDS 1 KB (4 w + j)); E: instruction m covers the stage's 1 KB
+  // number w + 8 m, i.e. rows kRowsPerCopy (w + 8 m) + lane / kC16.
   const size_t nvb = g.vpad / 32;
-  const char* pb = reinterpret_cast<const char*>(g.P) +
-                   (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024 +
-                   16 * lane;
+  const char* pbase = reinterpret_cast<const char*>(g.P) +
+                      (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024;
+  const uint32_t offP = 16u * (uint32_t)lane;
   const uint32_t epitch = 2u * (uint32_t)d;
   const char* ebase = reinterpret_cast<const char*>(g.a.E) + (size_t)u.j * BN * 2;
   const int v00 = u.t0 * kTile;
   const int nkc = (u.t1 - u.t0) * (kTile / kKC);
+  const int erow0 = lane / kC16;                     // row within the copy
+  const uint32_t ecol = 16u * (uint32_t)(lane % kC16);
+  const uint32_t a0 = (uint32_t)(uintptr_t)(lds_char*)st0, a1 = (uint32_t)(uintptr_t)(lds_char*)st1;
 
-  auto issue = [&](int kc, char* stg) {
+  auto issue = [&](int kc, uint32_t stg) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      dma16(pb + ((size_t)(j >> 1) * nvb + (j & 1) + 2 * kc) * 1024, stg + 1024 * (4 * w + j));
-    // rows past V - 1 (the tail of the last tile, whose weights are zero) read row V - 1
+      dma_asm(pbase + ((size_t)(j >> 1) * nvb + (j & 1) + 2 * kc) * 1024, offP,
+              stg + 1024u * (uint32_t)(4 * w + j));
+    // E rows past V - 1 (tail of the last tile, zero weights) read row V - 1
     const int vb = min(v00 + kc * kKC, V - 1);
+    const int lim = V - 1 - vb;
     const char* eb = ebase + (size_t)vb * epitch;
-    const int lim = V - 1 - vb;  // >= 0: last valid row of the chunk, relative to vb
 #pragma unroll
     for (int m = 0; m < kNEw; ++m) {
-      if (w + 8 * m < kNE) {
-        const int c16 = 64 * (w + 8 * m) + lane;
-        const int row = c16 / kC16, col = c16 - row * kC16;
-        dma16(eb + (uint32_t)min(row, lim) * epitch + 16u * (uint32_t)col,
-              stg + kPB + 1024 * (w + 8 * m));
-      }
+      const int row = kRowsPerCopy * (w + 8 * m) + erow0;
+      dma_asm(eb, (uint32_t)min(row, lim) * epitch + ecol,
+              stg + (uint32_t)kPB + 1024u * (uint32_t)(w + 8 * m));
     }
   };
 
-  // reference of the unit's range for the four A rows of this lane
-  int M[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) M[rb] = INT32_MIN;
-  const int* rbase = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + 64 * rw + ar;
-  for (int ht = 0; ht < 2 * (u.t1 - u.t0); ++ht) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) M[rb] = max(M[rb], rbase[(size_t)ht * R + 16 * rb]);
-  }
   f32x4 acc[4][NCB];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
 
-  // one chunk from stage sc (shift words sh7 per A row block); copy chunk kn into sn
-  auto chunk = [&](const char* sc, char* sn, int kn, bool copy, const uint32_t (&sh7)[4]) {
+  // one chunk from stage sc with the shifts of its half tile; copies chunk kn into sn
+  auto chunk = [&](const char* sc, uint32_t sn, int kn, bool copy, uint32_t shw) {
     vm_wait<0>();
     __syncthreads();
     if (copy) issue(kn, sn);
+    uint32_t sh7[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) sh7[rb] = ((shw >> (8 * rb)) & 0xFFu) << 7;
     const lds_char* sp = (const lds_char*)sc;
     const lds_char* se = (const lds_char*)(sc + kPB);
 #pragma unroll
@@ -665,19 +714,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     }
   };
 
-  issue(0, st0);
+  issue(0, a0);
+  const lds_char* shp = (const lds_char*)shb + 64 * rw + 4 * ar;
   for (int kc = 0; kc < nkc; kc += 2) {
-    // shifts of the half tile these two chunks cover
-    uint32_t sh7[4];
-    const int* rp = rbase + (size_t)(kc >> 1) * R;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int rf = rp[16 * rb];
-      const int sh = (rf == INT32_MIN) ? 0 : min(M[rb] - rf, 255);
-      sh7[rb] = (uint32_t)sh << 7;
-    }
-    chunk(st0, st1, kc + 1, true, sh7);
-    chunk(st1, st0, kc + 2, kc + 2 < nkc, sh7);
+    const uint32_t shw = lds_u32(shp + (kc >> 1) * kTile);  // half tile kc / 2
+    chunk(st0, a1, kc + 1, true, shw);
+    chunk(st1, a0, kc + 2, kc + 2 < nkc, shw);
   }
   vm_wait<0>();
   // expectation partial of this unit; the column-block-0 unit also records the references
@@ -735,9 +777,11 @@ __global__ __launch_bounds__(256) void k_gemm_init(const uint8_t* commit, int n,
 }
 
 // ---------------------------------------------------------------------------------------
-// Combine: one 256-thread workgroup per row.  Wave 0 merges the statistic partials of the
-// row's lanes (and their top-4 half-tile maxima); then every thread sums the expectation
-// partials of its columns.
+// Combine, in two kernels.  k_gemm_rows: one wave per row merges the statistic partials of
+// the row's lanes (and their top-4 half-tile maxima), writes lse / entropy / argmax / Gumbel
+// token, and the weights of the expectation sum: fac[s] = 2^(M_s - m) / lb' for the range
+// partials and coef[k] / lb' for the four exact corrections.  k_gemm_sc: one thread per
+// (row, column) forms sum_s fac[s] acc_s + sum_k coef[k] E[v_k].
 //
 // Expectation normaliser and top-4 correction.  The expectation pass multiplies bf16 weights
 // w~ = bf16(2^(z2 - ref)); dividing by the sum of the same rounded weights (lb) cancels a
@@ -745,100 +789,119 @@ __global__ __launch_bounds__(256) void k_gemm_init(const uint8_t* commit, int n,
 // otherwise dominate the error, are restored exactly: their residual w - w~ (w recomputed
 // here bit for bit as the logits pass computed it) is added, scaled, to numerator and lb.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gemm_combine(GemmK g) {
+__global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
   const int n_canvas = g.a.n_canvas;
   const size_t R = (size_t)n_canvas * kTile;
-  const int d = g.a.d;
-  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if ((size_t)r >= R) return;
   const int c = r / kTile, i = r - c * kTile;
   const int p = g.pos[c];
   const bool heavy = p < *g.n_nc_p;
-  __shared__ float sm, sl, sbase[64], scoef[4];
-  __shared__ int sidx[4];
-  const int t = threadIdx.x;
-  if (t < 64) {
-    const int L = lanes_at(p, n_canvas);
-    const int n_slot = 2 * min(L, g.n_tiles);
-    const size_t plane = (size_t)2 * kLanesMax * R;
-    float m = -INFINITY, l = 0.0f, a = 0.0f, lb = 0.0f, amv = -INFINITY, gv = -INFINITY;
-    int ami = 0x7FFFFFFF, gi = 0x7FFFFFFF;
-    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    int tv[4] = {0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
-    for (int s = t; s < n_slot; s += 64) {
-      const size_t o = (size_t)s * R + r;
-      argmax_merge(amv, ami, g.st_amv[o], g.st_ami[o]);
-      if (heavy) {
-        lse_merge_b(m, l, a, lb, g.st_m[o], g.st_l[o], g.st_a[o], g.st_lb[o]);
-        argmax_merge(gv, gi, g.st_gv[o], g.st_gi[o]);
+  const int L = lanes_at(p, n_canvas);
+  const int n_slot = 2 * min(L, g.n_tiles);
+  const size_t plane = (size_t)2 * kLanesMax * R;
+  float m = -INFINITY, l = 0.0f, a = 0.0f, lb = 0.0f, amv = -INFINITY, gv = -INFINITY;
+  int ami = 0x7FFFFFFF, gi = 0x7FFFFFFF;
+  float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  int tv[4] = {0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
+  for (int s = lane; s < n_slot; s += 64) {
+    const size_t o = (size_t)s * R + r;
+    argmax_merge(amv, ami, g.st_amv[o], g.st_ami[o]);
+    if (heavy) {
+      lse_merge_b(m, l, a, lb, g.st_m[o], g.st_l[o], g.st_a[o], g.st_lb[o]);
+      argmax_merge(gv, gi, g.st_gv[o], g.st_gi[o]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) top4_insert(tm, tv, g.st_tm[k * plane + o], g.st_tv[k * plane + o]);
-      }
+      for (int k = 0; k < 4; ++k) top4_insert(tm, tv, g.st_tm[k * plane + o], g.st_tv[k * plane + o]);
     }
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) {
-      argmax_merge(amv, ami, xor_f(amv, msk), xor_i(ami, msk));
-      if (heavy) {
-        const float m2 = xor_f(m, msk), l2 = xor_f(l, msk), a2 = xor_f(a, msk);
-        const float lb2 = xor_f(lb, msk);
-        lse_merge_b(m, l, a, lb, m2, l2, a2, lb2);
-        argmax_merge(gv, gi, xor_f(gv, msk), xor_i(gi, msk));
-        float om[4];
-        int ov[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          om[k] = xor_f(tm[k], msk);
-          ov[k] = xor_i(tv[k], msk);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) top4_insert(tm, tv, om[k], ov[k]);
-      }
-    }
-    if (t == 0) {
-      g.a.argmax_tok[r] = ami;
-      if (heavy) {
-        const float lg = hw_log2(l);
-        if (g.a.lse) g.a.lse[r] = kLn2 * (m + lg);
-        g.a.entropy[r] = fmaxf(0.0f, kLn2 * (lg - a / l));
-        g.a.gumbel_tok[r] = gi;
-        float lbc = lb;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float cf = 0.0f;
-          if (tm[k] != -INFINITY) {
-            const float ref = fminf(fmaxf(ceilf(tm[k]), -16777216.0f), 16777216.0f);
-            const float w = hw_exp2(__fsub_rn(tm[k], ref));
-            const float wr = __uint_as_float(f32_to_bf16_bits(w) << 16);
-            cf = (w - wr) * hw_exp2(ref - m);
-          }
-          scoef[k] = cf;
-          sidx[k] = cf != 0.0f ? tv[k] : 0;
-          lbc += cf;
-        }
-        sm = m;
-        sl = lbc;
-      }
-    }
-    if (heavy && g.a.selfcond != nullptr)
-      for (int s = t; s < g.n_range; s += 64)
-        sbase[s] = g.accM[(size_t)s * R + (size_t)p * kTile + i];
   }
-  __syncthreads();
-  if (!heavy || g.a.selfcond == nullptr) return;
-  const float m = sm;
-  const float linv = 1.0f / sl;
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) {
+    argmax_merge(amv, ami, xor_f(amv, msk), xor_i(ami, msk));
+    if (heavy) {
+      const float m2 = xor_f(m, msk), l2 = xor_f(l, msk), a2 = xor_f(a, msk);
+      const float lb2 = xor_f(lb, msk);
+      lse_merge_b(m, l, a, lb, m2, l2, a2, lb2);
+      argmax_merge(gv, gi, xor_f(gv, msk), xor_i(gi, msk));
+      float om[4];
+      int ov[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        om[k] = xor_f(tm[k], msk);
+        ov[k] = xor_i(tv[k], msk);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) top4_insert(tm, tv, om[k], ov[k]);
+    }
+  }
+  if (lane == 0) g.a.argmax_tok[r] = ami;
+  if (!heavy) return;
+  float cf[4];
+  float lbc = lb;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cf[k] = 0.0f;
+    if (tm[k] != -INFINITY) {
+      const float ref = fminf(fmaxf(ceilf(tm[k]), -16777216.0f), 16777216.0f);
+      const float w = hw_exp2(__fsub_rn(tm[k], ref));
+      const float wr = __uint_as_float(f32_to_bf16_bits(w) << 16);
+      cf[k] = (w - wr) * hw_exp2(ref - m);
+    }
+    lbc += cf[k];
+  }
+  const float linv = 1.0f / lbc;
+  if (lane == 0) {
+    const float lg = hw_log2(l);
+    if (g.a.lse) g.a.lse[r] = kLn2 * (m + lg);
+    g.a.entropy[r] = fmaxf(0.0f, kLn2 * (lg - a / l));
+    g.a.gumbel_tok[r] = gi;
+  }
+  if (g.a.selfcond == nullptr) return;
+  const size_t rp = (size_t)p * kTile + i;  // row among the non-commit rows
+  float* fr = g.fac + rp * kFacStride;
+  for (int s = lane; s < g.n_range; s += 64) {
+    const float base = g.accM[(size_t)s * R + rp];
+    fr[s] = base == -INFINITY ? 0.0f : hw_exp2(base - m) * linv;
+  }
+  if (lane < 4) {
+    const float cfl = lane == 0 ? cf[0] : lane == 1 ? cf[1] : lane == 2 ? cf[2] : cf[3];
+    const int tvl = lane == 0 ? tv[0] : lane == 1 ? tv[1] : lane == 2 ? tv[2] : tv[3];
+    fr[64 + lane] = cfl * linv;
+    reinterpret_cast<int*>(fr)[68 + lane] = cfl != 0.0f ? tvl : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gemm_sc(GemmK g) {
+  const int n_canvas = g.a.n_canvas;
+  const size_t R = (size_t)n_canvas * kTile;
+  const int d = g.a.d;
+  const int n_cb = (d + 255) / 256;
+  const int r = blockIdx.x / n_cb;
+  const int col = (blockIdx.x - r * n_cb) * 256 + threadIdx.x;
+  const int c = r / kTile, i = r - c * kTile;
+  const int p = g.pos[c];
+  if (p >= *g.n_nc_p || col >= d) return;
+  const size_t rp = (size_t)p * kTile + i;
+  const float* fr = g.fac + rp * kFacStride;
+  const float* src = g.accp + rp * d + col;
+  const size_t stride = R * d;
+  float acc = 0.0f;
+  const int nr = g.n_range;
+  int s = 0;
+  for (; s + 8 <= nr; s += 8) {
+    float x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = src[(size_t)(s + q) * stride];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += fr[s + q] * x[q];
+  }
+  for (; s < nr; ++s) acc += fr[s] * src[(size_t)s * stride];
+  const int* vi = reinterpret_cast<const int*>(fr) + 68;
   const uint16_t* E = g.a.E;
-  for (int k = t; k < d; k += 256) {
-    float acc = 0.0f;
-    for (int s = 0; s < g.n_range; ++s) {
-      const float base = sbase[s];
-      if (base == -INFINITY) continue;
-      acc += hw_exp2(base - m) * g.accp[((size_t)s * R + (size_t)p * kTile + i) * d + k];
-    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      acc += scoef[q] * __uint_as_float((uint32_t)E[(size_t)sidx[q] * d + k] << 16);
-    g.a.selfcond[(size_t)r * d + k] = acc * linv;
-  }
+  for (int k = 0; k < 4; ++k)
+    acc += fr[64 + k] * __uint_as_float((uint32_t)E[(size_t)vi[k] * d + col] << 16);
+  g.a.selfcond[(size_t)r * d + col] = acc;
 }
 
 }  // namespace
@@ -865,7 +928,8 @@ static void pick_selfcond_tiling(int n_canvas, int n_tiles, int d, int* ncb_out,
     const double inten = 2.0 * 256 * 32 * ncb * 64 / (32768.0 + 64.0 * 64 * ncb);
     const double eff = inten >= 140.0 ? 1.0 : inten / 140.0;
     const int rmax = n_tiles < 64 ? n_tiles : 64;
-    for (int nr = 1; nr <= rmax; ++nr) {
+    const int rmin = (n_tiles + kMaxUnitTiles - 1) / kMaxUnitTiles;  // shifts fit in LDS
+    for (int nr = rmin; nr <= rmax; ++nr) {
       const int pairs = n_canvas * nr;
       const int pairs_x = (pairs + 7) / 8;
       const int rounds = (pairs_x * n_col + 31) / 32;
@@ -906,6 +970,8 @@ GemmPlan gemm_plan(int n_canvas, int V, int d) {
   off += al256g((size_t)p.n_range * p.R * d * 4);
   p.off_accM = off;
   off += al256g((size_t)p.n_range * p.R * 4);
+  p.off_fac = off;
+  off += al256g(p.R * kFacStride * 4);
   p.bytes = off;
   return p;
 }
@@ -937,6 +1003,7 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   g.st_tv = reinterpret_cast<int*>(b + p.off_st + 12 * st);
   g.accp = reinterpret_cast<float*>(b + p.off_accp);
   g.accM = reinterpret_cast<float*>(b + p.off_accM);
+  g.fac = reinterpret_cast<float*>(b + p.off_fac);
   g.n_tiles = p.n_tiles;
   g.vpad = p.vpad;
   g.n_range = p.n_range;
@@ -959,7 +1026,11 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_gemm_combine, dim3((unsigned)p.R), dim3(256), 0, stream, g);
+  hipLaunchKernelGGL(k_gemm_rows, dim3((unsigned)((p.R + 3) / 4)), dim3(256), 0, stream, g);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.selfcond == nullptr) return e;
+  hipLaunchKernelGGL(k_gemm_sc, dim3((unsigned)(((a.d + 255) / 256) * p.R)), dim3(256), 0, stream,
+                     g);
   return hipGetLastError();
 }
 
