@@ -36,6 +36,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -211,11 +213,16 @@ struct GemmK {
 // z2 = S c2 and dz = z2 - ref are rounded separately (no contraction), so that the
 // combine can recompute the weight of a half tile's maximum bit for bit.
 // pt: this lane's 8-byte group in the weight block of the half tile's first 32 entries.
+// The running statistics live in LDS (lds_st: this lane's row; lanes l and l ^ 32 hold the
+// same row and compute identical values, lanes < 32 store them), so that the epilogue's
+// registers are left to the logits and the noise.
+typedef __attribute__((address_space(3))) RowAcc LdsRowAcc;
+
 template <bool kHeavy>
 __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, const f32x16& s2,
                                         const f32x16& s3, int vt0, int V, float c2,
                                         uint32_t row, uint32_t step, uint32_t k0, uint32_t k1,
-                                        uint16_t* pt, int* ref_out, RowAcc& st) {
+                                        uint16_t* pt, int* ref_out, LdsRowAcc* lds_st) {
   const int lane = threadIdx.x & 63;
   const int vb0 = vt0 + 4 * (lane >> 5);
   float m = -INFINITY, amv = -INFINITY;
@@ -235,17 +242,45 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
   scan(s3, vb0 + 96);
   m = fmaxf(m, xor_f(m, 32));
   argmax_merge(amv, ami, xor_f(amv, 32), xor_i(ami, 32));
-  argmax_merge(st.amv, st.ami, amv, ami);
+  const bool writer = lane < 32;
+  {
+    float sv = lds_st->amv;
+    int si = lds_st->ami;
+    argmax_merge(sv, si, amv, ami);
+    if (writer) {
+      lds_st->amv = sv;
+      lds_st->ami = si;
+    }
+  }
   if (!kHeavy) return;
   // integer reference >= every z2 of the half tile (clamped to +-2^24 so that differences
   // of references stay exact integers)
   const bool empty = (m == -INFINITY);
   const float ref = empty ? 0.0f : fminf(fmaxf(ceilf(m), -16777216.0f), 16777216.0f);
   // the half tile's maximum (its entry is the argmax of S: c2 > 0) joins the row's top four
-  if (!empty) top4_insert(st.tm, st.tv, m, ami);
+  if (!empty) {
+    float tm[4];
+    int tv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tm[k] = lds_st->tm[k];
+      tv[k] = lds_st->tv[k];
+    }
+    top4_insert(tm, tv, m, ami);
+    if (writer) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lds_st->tm[k] = tm[k];
+        lds_st->tv[k] = tv[k];
+      }
+    }
+  }
   float ls = 0.0f, as = 0.0f, lsb = 0.0f, gv = -INFINITY;
   int gi = 0x7FFFFFFF;
-  auto block = [&](const f32x16& sb, int vbb, uint16_t* pbk) {
+  // kMasked: the block reaches past V (only the last tile); a full block has no checks, so
+  // no per-entry branches or selects
+  auto block = [&](auto masked, const f32x16& sb, int vbb, uint16_t* pbk) {
+    constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int vb = vbb + 8 * q;
@@ -253,40 +288,68 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool ok = vb + j < V;
         const float z2 = __fmul_rn(sb[4 * q + j], c2);
         const float dz = __fsub_rn(z2, ref);
-        const float pe = ok ? hw_exp2(dz) : 0.0f;
-        ls += pe;
-        as += ok ? pe * dz : 0.0f;
-        argmax_merge(gv, gi, ok ? z2 + gumbel2_from_word(wd[j]) : -INFINITY, vb + j);
-        pv[j] = pe;
+        const float g2 = gumbel2_from_word(wd[j]);
+        if (kMasked) {
+          const bool ok = vb + j < V;
+          const float pe = ok ? hw_exp2(dz) : 0.0f;
+          ls += pe;
+          as += pe * (ok ? dz : 0.0f);
+          argmax_merge(gv, gi, ok ? z2 + g2 : -INFINITY, vb + j);
+          pv[j] = pe;
+        } else {
+          const float pe = hw_exp2(dz);
+          ls += pe;
+          as += pe * dz;
+          argmax_merge(gv, gi, z2 + g2, vb + j);
+          pv[j] = pe;
+        }
       }
       const uint32_t w01 = pack_bf16x2(pv[0], pv[1]), w23 = pack_bf16x2(pv[2], pv[3]);
       lsb += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
       *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
     }
   };
-  // one 32-entry block at a time (a run-time loop: the Philox streams of the blocks would
-  // otherwise be interleaved by the scheduler at a high register cost)
+  const bool full = vt0 + kHalf <= V;
+  // one 32-entry block at a time, in a run-time loop (one copy of the block's code: unrolled,
+  // the blocks' Philox streams would compete for the registers that hold the logits)
+  auto run = [&](auto masked) {
 #pragma unroll 1
-  for (int mb = 0; mb < 4; ++mb) {
-    f32x16 sb;
-    switch (mb) {
-      case 0: sb = s0; break;
-      case 1: sb = s1; break;
-      case 2: sb = s2; break;
-      default: sb = s3; break;
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x16 sb;
+      switch (mb) {
+        case 0: sb = s0; break;
+        case 1: sb = s1; break;
+        case 2: sb = s2; break;
+        default: sb = s3; break;
+      }
+      block(masked, sb, vb0 + 32 * mb, pt + 512 * mb);
     }
-    block(sb, vb0 + 32 * mb, pt + 512 * mb);
-  }
+  };
+  if (full)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
+  __builtin_amdgcn_sched_barrier(0);
   ls += xor_f(ls, 32);
   as += xor_f(as, 32);
   lsb += xor_f(lsb, 32);
   argmax_merge(gv, gi, xor_f(gv, 32), xor_i(gi, 32));
-  if (lane < 32) *ref_out = empty ? INT32_MIN : (int)ref;
-  lse_merge_b(st.m, st.l, st.a, st.lb, empty ? -INFINITY : ref, ls, as, lsb);
-  argmax_merge(st.gv, st.gi, gv, gi);
+  if (writer) *ref_out = empty ? INT32_MIN : (int)ref;
+  float sm = lds_st->m, sl = lds_st->l, sa = lds_st->a, slb = lds_st->lb;
+  float sgv = lds_st->gv;
+  int sgi = lds_st->gi;
+  lse_merge_b(sm, sl, sa, slb, empty ? -INFINITY : ref, ls, as, lsb);
+  argmax_merge(sgv, sgi, gv, gi);
+  if (writer) {
+    lds_st->m = sm;
+    lds_st->l = sl;
+    lds_st->a = sa;
+    lds_st->lb = slb;
+    lds_st->gv = sgv;
+    lds_st->gi = sgi;
+  }
 }
 
 // Round r of the canvas order: canvases [start, start + g).  Rounds of 16 while 16 or more
@@ -375,9 +438,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   };
 
   f32x16 acc[4][2];
-  RowAcc sa[2];
-  row_acc_reset(sa[0]);
-  row_acc_reset(sa[1]);
+  // running statistics of this wave's 64 rows: [wave][nb][row in block]
+  __shared__ RowAcc lds_stats[8][2][32];
+  LdsRowAcc* st0p = (LdsRowAcc*)(&lds_stats[w][0][fr]);
+  LdsRowAcc* st1p = (LdsRowAcc*)(&lds_stats[w][1][fr]);
+  if (lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      LdsRowAcc* q = nb ? st1p : st0p;
+      q->m = -INFINITY;
+      q->l = 0.0f;
+      q->a = 0.0f;
+      q->lb = 0.0f;
+      q->amv = -INFINITY;
+      q->gv = -INFINITY;
+      q->ami = 0x7FFFFFFF;
+      q->gi = 0x7FFFFFFF;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        q->tm[k] = -INFINITY;
+        q->tv[k] = 0x7FFFFFFF;
+      }
+    }
+  }
 
   // compute the chunk in stage sc; meanwhile copy chunk kn of the tile (eb, oe) into sn
   auto chunk = [&](const char* sc, char* sn, int kn, const char* eb, const uint32_t (&oe)[4]) {
@@ -472,14 +555,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     const size_t vblk = (size_t)(vt0 >> 5) * 512;  // first 32-entry block of the half tile
     if (heavy) {
       epi_row<true>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, row0, step, k0, k1,
-                    prow0 + vblk, rout0, sa[0]);
+                    prow0 + vblk, rout0, st0p);
       epi_row<true>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, row1, step, k0, k1,
-                    prow1 + vblk, rout0 + 32, sa[1]);
+                    prow1 + vblk, rout0 + 32, st1p);
     } else {
       epi_row<false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, row0, step, 0, 0,
-                     prow0, rout0, sa[0]);
+                     prow0, rout0, st0p);
       epi_row<false>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, row1, step, 0, 0,
-                     prow1, rout0 + 32, sa[1]);
+                     prow1, rout0 + 32, st1p);
     }
   }
   vm_wait<0>();
@@ -487,24 +570,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   if (lane < 32) {
     const int slot = 2 * ln.lane + vh;
     const size_t o0 = (size_t)slot * R + (size_t)c * kTile + rloc0;
+    const size_t plane = (size_t)2 * kLanesMax * R;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const size_t o = o0 + 32 * nb;
-      g.st_amv[o] = sa[nb].amv;
-      g.st_ami[o] = sa[nb].ami;
+      const LdsRowAcc* st = nb ? st1p : st0p;
+      g.st_amv[o] = st->amv;
+      g.st_ami[o] = st->ami;
       if (heavy) {
-        g.st_m[o] = sa[nb].m;
-        g.st_l[o] = sa[nb].l;
-        g.st_lb[o] = sa[nb].lb;
-        const size_t plane = (size_t)2 * kLanesMax * R;
+        g.st_m[o] = st->m;
+        g.st_l[o] = st->l;
+        g.st_a[o] = st->a;
+        g.st_lb[o] = st->lb;
+        g.st_gv[o] = st->gv;
+        g.st_gi[o] = st->gi;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          g.st_tm[k * plane + o] = sa[nb].tm[k];
-          g.st_tv[k * plane + o] = sa[nb].tv[k];
+          g.st_tm[k * plane + o] = st->tm[k];
+          g.st_tv[k * plane + o] = st->tv[k];
         }
-        g.st_a[o] = sa[nb].a;
-        g.st_gv[o] = sa[nb].gv;
-        g.st_gi[o] = sa[nb].gi;
       }
     }
   }
