@@ -65,7 +65,9 @@ struct GemmPlan {
   int n_range;    // vocabulary ranges of the expectation pass
   int n_colblk;   // column blocks of the expectation pass
   int n_rounds;   // canvas rounds of the logits pass (256 workgroups each)
-  int n_units_xcd;  // expectation units per XCD at most
+  int n_units_xcd;  // expectation units per XCD at most (pair-per-XCD mapping)
+  int n_units;      // expectation units (flat mapping)
+  int flat;         // 1: flat unit mapping
   size_t off_small, off_P, off_ref, off_st, off_accp, off_accM, off_fac;
   size_t bytes;
 };

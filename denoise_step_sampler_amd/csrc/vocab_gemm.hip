@@ -205,6 +205,7 @@ struct GemmK {
   int n_range;        // vocabulary ranges of the expectation pass
   int ncb;            // 16-column blocks per wave in the expectation pass
   int n_colblk;       // d / (32 ncb)
+  int flat;           // expectation units mapped flat (1) or pair-per-XCD (0)
 };
 
 // Per-lane epilogue of one row (32-row block of this wave) over the wave's 128 entries: the
@@ -643,12 +644,14 @@ struct Unit {
   bool valid;
 };
 
-// Local unit lu of XCD x: its pair q = x + 8 (lu / n_colblk), column block lu % n_colblk.
+// XCD mapping: local unit lu of XCD x is column block lu % n_colblk of pair
+// q = x + 8 (lu / n_colblk).  Flat mapping (x = -1): unit lu is column block lu % n_colblk of
+// pair lu / n_colblk (used when pinning pairs to XCDs would leave CUs idle).
 __device__ __forceinline__ Unit unit_at(int x, int lu, int n_nc, int n_range, int n_colblk, int T) {
   Unit u;
   const int i = lu / n_colblk;
   u.j = lu - i * n_colblk;
-  const int q = x + 8 * i;
+  const int q = x < 0 ? i : x + 8 * i;
   u.valid = q < n_nc * n_range;
   const int qq = u.valid ? q : 0;
   u.s = qq / n_nc;
@@ -707,7 +710,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   const int T = g.n_tiles;
   const int n_nc = *g.n_nc_p;
   const size_t R = (size_t)g.a.n_canvas * kTile;
-  const Unit u = unit_at(blockIdx.x & 7, blockIdx.x >> 3, n_nc, g.n_range, g.n_colblk, T);
+  const Unit u = g.flat ? unit_at(-1, blockIdx.x, n_nc, g.n_range, g.n_colblk, T)
+                       : unit_at(blockIdx.x & 7, blockIdx.x >> 3, n_nc, g.n_range, g.n_colblk, T);
   if (!u.valid || u.t1 <= u.t0) return;
   const int nh = 2 * (u.t1 - u.t0);  // half tiles of the unit (<= 2 kMaxUnitTiles)
 
@@ -1002,9 +1006,10 @@ bool gemm_supported(int d) { return d % 128 == 0; }
 // Column blocking and vocabulary ranges of the expectation pass, from a cost model of the
 // persistent schedule: rounds of the busiest XCD x unit time (scaled by the MFMA-to-byte
 // intensity of the unit's tile), plus the HBM time of writing and reading the partials.
-static void pick_selfcond_tiling(int n_canvas, int n_tiles, int d, int* ncb_out, int* nr_out) {
+static void pick_selfcond_tiling(int n_canvas, int n_tiles, int d, int* ncb_out, int* nr_out,
+                                 int* flat_out) {
   double best = 1e300;
-  int bn = 2, br = 1;
+  int bn = 2, br = 1, bf = 0;
   for (int qi = 0; qi < 3; ++qi) {
     const int ncb = kNcbChoices[qi];
     if (d % (32 * ncb) != 0) continue;
@@ -1014,22 +1019,31 @@ static void pick_selfcond_tiling(int n_canvas, int n_tiles, int d, int* ncb_out,
     const int rmax = n_tiles < 64 ? n_tiles : 64;
     const int rmin = (n_tiles + kMaxUnitTiles - 1) / kMaxUnitTiles;  // shifts fit in LDS
     for (int nr = rmin; nr <= rmax; ++nr) {
-      const int pairs = n_canvas * nr;
-      const int pairs_x = (pairs + 7) / 8;
-      const int rounds = (pairs_x * n_col + 31) / 32;
       const int tiles = (n_tiles + nr - 1) / nr;
       const double unit = (double)tiles * 256.0 * 256.0 * 32.0 * ncb * 2.0 / (9.77e12 * 0.5 * eff);
       const double part = (double)n_canvas * 256.0 * d * 4.0 * nr * 2.0 / 5.0e12;
-      const double cost = rounds * unit + part;
-      if (cost < best * 0.999) {
-        best = cost;
-        bn = ncb;
-        br = nr;
+      for (int flat = 0; flat < 2; ++flat) {
+        int rounds;
+        if (flat) {
+          rounds = (n_canvas * nr * n_col + 255) / 256;
+        } else {
+          const int pairs_x = (n_canvas * nr + 7) / 8;
+          rounds = (pairs_x * n_col + 31) / 32;
+        }
+        // the flat mapping gives up the L2 sharing of weights and E across a pair's units
+        const double cost = rounds * unit * (flat ? 1.05 : 1.0) + part;
+        if (cost < best * 0.999) {
+          best = cost;
+          bn = ncb;
+          br = nr;
+          bf = flat;
+        }
       }
     }
   }
   *ncb_out = bn;
   *nr_out = br;
+  *flat_out = bf;
 }
 
 GemmPlan gemm_plan(int n_canvas, int V, int d) {
@@ -1037,10 +1051,11 @@ GemmPlan gemm_plan(int n_canvas, int V, int d) {
   p.R = (size_t)n_canvas * kTile;
   p.n_tiles = (V + kTile - 1) / kTile;
   p.vpad = (size_t)p.n_tiles * kTile;
-  pick_selfcond_tiling(n_canvas, p.n_tiles, d, &p.ncb, &p.n_range);
+  pick_selfcond_tiling(n_canvas, p.n_tiles, d, &p.ncb, &p.n_range, &p.flat);
   p.n_colblk = d / (32 * p.ncb);
   p.n_rounds = n_canvas / 16 + __builtin_popcount((unsigned)(n_canvas % 16));
   p.n_units_xcd = ((n_canvas * p.n_range + 7) / 8) * p.n_colblk;
+  p.n_units = n_canvas * p.n_range * p.n_colblk;
   size_t off = 0;
   p.off_small = off;
   off += al256g((size_t)(2 * n_canvas + 64) * 4);
@@ -1093,6 +1108,7 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   g.n_range = p.n_range;
   g.ncb = p.ncb;
   g.n_colblk = p.n_colblk;
+  g.flat = p.flat;
   hipLaunchKernelGGL(k_gemm_init, dim3(1), dim3(256), 0, stream, a.commit, a.n_canvas, order,
                      pos, n_nc);
   hipError_t e = hipGetLastError();
@@ -1101,7 +1117,7 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.selfcond != nullptr) {
-    const dim3 grid((unsigned)(8 * p.n_units_xcd));
+    const dim3 grid((unsigned)(p.flat ? p.n_units : 8 * p.n_units_xcd));
     switch (p.ncb) {
       case 8: hipLaunchKernelGGL(k_gemm_selfcond<8>, grid, dim3(512), 0, stream, g); break;
       case 4: hipLaunchKernelGGL(k_gemm_selfcond<4>, grid, dim3(512), 0, stream, g); break;
