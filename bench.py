@@ -21,10 +21,45 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "denoise_step_sampler_amd", "csrc", "vocab_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_logits.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of k_gemm_logits from the committed counter summary, or None when
+    there is none for this workload or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash(KERNEL_SRC):
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else float(w["hbm_bytes_per_launch"])
+
+
+def copy_probe(mb: int, reps: int) -> int:
+    """A plain device copy of mb MiB, repeated: the calibration kernel for the HBM counters."""
+    import torch
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps}), flush=True)
+    return 0
 
 
 def algorithmic_flops(wl) -> float:
@@ -73,6 +108,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -88,6 +125,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, 5)
     log(f"[bench] building inputs for workload {args.workload}")
     wl = synth.workload(args.workload, seed=args.seed)
     b = runner.from_workload(wl)
@@ -128,8 +167,26 @@ def main() -> int:
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.3f}s), "
         f"vocab pass {vp_avg:.3f} ms (min {min(vp_ms):.3f})")
 
+    # the dominant kernel, k_gemm_logits (logits + epilogue, 2 R V d flops): the same pass
+    # without the expectation runs it plus two small kernels (canvas order, row statistics),
+    # timed the same way on the same stream
+    from denoise_step_sampler_amd import binding as B
+    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev2[k][0].record(stream)
+        B.dg_vocab_pass(b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed,
+                        b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, None, b.workspace,
+                        stream=stream)
+        ev2[k][1].record(stream)
+    torch.cuda.synchronize()
+    k1_ms = float(np.mean([a.elapsed_time(z) for a, z in ev2]))
+    log(f"[bench] logits kernel (pass without the expectation): {k1_ms:.3f} ms")
+
     flops = algorithmic_flops(wl)
-    ach_tflops = flops / (vp_avg * 1e-3) / 1e12
+    flops_k1 = 2.0 * wl.R * wl.V * wl.d
+    ach_k1 = flops_k1 / (k1_ms * 1e-3) / 1e12
+    gemm_path = wl.d % 128 == 0 and os.environ.get("DG_VOCAB_PATH") is None
     positions = wl.R
     res = {
         "metric": "canvas-positions/sec per denoise step",
@@ -144,13 +201,14 @@ def main() -> int:
                    "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget},
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "vocab_pass": {"avg_launch_ms": vp_avg, "algorithmic_flops": flops,
+                       "achieved_tflops": flops / (vp_avg * 1e-3) / 1e12},
         "roofline": {
-            "kernel": "k_vp_fused (dg_vocab_pass: init + fused kernel + combine)"
-                      if wl.d % 256 == 0 and os.environ.get("DG_VOCAB_PATH") != "split"
-                      else "dg_vocab_pass (split kernels)",
-            "bound": "mfma", "achieved": ach_tflops, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": ach_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-            "algorithmic_flops_per_launch": flops, "avg_launch_ms": vp_avg},
+            "kernel": "k_gemm_logits" if gemm_path else "dg_vocab_pass (non-default path)",
+            "bound": "mfma", "achieved": ach_k1, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": ach_k1 / PEAK_BF16_TFLOPS,
+            "traffic": measured_traffic(args.workload) if gemm_path else None,
+            "algorithmic_flops_per_launch": flops_k1, "avg_launch_ms": k1_ms},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f}s of oracle work)")
