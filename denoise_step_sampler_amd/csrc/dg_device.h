@@ -26,7 +26,7 @@ constexpr uint32_t kTagQSample = 0x51534D50u;
 // with the round key; the key advances by the Weyl constants between rounds.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll 1
+#pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;

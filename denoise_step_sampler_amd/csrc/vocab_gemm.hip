@@ -224,6 +224,9 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
                                         const f32x16& s3, int vt0, int V, float c2,
                                         uint32_t row, uint32_t step, uint32_t k0, uint32_t k1,
                                         uint16_t* pt, int* ref_out, LdsRowAcc* lds_st) {
+  // HIP contracts a * b - c into one fma by default, which would round dz once instead of
+  // twice and break the bit-for-bit recomputation in the combine
+#pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int vb0 = vt0 + 4 * (lane >> 5);
   float m = -INFINITY, amv = -INFINITY;
