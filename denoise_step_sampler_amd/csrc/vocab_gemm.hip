@@ -609,21 +609,29 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f3
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// B operand of v_mfma_f32_16x16x32_bf16 for 16 columns at byte offset cbyte of the staged
-// E rows [k0, k0 + 32) (row pitch `pitch` bytes): lane (g = lane / 16, i = lane % 16) needs
+// Bank swizzle of the staged E rows of the expectation pass: the 32-byte column pair p of
+// staged row `row` sits at pair p ^ e_swz(row).  A transpose read touches, per lane group,
+// rows k0 + 8 g + (0..3) (and + 4): with 16 pairs a row (NCB >= 4, 512- or 256-byte rows, so
+// every row starts on the same bank) the low two row bits and bit 3 spread those rows over
+// the eight 32-byte bank windows; with 4 pairs a row (NCB = 2, two rows per 256 bytes) row
+// bit 0 already alternates the half, so bits 1 and 3 pick the pair.
+template <int NCB>
+__device__ __forceinline__ int e_swz(int row) {
+  return NCB >= 4 ? ((row & 3) | (((row >> 3) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+}
+
+// B operand of v_mfma_f32_16x16x32_bf16 for 16 columns of the staged E rows [k0, k0 + 32)
+// (k0 a multiple of 32; row pitch `pitch` bytes): lane (g = lane / 16, i = lane % 16) needs
 // E[k0 + 8 g + 0..7][col i].  Two transpose reads: lane j of a 16-lane group addresses row
-// k0 + 8 g + 4 half + j / 4, columns 4 (j % 4) .. + 3; lane i then holds rows + 0..3 of
-// column i.
-__device__ __forceinline__ u32x4 e_frag(const lds_char* e, int pitch, int k0, int cbyte) {
-  const int lane = threadIdx.x & 63;
-  const int gq = lane >> 4, j = lane & 15;
-  const int row = k0 + 8 * gq + (j >> 2);
-  const int off = row * pitch + cbyte + 8 * (j & 3);
+// k0 + 8 g + 4 half + j / 4, bytes 8 (j % 4) .. + 7 of the columns' 32-byte pair; lane i then
+// holds rows + 0..3 of column i.  `a` is the lane's byte address of row 8 g + j / 4 and of the
+// columns' swizzled pair (row * pitch + 32 (pair ^ e_swz(row)) + 8 (j % 4)).
+__device__ __forceinline__ u32x4 e_frag(const lds_char* e, int pitch, int k0, int a) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(const_cast<lds_char*>(e) + off));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(const_cast<lds_char*>(e) + off + 4 * pitch));
+  const lds_char* q = e + a + k0 * pitch;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q + 4 * pitch));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
@@ -754,7 +762,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   const int v00 = u.t0 * kTile;
   const int nkc = (u.t1 - u.t0) * (kTile / kKC);
   const int erow0 = lane / kC16;                     // row within the copy
-  const uint32_t ecol = 16u * (uint32_t)(lane % kC16);
+  // swizzled 16-byte column chunk this lane fetches into its (linear) LDS slot; the rows a
+  // lane fills, kRowsPerCopy (w + 8 m) + erow0, agree in their low four bits for every m, so
+  // one value serves all of the lane's copies
+  static_assert((8 * kRowsPerCopy) % 16 == 0, "copies of one lane share the swizzle");
+  static_assert(kC16 >= 8 && (NCB >= 4 ? kC16 >= 16 : true), "swizzle stays within a row");
+  const uint32_t ecol =
+      16u * (uint32_t)((lane % kC16) ^ (2 * e_swz<NCB>(kRowsPerCopy * w + erow0)));
+  // this lane's transpose-read address of column block 0 (block cb: ea0 ^ 32 cb; the
+  // swizzle is an XOR on the pair index and the blocks of a wave are pairs 8 cw .. 8 cw + 7,
+  // or 4 cw .. + 3, or 2 cw .. + 1: XOR with 32 cb stays among them)
+  const int erl = 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int ea0 = erl * kPitchE + ((32 * NCB * cw) ^ (32 * e_swz<NCB>(erl))) + 8 * (lane & 3);
   const uint32_t a0 = (uint32_t)(uintptr_t)(lds_char*)st0, a1 = (uint32_t)(uintptr_t)(lds_char*)st1;
 
   auto issue = [&](int kc, uint32_t stg) {
@@ -766,9 +785,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     const int vb = min(v00 + kc * kKC, V - 1);
     const int lim = V - 1 - vb;
     const char* eb = ebase + (size_t)vb * epitch;
+    // the lane's first row, opaque here so that each copy's clamped row is formed next to
+    // its copy (three VALU operations) instead of being kept per copy for the whole loop
+    int row0 = kRowsPerCopy * w + erow0;
+    asm volatile("" : "+v"(row0));
 #pragma unroll
     for (int m = 0; m < kNEw; ++m) {
-      const int row = kRowsPerCopy * (w + 8 * m) + erow0;
+      const int row = row0 + 8 * kRowsPerCopy * m;
       dma_asm(eb, (uint32_t)min(row, lim) * epitch + ecol,
               stg + (uint32_t)kPB + 1024u * (uint32_t)(w + 8 * m));
     }
@@ -790,6 +813,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     for (int rb = 0; rb < 4; ++rb) sh7[rb] = ((shw >> (8 * rb)) & 0xFFu) << 7;
     const lds_char* sp = (const lds_char*)sc;
     const lds_char* se = (const lds_char*)(sc + kPB);
+    // the swizzle term, opaque to the compiler per chunk: the swizzled read addresses are
+    // formed next to their reads instead of being hoisted out of the loop (which holds one
+    // register per column block for the whole loop and spills)
+    int ea = ea0;
+    asm volatile("" : "+v"(ea));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 fa[4];
@@ -798,7 +826,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
         fa[rb] = shift_down(lds_read16(sp + ((4 * rw + rb) * 2 + ks) * 1024 + 16 * lane), sh7[rb]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const u32x4 fb = e_frag(se, kPitchE, 32 * ks, 2 * (16 * NCB * cw + 16 * cb));
+        const u32x4 fb = e_frag(se, kPitchE, 32 * ks, ea ^ (32 * cb));
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
       }
