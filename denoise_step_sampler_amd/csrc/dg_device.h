@@ -31,9 +31,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
     const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
     u32x4 n;
-    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    // three-way XORs as one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+    n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);
     n.y = (uint32_t)p1;
-    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
     n.w = (uint32_t)p0;
     c = n;
     k0 += 0x9E3779B9u;
@@ -53,15 +54,16 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 
 // Gumbel noise in base-2 units, g * log2(e) = -log2(-ln u), for the 32-bit word x with
 // u = ((x >> 9) + 0.5) 2^-23.  -ln u is taken from w = 1 - u (exact in fp32) by its series
-// when w < 1/16, so that draws near u = 1 (the large Gumbel values that decide the sample)
-// keep full relative precision; otherwise from the hardware log2.
+// w + w^2/2 + w^3/3 when w < 2^-6 (truncation below w^3/4 <= 1e-6 relative), so that draws
+// near u = 1 (the large Gumbel values that decide the sample) keep full relative precision;
+// otherwise from the hardware log2 (there -ln u >= 0.0156, so an absolute error of the log
+// near 1e-7 stays below 1e-5 relative).
 __device__ __forceinline__ float gumbel2_from_word(uint32_t x) {
   const float u = ((float)(x >> 9) + 0.5f) * 0x1p-23f;
-  const float w = ((float)((~x) >> 9) + 0.5f) * 0x1p-23f;
-  const float series =
-      w * (1.0f + w * (0.5f + w * (0.33333333f + w * (0.25f + w * (0.2f + w * 0.16666667f)))));
+  const float w = 1.0f - u;  // exact: both are odd multiples of 2^-24 below 1
+  const float series = w * (1.0f + w * (0.5f + w * 0.33333333f));
   const float direct = -hw_log2(u) * kLn2;
-  const float e = (w < 0.0625f) ? series : direct;
+  const float e = (w < 0.015625f) ? series : direct;
   return -hw_log2(e);
 }
 
@@ -72,8 +74,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+// acc + the two bf16 halves of w (one v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(float acc, uint32_t w) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -100,6 +110,13 @@ __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m,
 __device__ __forceinline__ int xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
 // (value, index) pair: larger value wins, ties go to the smaller index.
+// Running argmax over entries met in increasing index order: a later entry replaces the
+// current one only when strictly larger, which keeps the smallest index among equal values.
+__device__ __forceinline__ void argmax_next(float& v, int& i, float v2, int i2) {
+  const bool take = v2 > v;
+  v = take ? v2 : v;
+  i = take ? i2 : i;
+}
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
   const bool take = (v2 > v) | ((v2 == v) & (i2 < i));  // branch-free: selects, no exec masks
   v = take ? v2 : v;

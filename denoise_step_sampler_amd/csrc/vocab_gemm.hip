@@ -236,7 +236,7 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
     for (int i = 0; i < 16; ++i) {
       const int v = vb + 8 * (i >> 2) + (i & 3);
       const float x = v < V ? sb[i] : -INFINITY;
-      argmax_merge(amv, ami, x, v);
+      argmax_next(amv, ami, x, v);  // v increases along the scan
       m = fmaxf(m, __fmul_rn(x, c2));
     }
   };
@@ -300,18 +300,18 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
           const float pe = ok ? hw_exp2(dz) : 0.0f;
           ls += pe;
           as += pe * (ok ? dz : 0.0f);
-          argmax_merge(gv, gi, ok ? z2 + g2 : -INFINITY, vb + j);
+          argmax_next(gv, gi, ok ? z2 + g2 : -INFINITY, vb + j);
           pv[j] = pe;
         } else {
           const float pe = hw_exp2(dz);
           ls += pe;
           as += pe * dz;
-          argmax_merge(gv, gi, z2 + g2, vb + j);
+          argmax_next(gv, gi, z2 + g2, vb + j);  // entries in increasing order
           pv[j] = pe;
         }
       }
       const uint32_t w01 = pack_bf16x2(pv[0], pv[1]), w23 = pack_bf16x2(pv[2], pv[3]);
-      lsb += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+      lsb = add_bf16x2(add_bf16x2(lsb, w01), w23);
       *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
     }
   };
