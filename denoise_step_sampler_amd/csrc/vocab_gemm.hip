@@ -57,6 +57,7 @@ constexpr int kRow = 2 * kKC;   // bytes of one staged row: one 128-byte line
 constexpr int kLanesMax = 256;  // vocabulary lanes per canvas at most (one canvas per GPU)
 constexpr int kWG = 256;        // workgroups per round of the logits pass
 constexpr int kFacStride = 72;  // floats per row of the combine's weights
+constexpr int kRoundMax = 32;   // canvases per round of the logits pass (four per XCD)
 
 __device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
@@ -65,6 +66,21 @@ __device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
 __device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_dst, 16, 0, 0);
 }
+
+// LDS DMA issued as inline assembly: the compiler does not see these copies, so it neither
+// waits for them before unrelated LDS reads (it cannot tell the two stages apart for the
+// transpose reads) nor counts them; the kernel waits for them explicitly (vm_wait) before the
+// barrier that publishes a stage.  base is wave-uniform, off per lane, dst the wave-uniform
+// LDS address of the 1 KB destination; the one-cycle nop covers the M0 -> LDS DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_asm(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(dst)
+               : "m0");
+}
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -77,14 +93,16 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // ---------------------------------------------------------------------------------------
 // Schedule of the logits pass.  Canvases are taken in `order` (non-commit first) in rounds
-// of g = a power of two <= 16; a round gives each canvas L = 256 / g vocabulary lanes, and
-// lane l of a canvas processes tiles l, l + L, l + 2L, ...  Workgroup b runs on XCD b % 8
+// of g = a power of two <= kRoundMax; a round gives each canvas L = 256 / g vocabulary
+// lanes, and lane l of a canvas processes tiles l, l + L, l + 2L, ...  The canvases of an
+// XCD read the same E tiles at about the same time, so each E line is fetched into its L2
+// once for all of them.  Workgroup b runs on XCD b % 8
 // (the dispatcher deals workgroups to the XCDs round-robin), slot b / 8:
 //   g >= 8: canvas k = 8 (slot % (g/8)) + xcd, lane = slot / (g/8)   (g/8 canvases per XCD)
 //   g <  8: canvas k = xcd % g,                lane = 32 (xcd / g) + slot
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int round_size(int remaining) {
-  int g = 16;
+__device__ __forceinline__ int round_size(int remaining, int gmax) {
+  int g = gmax;
   while (g > remaining) g >>= 1;
   return g;
 }
@@ -111,10 +129,10 @@ __device__ __forceinline__ Lane lane_of(int b, int g) {
 }
 
 // Lanes per canvas of the canvas at position pos of the order (same rounds as above).
-__device__ __forceinline__ int lanes_at(int pos, int n_canvas) {
+__device__ __forceinline__ int lanes_at(int pos, int n_canvas, int gmax) {
   int start = 0;
   for (;;) {
-    const int g = round_size(n_canvas - start);
+    const int g = round_size(n_canvas - start, gmax);
     if (pos < start + g) return kWG / g;
     start += g;
   }
@@ -206,6 +224,7 @@ struct GemmK {
   int ncb;            // 16-column blocks per wave in the expectation pass
   int n_colblk;       // d / (32 ncb)
   int flat;           // expectation units mapped flat (1) or pair-per-XCD (0)
+  int gmax;           // largest round of the logits pass (canvases)
 };
 
 // Per-lane epilogue of one row (32-row block of this wave) over the wave's 128 entries: the
@@ -356,18 +375,18 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
   }
 }
 
-// Round r of the canvas order: canvases [start, start + g).  Rounds of 16 while 16 or more
-// remain, then the binary decomposition of the rest (8, 4, 2, 1).
-__device__ __forceinline__ void round_info(int r, int n_canvas, int& start, int& gsz) {
-  const int full = n_canvas / 16;
+// Round r of the canvas order: canvases [start, start + g).  Rounds of gmax while gmax or
+// more remain, then the binary decomposition of the rest.
+__device__ __forceinline__ void round_info(int r, int n_canvas, int gmax, int& start, int& gsz) {
+  const int full = n_canvas / gmax;
   if (r < full) {
-    start = 16 * r;
-    gsz = 16;
+    start = gmax * r;
+    gsz = gmax;
     return;
   }
-  start = 16 * full;
+  start = gmax * full;
   int rem = n_canvas - start, k = r - full;
-  for (int gg = 8; gg >= 1; gg >>= 1) {
+  for (int gg = gmax >> 1; gg >= 1; gg >>= 1) {
     if (rem & gg) {
       if (k == 0) {
         gsz = gg;
@@ -380,11 +399,22 @@ __device__ __forceinline__ void round_info(int r, int n_canvas, int& start, int&
   gsz = 0;
 }
 
-// One workgroup per (round, slot): the tiles t = lane, lane + L, ... of one canvas.
+// One workgroup per (round, slot): the tiles t = lane, lane + L, ... of one canvas.  K is
+// staged in chunks of 32 elements (64-byte rows: 256 E rows + 256 h rows, 32 KB a stage)
+// through a ring of four stages: a chunk's copies are issued three chunks before it is
+// multiplied, which covers the latency of E lines that miss in L2.
+constexpr int kKC1 = 32;           // K chunk of the logits pass
+constexpr int kRow1 = 2 * kKC1;    // bytes of one staged row
+constexpr int kNst1 = 4;           // stages
+
+// 16-byte slot of segment s in staged 64-byte row r: the sixteen consecutive rows one
+// ds_read_b128 pass serves fall on distinct banks.
+__device__ __forceinline__ int swz1(int r) { return (r >> 2) & 3; }
+
 __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
-  constexpr int kStage = 512 * kRow;  // 256 E rows + 256 h rows
-  __shared__ __attribute__((aligned(1024))) char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  constexpr int kStage = 512 * kRow1;  // 256 E rows + 256 h rows
+  constexpr int kHOff = kTile * kRow1;
+  __shared__ __attribute__((aligned(1024))) char stg[kNst1][kStage];
   const uint16_t* E = g.a.E;
   const uint16_t* h = g.a.h;
   const int V = g.a.V, d = g.a.d, n_canvas = g.a.n_canvas;
@@ -392,54 +422,61 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int vh = w & 1, rq = w >> 1;  // wave tile: vocabulary half vh x rows [64 rq, 64 rq + 64)
   const int T = g.n_tiles;
-  const int nk = d / kKC;
+  const int nk = d / kKC1;  // a multiple of kNst1 (d % 128 == 0)
   const size_t R = (size_t)n_canvas * kTile;
 
   int start, gsz;
-  round_info(blockIdx.x >> 8, n_canvas, start, gsz);
+  round_info(blockIdx.x >> 8, n_canvas, g.gmax, start, gsz);
   const Lane ln = lane_of(blockIdx.x & 255, gsz);
   if (gsz == 0 || ln.lane >= T) return;
   const int c = __builtin_amdgcn_readfirstlane(g.order[start + ln.k]);
   const int p = __builtin_amdgcn_readfirstlane(g.pos[c]);
   const bool heavy = p < *g.n_nc_p;
 
-  // LDS fragment offsets (stage-relative) of this lane for the four 16-wide K steps
-  const int sw = swz(fr);
-  uint32_t rdE[4], rdH[4];
+  // LDS fragment offsets (stage-relative) of this lane for the two 16-wide K steps
+  const int sw = swz1(fr);
+  uint32_t rdE[2], rdH[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    rdE[ks] = (uint32_t)((128 * vh + fr) * kRow + 16 * ((2 * ks + fh) ^ sw));
-    rdH[ks] = (uint32_t)(kTile * kRow + (64 * rq + fr) * kRow + 16 * ((2 * ks + fh) ^ sw));
+  for (int ks = 0; ks < 2; ++ks) {
+    rdE[ks] = (uint32_t)((128 * vh + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
+    rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
   }
-  // DMA: wave w copies E rows and h rows [32 w, 32 w + 32) of the tile, 8 rows per
-  // instruction; lane -> row 8 j + lane / 8, slot lane % 8, global segment slot ^ swz(row).
-  // Sources: a wave-uniform base plus a 32-bit lane offset.
-  const int dlrow = lane >> 3;
+  // DMA: a copy moves 16 staged rows (1 KB); lane -> row 16 j + lane / 4, slot lane % 4,
+  // global segment slot ^ swz1(row) = slot ^ ((lane / 16) % 4).  Wave w copies E rows and
+  // h rows [32 w, 32 w + 32) of the stage, two copies each.  Sources: a wave-uniform base
+  // plus a 32-bit lane offset.
+  const int dlrow = lane >> 2;
   const uint32_t pitch = 2u * (uint32_t)d;
-  uint32_t offJ[4];
+  const uint32_t seg = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  uint32_t offH[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    offJ[j] = (uint32_t)(8 * j + dlrow) * pitch + 16u * (uint32_t)((lane & 7) ^ swz(8 * j + dlrow));
+  for (int j = 0; j < 2; ++j) offH[j] = (uint32_t)(16 * j + dlrow) * pitch + seg;
   const char* hb = reinterpret_cast<const char*>(h) + ((size_t)c * kTile + 32 * w) * pitch;
   // E rows of the wave's block of tile tt, clamped to V - 1: base row and lane offsets
-  auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[4]) {
+  auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[2]) {
     const int r0 = tt * kTile + 32 * w;
     const int rb = min(r0, V - 1);
     eb = reinterpret_cast<const char*>(E) + (size_t)rb * pitch;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rv = min(r0 + 8 * j + dlrow, V - 1);
-      oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz(8 * j + dlrow));
+    for (int j = 0; j < 2; ++j) {
+      const int rv = min(r0 + 16 * j + dlrow, V - 1);
+      oe[j] = (uint32_t)(rv - rb) * pitch + seg;
     }
   };
-  // copies of chunk kc of a tile whose E source is (eb, oe)
-  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[4], char* stg) {
-    const uint32_t kb = (uint32_t)kc * (2u * kKC);
+  // copies of chunk kc of a tile whose E source is (eb, oe) into the stage at LDS address
+  // dst (inline-assembly DMA: the compiler would otherwise wait for every copy in flight
+  // before the next read of LDS, the stages it cannot tell apart)
+  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[2], uint32_t dst) {
+    const uint32_t kb = (uint32_t)kc * (uint32_t)kRow1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(eb + kb + oe[j], stg + 1024 * (4 * w + j));
+    for (int j = 0; j < 2; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(2 * w + j));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(hb + kb + offJ[j], stg + kTile * kRow + 1024 * (4 * w + j));
+    for (int j = 0; j < 2; ++j)
+      dma_asm(hb + kb, offH[j], dst + (uint32_t)kHOff + 1024u * (uint32_t)(2 * w + j));
   };
+  uint32_t sa[kNst1];  // LDS addresses of the stages
+#pragma unroll
+  for (int q = 0; q < kNst1; ++q) sa[q] = (uint32_t)(uintptr_t)(lds_char*)stg[q];
 
   f32x16 acc[4][2];
   // running statistics of this wave's 64 rows: [wave][nb][row in block]
@@ -466,38 +503,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     }
   }
 
-  // compute the chunk in stage sc; meanwhile copy chunk kn of the tile (eb, oe) into sn
-  auto chunk = [&](const char* sc, char* sn, int kn, const char* eb, const uint32_t (&oe)[4]) {
-    vm_wait<0>();
+  // compute the chunk in stage sc once its copies have landed (the two chunks issued after
+  // it, 8 copies of this wave, may still be in flight); meanwhile copy chunk kn of the tile
+  // (eb, oe) into sn, the stage every wave finished reading before the barrier
+  auto chunk = [&](const char* sc, uint32_t sn, int kn, const char* eb, const uint32_t (&oe)[2]) {
+    vm_wait<8>();
     __syncthreads();
     const lds_char* s = (const lds_char*)sc;
     u32x4 fa[2][4], fb[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) fa[0][mb] = lds_read16(s + rdE[0] + 32 * kRow * mb);
+    for (int mb = 0; mb < 4; ++mb) fa[0][mb] = lds_read16(s + rdE[0] + 32 * kRow1 * mb);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow * nb);
+    for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow1 * nb);
     issue(kn, eb, oe, sn);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cb = ks & 1;
-      if (ks < 3) {
+    for (int mb = 0; mb < 4; ++mb) fa[1][mb] = lds_read16(s + rdE[1] + 32 * kRow1 * mb);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          fa[cb ^ 1][mb] = lds_read16(s + rdE[ks + 1] + 32 * kRow * mb);
+    for (int nb = 0; nb < 2; ++nb) fb[1][nb] = lds_read16(s + rdH[1] + 32 * kRow1 * nb);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          fb[cb ^ 1][nb] = lds_read16(s + rdH[ks + 1] + 32 * kRow * nb);
-      }
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[cb][mb], fb[cb][nb], acc[mb][nb]);
-    }
-    // order: the stage's first reads, then per 16-wide step its MFMAs interleaved with the
-    // next step's reads (and, in the first step, this wave's eight copies of the next chunk)
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = mfma32x32x16(fa[ks][mb], fb[ks][nb], acc[mb][nb]);
+    // order: the first step's reads, then its MFMAs interleaved with the second step's
+    // reads and this wave's four copies, then the second step's MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -505,24 +539,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
   };
 
   const float c2 = kLog2e / g.a.temperature[c];
   const uint32_t step = (uint32_t)g.a.step[c];
   const uint32_t k0 = g.a.k0, k1 = g.a.k1;
-  const int rloc0 = 64 * rq + fr, rloc1 = rloc0 + 32;  // rows (in the canvas) of blocks 0, 1
+  const int rloc0 = 64 * rq + fr;  // row (in the canvas) of block 0; block 1 is 32 rows on
   const uint32_t row0 = (uint32_t)(c * kTile + rloc0), row1 = row0 + 32;
   // weight blocks of rows rloc0 (row16 = 16 p + 4 rq + fr / 16) and rloc0 + 32 (row16 + 2);
   // lane group (fr % 16, fh) at element 8 (fr % 16) + 4 fh of a block
@@ -531,28 +556,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   uint16_t* prow1 = prow0 + 2 * nvb * 512;
 
   const char* eb;
-  uint32_t oe[4];
+  uint32_t oe[2];
   e_src(ln.lane, eb, oe);
-  issue(0, eb, oe, st0);
-  // nk is even: every tile starts on stage 0, and its last chunk copies the next tile's
-  // first chunk (or, after the last tile, repeats this tile's; never read)
+#pragma unroll
+  for (int q = 0; q < kNst1 - 1; ++q) issue(q, eb, oe, sa[q]);
+  // nk is a multiple of four: every tile starts on stage 0; its last three chunks copy the
+  // next tile's first three (after the last tile, this tile's again; never read)
   for (int tt = ln.lane; tt < T; tt += ln.L) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{0};
     const char* ebn;
-    uint32_t oen[4];
+    uint32_t oen[2];
     e_src(tt + ln.L < T ? tt + ln.L : tt, ebn, oen);
-    for (int kc = 0; kc < nk - 2; kc += 2) {
-      chunk(st0, st1, kc + 1, eb, oe);
-      chunk(st1, st0, kc + 2, eb, oe);
+    // the previous epilogue's stores sit behind this tile's first copies in the count
+    vm_wait<0>();
+    for (int kc = 0; kc < nk - kNst1; kc += kNst1) {
+      chunk(stg[0], sa[3], kc + 3, eb, oe);
+      chunk(stg[1], sa[0], kc + 4, eb, oe);
+      chunk(stg[2], sa[1], kc + 5, eb, oe);
+      chunk(stg[3], sa[2], kc + 6, eb, oe);
     }
-    chunk(st0, st1, nk - 1, eb, oe);
-    chunk(st1, st0, 0, ebn, oen);
+    chunk(stg[0], sa[3], nk - 1, eb, oe);
+    chunk(stg[1], sa[0], 0, ebn, oen);
+    chunk(stg[2], sa[1], 1, ebn, oen);
+    chunk(stg[3], sa[2], 2, ebn, oen);
     eb = ebn;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) oe[j] = oen[j];
+    for (int j = 0; j < 2; ++j) oe[j] = oen[j];
     // ---- epilogue of tile tt
     const int vt0 = tt * kTile + kHalf * vh;
     int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
@@ -672,20 +704,6 @@ __device__ __forceinline__ Unit unit_at(int x, int lu, int n_nc, int n_range, in
   return u;
 }
 
-// LDS DMA issued as inline assembly: the compiler does not see these copies, so it neither
-// waits for them before unrelated LDS reads (it cannot tell the two stages apart for the
-// transpose reads) nor counts them; the kernel waits for them explicitly (vm_wait) before the
-// barrier that publishes a stage.  base is wave-uniform, off per lane, dst the wave-uniform
-// LDS address of the 1 KB destination; the one-cycle nop covers the M0 -> LDS DMA hazard.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_asm(const void* base, uint32_t off, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(dst)
-               : "m0");
-}
-#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
@@ -917,7 +935,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
   const int c = r / kTile, i = r - c * kTile;
   const int p = g.pos[c];
   const bool heavy = p < *g.n_nc_p;
-  const int L = lanes_at(p, n_canvas);
+  const int L = lanes_at(p, n_canvas, g.gmax);
   const int n_slot = 2 * min(L, g.n_tiles);
   const size_t plane = (size_t)2 * kLanesMax * R;
   float m = -INFINITY, l = 0.0f, a = 0.0f, lb = 0.0f, amv = -INFINITY, gv = -INFINITY;
@@ -1084,7 +1102,8 @@ GemmPlan gemm_plan(int n_canvas, int V, int d) {
   p.vpad = (size_t)p.n_tiles * kTile;
   pick_selfcond_tiling(n_canvas, p.n_tiles, d, &p.ncb, &p.n_range, &p.flat);
   p.n_colblk = d / (32 * p.ncb);
-  p.n_rounds = n_canvas / 16 + __builtin_popcount((unsigned)(n_canvas % 16));
+  p.gmax = kRoundMax;
+  p.n_rounds = n_canvas / p.gmax + __builtin_popcount((unsigned)(n_canvas % p.gmax));
   p.n_units_xcd = ((n_canvas * p.n_range + 7) / 8) * p.n_colblk;
   p.n_units = n_canvas * p.n_range * p.n_colblk;
   size_t off = 0;
@@ -1140,6 +1159,7 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   g.ncb = p.ncb;
   g.n_colblk = p.n_colblk;
   g.flat = p.flat;
+  g.gmax = p.gmax;
   hipLaunchKernelGGL(k_gemm_init, dim3(1), dim3(256), 0, stream, a.commit, a.n_canvas, order,
                      pos, n_nc);
   hipError_t e = hipGetLastError();
