@@ -21,18 +21,21 @@
 //                   M = max ref by subtracting (M - ref) from its bf16 exponent field with
 //                   unsigned saturation (v_pk_sub_u16 clamp): an exact power-of-two scaling
 //                   (flush to zero below 2^-126), so every weight is rounded to bf16 once.
-//   k_gemm_combine  per row: merges the statistic partials (max/sum/moment merge of the
+//   k_gemm_rows     per row: merges the statistic partials (max/sum/moment merge of the
 //                   chunked logsumexp in "DiffusionGemma-Lite", (value, -index) max for the
-//                   tokens) and sums the expectation partials with weights 2^(M_s - m) / l.
+//                   tokens), corrects the four largest weights' bf16 rounding exactly and
+//                   forms the range weights 2^(M_s - m) / lb of the expectation partials;
+//   k_gemm_sc       per row and column: the weighted sum of the expectation partials.
 //
-// Both GEMMs are persistent (one 512-thread workgroup per CU), stage operands through LDS
-// by LDS DMA (global_load_lds_dwordx4, 1 KB per instruction) into two 64-element K stages,
-// and interleave the DMA issue and the fragment reads with the MFMAs.  Work is mapped to
-// the eight XCDs so that the CUs of one XCD share operands through their L2: the logits
-// pass runs up to two canvases per XCD over the same vocabulary tiles (h of both canvases
-// stays in L2, each E line is read by both), the expectation pass runs the column blocks
-// of one (range, canvas) pair on one XCD (the weights are read once from HBM, E of the
-// range by every canvas of the XCD).
+// Both GEMMs run 512-thread workgroups (one per CU) on 256 x 256 tiles and stage their
+// operands through LDS by LDS DMA (global_load_lds_dwordx4, 1 KB per instruction, issued as
+// inline assembly with explicit vmcnt waits) in a ring of four stages of 32-element K
+// chunks, so each chunk's copies are issued three chunks before it is multiplied.  Work is
+// mapped to the eight XCDs so that the CUs of one XCD share operands through their L2: the
+// logits pass runs four canvases per XCD over the same vocabulary tiles (each E line is
+// read by all four), the expectation pass runs the column blocks of one (range, canvas)
+// pair on one XCD (the weights are read once from HBM, E of the range by every canvas of
+// the XCD).
 #include <stdlib.h>
 #include <string.h>
 
@@ -45,15 +48,11 @@ namespace dg {
 namespace {
 
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 256;      // vocabulary tile of the logits pass (and rows per canvas)
 constexpr int kHalf = 128;      // granularity of the weight references
-constexpr int kKC = 64;         // K chunk (elements) per LDS stage
-constexpr int kRow = 2 * kKC;   // bytes of one staged row: one 128-byte line
 constexpr int kLanesMax = 256;  // vocabulary lanes per canvas at most (one canvas per GPU)
 constexpr int kWG = 256;        // workgroups per round of the logits pass
 constexpr int kFacStride = 72;  // floats per row of the combine's weights
@@ -63,9 +62,6 @@ __device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
 }
 
-__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds_dst, 16, 0, 0);
-}
 
 // LDS DMA issued as inline assembly: the compiler does not see these copies, so it neither
 // waits for them before unrelated LDS reads (it cannot tell the two stages apart for the
@@ -87,9 +83,6 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// 16-byte slot of segment s in staged row r: XOR swizzle over the eight segments of the
-// 128-byte row, so that the rows one ds_read_b128 pass serves fall on distinct banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // ---------------------------------------------------------------------------------------
 // Schedule of the logits pass.  Canvases are taken in `order` (non-commit first) in rounds
@@ -717,21 +710,23 @@ template <int NCB>
 __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int BN = 32 * NCB;            // columns of a unit
   constexpr int kPitchE = 2 * BN;         // bytes of one staged E row
-  constexpr int kPB = kTile * kRow;       // weights: 256 rows x 64 entries (32 KB)
-  constexpr int kEB = kKC * kPitchE;      // E: 64 rows x BN columns
+  constexpr int kKC2 = 32;                // K chunk (vocabulary entries) per stage
+  constexpr int kNst2 = 4;                // stages: copies run three chunks ahead
+  constexpr int kPB = kTile * 2 * kKC2;   // weights: 16 fragment blocks of 1 KB (16 KB)
+  constexpr int kEB = kKC2 * kPitchE;     // E: 32 rows x BN columns
   constexpr int kStage = kPB + kEB;
-  constexpr int kNE = kEB / 1024;         // E copies per stage (4 NCB)
-  constexpr int kNEw = kNE / 8;           // E copies per wave
-  static_assert(kNE % 8 == 0, "E copies must divide among the eight waves");
+  constexpr int kNE = kEB / 1024;         // E copies per stage (2 NCB)
+  constexpr int kNEw = kNE >= 8 ? kNE / 8 : 1;  // E copies per wave (waves >= kNE repeat one)
+  static_assert(kNE % 8 == 0 || kNE < 8, "E copies must divide among the eight waves");
+  constexpr int kCpw = 2 + kNEw;          // copies per wave and chunk
   constexpr int kC16 = BN / 8;            // 16-byte chunks per staged E row
   constexpr int kRowsPerCopy = 1024 / kPitchE;  // E rows per 1 KB copy
-  __shared__ __attribute__((aligned(1024))) char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char stg[kNst2][kStage];
   // exponent shifts: byte (ht, row) at 256 ht + 64 rw + 4 (row % 16) + rb for
   // row = 64 rw + 16 rb + row % 16, so one 32-bit read gives a lane its four A rows
   __shared__ __attribute__((aligned(16))) uint8_t shb[2 * kMaxUnitTiles * kTile];
   // the prologue's two partial maxima per row live in stage 1 (no copy has been issued yet)
-  int (*sM)[kTile] = reinterpret_cast<int (*)[kTile]>(st1);
+  int (*sM)[kTile] = reinterpret_cast<int (*)[kTile]>(stg[1]);
   const int V = g.a.V, d = g.a.d;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -767,10 +762,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   int M[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) M[rb] = sM[0][64 * rw + 16 * rb + ar];
+  __syncthreads();  // sM (stage 1) is overwritten by the first copies
 
-  // ---- copies.  Weights: instruction j of wave w covers fragment block (row16 2w + j / 2,
-  // ks j % 2) of the chunk (LDS 1 KB (4 w + j)); E: instruction m covers the stage's 1 KB
-  // number w + 8 m, i.e. rows kRowsPerCopy (w + 8 m) + lane / kC16.
+  // ---- copies.  Weights: copy j of wave w moves the fragment block of row16 2 w + j for
+  // the chunk (LDS 1 KB number 2 w + j); E: copy m moves the stage's 1 KB number
+  // (w + 8 m) % kNE, i.e. rows kRowsPerCopy ((w + 8 m) % kNE) + lane / kC16.
   const size_t nvb = g.vpad / 32;
   const char* pbase = reinterpret_cast<const char*>(g.P) +
                       (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024;
@@ -778,40 +774,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   const uint32_t epitch = 2u * (uint32_t)d;
   const char* ebase = reinterpret_cast<const char*>(g.a.E) + (size_t)u.j * BN * 2;
   const int v00 = u.t0 * kTile;
-  const int nkc = (u.t1 - u.t0) * (kTile / kKC);
+  const int nkc = (u.t1 - u.t0) * (kTile / kKC2);  // a multiple of 8
   const int erow0 = lane / kC16;                     // row within the copy
+  const int ew = kNE >= 8 ? w : w % kNE;             // this wave's first E copy
   // swizzled 16-byte column chunk this lane fetches into its (linear) LDS slot; the rows a
-  // lane fills, kRowsPerCopy (w + 8 m) + erow0, agree in their low four bits for every m, so
+  // lane fills, kRowsPerCopy (ew + 8 m) + erow0, agree in their low four bits for every m, so
   // one value serves all of the lane's copies
   static_assert((8 * kRowsPerCopy) % 16 == 0, "copies of one lane share the swizzle");
   static_assert(kC16 >= 8 && (NCB >= 4 ? kC16 >= 16 : true), "swizzle stays within a row");
   const uint32_t ecol =
-      16u * (uint32_t)((lane % kC16) ^ (2 * e_swz<NCB>(kRowsPerCopy * w + erow0)));
+      16u * (uint32_t)((lane % kC16) ^ (2 * e_swz<NCB>(kRowsPerCopy * ew + erow0)));
   // this lane's transpose-read address of column block 0 (block cb: ea0 ^ 32 cb; the
   // swizzle is an XOR on the pair index and the blocks of a wave are pairs 8 cw .. 8 cw + 7,
   // or 4 cw .. + 3, or 2 cw .. + 1: XOR with 32 cb stays among them)
   const int erl = 8 * (lane >> 4) + ((lane & 15) >> 2);
   const int ea0 = erl * kPitchE + ((32 * NCB * cw) ^ (32 * e_swz<NCB>(erl))) + 8 * (lane & 3);
-  const uint32_t a0 = (uint32_t)(uintptr_t)(lds_char*)st0, a1 = (uint32_t)(uintptr_t)(lds_char*)st1;
-
-  auto issue = [&](int kc, uint32_t stg) {
+  uint32_t sa[kNst2];  // LDS addresses of the stages
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma_asm(pbase + ((size_t)(j >> 1) * nvb + (j & 1) + 2 * kc) * 1024, offP,
-              stg + 1024u * (uint32_t)(4 * w + j));
+  for (int q = 0; q < kNst2; ++q) sa[q] = (uint32_t)(uintptr_t)(lds_char*)stg[q];
+
+  // copies of chunk kc (clamped to the unit's last chunk: the copies issued past the end go
+  // to a stage nobody reads again)
+  auto issue = [&](int kc, uint32_t dst) {
+    kc = min(kc, nkc - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma_asm(pbase + ((size_t)j * nvb + kc) * 1024, offP, dst + 1024u * (uint32_t)(2 * w + j));
     // E rows past V - 1 (tail of the last tile, zero weights) read row V - 1
-    const int vb = min(v00 + kc * kKC, V - 1);
+    const int vb = min(v00 + kc * kKC2, V - 1);
     const int lim = V - 1 - vb;
     const char* eb = ebase + (size_t)vb * epitch;
     // the lane's first row, opaque here so that each copy's clamped row is formed next to
     // its copy (three VALU operations) instead of being kept per copy for the whole loop
-    int row0 = kRowsPerCopy * w + erow0;
+    int row0 = kRowsPerCopy * ew + erow0;
     asm volatile("" : "+v"(row0));
 #pragma unroll
     for (int m = 0; m < kNEw; ++m) {
       const int row = row0 + 8 * kRowsPerCopy * m;
       dma_asm(eb, (uint32_t)min(row, lim) * epitch + ecol,
-              stg + (uint32_t)kPB + 1024u * (uint32_t)(w + 8 * m));
+              dst + (uint32_t)kPB + 1024u * (uint32_t)(ew + 8 * m));
     }
   };
 
@@ -821,11 +822,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
 
-  // one chunk from stage sc with the shifts of its half tile; copies chunk kn into sn
-  auto chunk = [&](const char* sc, uint32_t sn, int kn, bool copy, uint32_t shw) {
-    vm_wait<0>();
+  // one chunk from stage sc once its copies have landed (the two chunks issued after it may
+  // still be in flight), with the shifts of its half tile; copies chunk kn into stage sn,
+  // which every wave finished reading before the barrier
+  auto chunk = [&](const char* sc, uint32_t sn, int kn, uint32_t shw) {
+    vm_wait<2 * kCpw>();
     __syncthreads();
-    if (copy) issue(kn, sn);
+    issue(kn, sn);
     uint32_t sh7[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) sh7[rb] = ((shw >> (8 * rb)) & 0xFFu) << 7;
@@ -836,27 +839,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     // register per column block for the whole loop and spills)
     int ea = ea0;
     asm volatile("" : "+v"(ea));
+    u32x4 fa[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 fa[4];
+    for (int rb = 0; rb < 4; ++rb)
+      fa[rb] = shift_down(lds_read16(sp + (4 * rw + rb) * 1024 + 16 * lane), sh7[rb]);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        fa[rb] = shift_down(lds_read16(sp + ((4 * rw + rb) * 2 + ks) * 1024 + 16 * lane), sh7[rb]);
+    for (int cb = 0; cb < NCB; ++cb) {
+      const u32x4 fb = e_frag(se, kPitchE, 0, ea ^ (32 * cb));
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const u32x4 fb = e_frag(se, kPitchE, 32 * ks, ea ^ (32 * cb));
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
-      }
+      for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
     }
   };
 
-  issue(0, a0);
+#pragma unroll
+  for (int q = 0; q < kNst2 - 1; ++q) issue(q, sa[q]);
   const lds_char* shp = (const lds_char*)shb + 64 * rw + 4 * ar;
-  for (int kc = 0; kc < nkc; kc += 2) {
-    const uint32_t shw = lds_u32(shp + (kc >> 1) * kTile);  // half tile kc / 2
-    chunk(st0, a1, kc + 1, true, shw);
-    chunk(st1, a0, kc + 2, kc + 2 < nkc, shw);
+  for (int kc = 0; kc < nkc; kc += kNst2) {
+    const uint32_t shw = lds_u32(shp + (kc >> 2) * kTile);  // half tile kc / 4
+    chunk(stg[0], sa[3], kc + 3, shw);
+    chunk(stg[1], sa[0], kc + 4, shw);
+    chunk(stg[2], sa[1], kc + 5, shw);
+    chunk(stg[3], sa[2], kc + 6, shw);
   }
   vm_wait<0>();
   // expectation partial of this unit; the column-block-0 unit also records the references
