@@ -393,16 +393,16 @@ __device__ __forceinline__ void round_info(int r, int n_canvas, int gmax, int& s
 }
 
 // One workgroup per (round, slot): the tiles t = lane, lane + L, ... of one canvas.  K is
-// staged in chunks of 32 elements (64-byte rows: 256 E rows + 256 h rows, 32 KB a stage)
-// through a ring of four stages: a chunk's copies are issued three chunks before it is
-// multiplied, which covers the latency of E lines that miss in L2.
-constexpr int kKC1 = 32;           // K chunk of the logits pass
+// staged in chunks of 64 elements (one 128-byte line per row: 256 E rows + 256 h rows,
+// 64 KB a stage) through two stages; whole lines per copy keep the L2 -> LDS stream at its
+// best rate, and a chunk's copies are issued a full chunk before it is multiplied.
+constexpr int kKC1 = 64;           // K chunk of the logits pass
 constexpr int kRow1 = 2 * kKC1;    // bytes of one staged row
-constexpr int kNst1 = 4;           // stages
+constexpr int kNst1 = 2;           // stages
 
-// 16-byte slot of segment s in staged 64-byte row r: the sixteen consecutive rows one
-// ds_read_b128 pass serves fall on distinct banks.
-__device__ __forceinline__ int swz1(int r) { return (r >> 2) & 3; }
+// 16-byte slot of segment s in staged 128-byte row r: XOR swizzle over the eight segments,
+// so that the sixteen consecutive rows one ds_read_b128 pass serves fall on distinct banks.
+__device__ __forceinline__ int swz1(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   constexpr int kStage = 512 * kRow1;  // 256 E rows + 256 h rows
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int vh = w & 1, rq = w >> 1;  // wave tile: vocabulary half vh x rows [64 rq, 64 rq + 64)
   const int T = g.n_tiles;
-  const int nk = d / kKC1;  // a multiple of kNst1 (d % 128 == 0)
+  const int nk = d / kKC1;  // even (d % 128 == 0)
   const size_t R = (size_t)n_canvas * kTile;
 
   int start, gsz;
@@ -426,46 +426,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   const int p = __builtin_amdgcn_readfirstlane(g.pos[c]);
   const bool heavy = p < *g.n_nc_p;
 
-  // LDS fragment offsets (stage-relative) of this lane for the two 16-wide K steps
+  // LDS fragment offsets (stage-relative) of this lane for the four 16-wide K steps
   const int sw = swz1(fr);
-  uint32_t rdE[2], rdH[2];
+  uint32_t rdE[4], rdH[4];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < 4; ++ks) {
     rdE[ks] = (uint32_t)((128 * vh + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
     rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
   }
-  // DMA: a copy moves 16 staged rows (1 KB); lane -> row 16 j + lane / 4, slot lane % 4,
-  // global segment slot ^ swz1(row) = slot ^ ((lane / 16) % 4).  Wave w copies E rows and
-  // h rows [32 w, 32 w + 32) of the stage, two copies each.  Sources: a wave-uniform base
-  // plus a 32-bit lane offset.
-  const int dlrow = lane >> 2;
+  // DMA: a copy moves 8 staged rows (1 KB); lane -> row 8 j + lane / 8, slot lane % 8,
+  // global segment slot ^ swz1(row).  Wave w copies E rows and h rows [32 w, 32 w + 32) of
+  // the stage, four copies each.  Sources: a wave-uniform base plus a 32-bit lane offset.
+  const int dlrow = lane >> 3;
   const uint32_t pitch = 2u * (uint32_t)d;
-  const uint32_t seg = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  uint32_t offH[2];
+  uint32_t offH[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) offH[j] = (uint32_t)(16 * j + dlrow) * pitch + seg;
+  for (int j = 0; j < 4; ++j)
+    offH[j] = (uint32_t)(8 * j + dlrow) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
   const char* hb = reinterpret_cast<const char*>(h) + ((size_t)c * kTile + 32 * w) * pitch;
   // E rows of the wave's block of tile tt, clamped to V - 1: base row and lane offsets
-  auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[2]) {
+  auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[4]) {
     const int r0 = tt * kTile + 32 * w;
     const int rb = min(r0, V - 1);
     eb = reinterpret_cast<const char*>(E) + (size_t)rb * pitch;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rv = min(r0 + 16 * j + dlrow, V - 1);
-      oe[j] = (uint32_t)(rv - rb) * pitch + seg;
+    for (int j = 0; j < 4; ++j) {
+      const int rv = min(r0 + 8 * j + dlrow, V - 1);
+      oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
     }
   };
   // copies of chunk kc of a tile whose E source is (eb, oe) into the stage at LDS address
   // dst (inline-assembly DMA: the compiler would otherwise wait for every copy in flight
   // before the next read of LDS, the stages it cannot tell apart)
-  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[2], uint32_t dst) {
+  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[4], uint32_t dst) {
     const uint32_t kb = (uint32_t)kc * (uint32_t)kRow1;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(2 * w + j));
+    for (int j = 0; j < 4; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(4 * w + j));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      dma_asm(hb + kb, offH[j], dst + (uint32_t)kHOff + 1024u * (uint32_t)(2 * w + j));
+    for (int j = 0; j < 4; ++j)
+      dma_asm(hb + kb, offH[j], dst + (uint32_t)kHOff + 1024u * (uint32_t)(4 * w + j));
   };
   uint32_t sa[kNst1];  // LDS addresses of the stages
 #pragma unroll
@@ -496,11 +495,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     }
   }
 
-  // compute the chunk in stage sc once its copies have landed (the two chunks issued after
-  // it, 8 copies of this wave, may still be in flight); meanwhile copy chunk kn of the tile
-  // (eb, oe) into sn, the stage every wave finished reading before the barrier
-  auto chunk = [&](const char* sc, uint32_t sn, int kn, const char* eb, const uint32_t (&oe)[2]) {
-    vm_wait<8>();
+  // compute the chunk in stage sc once every copy has landed; meanwhile copy chunk kn of the
+  // tile (eb, oe) into stage sn, which every wave finished reading before the barrier
+  auto chunk = [&](const char* sc, uint32_t sn, int kn, const char* eb, const uint32_t (&oe)[4]) {
+    vm_wait<0>();
     __syncthreads();
     const lds_char* s = (const lds_char*)sc;
     u32x4 fa[2][4], fb[2][2];
@@ -510,21 +508,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow1 * nb);
     issue(kn, eb, oe, sn);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) fa[1][mb] = lds_read16(s + rdE[1] + 32 * kRow1 * mb);
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cb = ks & 1;
+      if (ks < 3) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) fb[1][nb] = lds_read16(s + rdH[1] + 32 * kRow1 * nb);
+        for (int mb = 0; mb < 4; ++mb)
+          fa[cb ^ 1][mb] = lds_read16(s + rdE[ks + 1] + 32 * kRow1 * mb);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+        for (int nb = 0; nb < 2; ++nb)
+          fb[cb ^ 1][nb] = lds_read16(s + rdH[ks + 1] + 32 * kRow1 * nb);
+      }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = mfma32x32x16(fa[ks][mb], fb[ks][nb], acc[mb][nb]);
-    // order: the first step's reads, then its MFMAs interleaved with the second step's
-    // reads and this wave's four copies, then the second step's MFMAs
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[cb][mb], fb[cb][nb], acc[mb][nb]);
+    }
+    // order: the stage's first reads, then per 16-wide step its MFMAs interleaved with the
+    // next step's reads (and, in the first step, this wave's eight copies of the next chunk)
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 6; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -532,9 +535,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   const float c2 = kLog2e / g.a.temperature[c];
@@ -549,35 +561,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   uint16_t* prow1 = prow0 + 2 * nvb * 512;
 
   const char* eb;
-  uint32_t oe[2];
+  uint32_t oe[4];
   e_src(ln.lane, eb, oe);
-#pragma unroll
-  for (int q = 0; q < kNst1 - 1; ++q) issue(q, eb, oe, sa[q]);
-  // nk is a multiple of four: every tile starts on stage 0; its last three chunks copy the
-  // next tile's first three (after the last tile, this tile's again; never read)
+  issue(0, eb, oe, sa[0]);
+  // nk is even: every tile starts on stage 0, and its last chunk copies the next tile's
+  // first chunk (or, after the last tile, repeats this tile's; never read)
   for (int tt = ln.lane; tt < T; tt += ln.L) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{0};
     const char* ebn;
-    uint32_t oen[2];
+    uint32_t oen[4];
     e_src(tt + ln.L < T ? tt + ln.L : tt, ebn, oen);
-    // the previous epilogue's stores sit behind this tile's first copies in the count
-    vm_wait<0>();
-    for (int kc = 0; kc < nk - kNst1; kc += kNst1) {
-      chunk(stg[0], sa[3], kc + 3, eb, oe);
-      chunk(stg[1], sa[0], kc + 4, eb, oe);
-      chunk(stg[2], sa[1], kc + 5, eb, oe);
-      chunk(stg[3], sa[2], kc + 6, eb, oe);
+    for (int kc = 0; kc < nk - 2; kc += 2) {
+      chunk(stg[0], sa[1], kc + 1, eb, oe);
+      chunk(stg[1], sa[0], kc + 2, eb, oe);
     }
-    chunk(stg[0], sa[3], nk - 1, eb, oe);
+    chunk(stg[0], sa[1], nk - 1, eb, oe);
     chunk(stg[1], sa[0], 0, ebn, oen);
-    chunk(stg[2], sa[1], 1, ebn, oen);
-    chunk(stg[3], sa[2], 2, ebn, oen);
     eb = ebn;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) oe[j] = oen[j];
+    for (int j = 0; j < 4; ++j) oe[j] = oen[j];
     // ---- epilogue of tile tt
     const int vt0 = tt * kTile + kHalf * vh;
     int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
