@@ -52,19 +52,17 @@ __device__ __forceinline__ int uniform_token(uint32_t x, uint32_t V) {
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Gumbel noise in base-2 units, g * log2(e) = -log2(-ln u), for the 32-bit word x with
-// u = ((x >> 9) + 0.5) 2^-23.  -ln u is taken from w = 1 - u (exact in fp32) by its series
-// w + w^2/2 + w^3/3 when w < 2^-6 (truncation below w^3/4 <= 1e-6 relative), so that draws
-// near u = 1 (the large Gumbel values that decide the sample) keep full relative precision;
-// otherwise from the hardware log2 (there -ln u >= 0.0156, so an absolute error of the log
-// near 1e-7 stays below 1e-5 relative).
-__device__ __forceinline__ float gumbel2_from_word(uint32_t x) {
+// Gumbel noise in base-2 units up to a constant: for the 32-bit word x with
+// u = ((x >> 9) + 0.5) 2^-23 the Gumbel value is g = -ln(-ln u), and
+//   g log2(e) = -log2(-log2 u) - log2(ln 2);
+// this returns -log2(-log2 u), i.e. g log2(e) shifted by the constant log2(ln 2), which
+// leaves every argmax of z log2(e) + noise unchanged.  Both logarithms are the hardware
+// log2 (v_log_f32), whose result is within about 1e-7 relative for every u of this form,
+// u near 1 included (measured on gfx950 against fp64), so the large Gumbel values that
+// decide the sample keep full relative precision.
+__device__ __forceinline__ float gumbel2s_from_word(uint32_t x) {
   const float u = ((float)(x >> 9) + 0.5f) * 0x1p-23f;
-  const float w = 1.0f - u;  // exact: both are odd multiples of 2^-24 below 1
-  const float series = w * (1.0f + w * (0.5f + w * 0.33333333f));
-  const float direct = -hw_log2(u) * kLn2;
-  const float e = (w < 0.015625f) ? series : direct;
-  return -hw_log2(e);
+  return -hw_log2(-hw_log2(u));
 }
 
 // ---------------------------------------------------------------------------------------

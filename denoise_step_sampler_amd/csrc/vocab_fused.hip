@@ -504,7 +504,7 @@ __device__ __forceinline__ void piece_part(Piece& p, int q, int V, float c2, uin
     const float z2 = p.s[4 * q + j] * c2;
     const float dz = z2 - p.m;
     float pe = hw_exp2(dz);
-    const float y = z2 + gumbel2_from_word(wd[j]);
+    const float y = z2 + gumbel2s_from_word(wd[j]);
     const bool ok = !kMasked || vb + j < V;
     pe = ok ? pe : 0.0f;
     p.ls += pe;

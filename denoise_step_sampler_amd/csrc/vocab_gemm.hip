@@ -241,7 +241,7 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int vb0 = vt0 + 4 * (lane >> 5);
-  float m = -INFINITY, amv = -INFINITY;
+  float amv = -INFINITY;
   int ami = 0x7FFFFFFF;
   auto scan = [&](const f32x16& sb, int vb) {
 #pragma unroll
@@ -249,15 +249,16 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       const int v = vb + 8 * (i >> 2) + (i & 3);
       const float x = v < V ? sb[i] : -INFINITY;
       argmax_next(amv, ami, x, v);  // v increases along the scan
-      m = fmaxf(m, __fmul_rn(x, c2));
     }
   };
   scan(s0, vb0);
   scan(s1, vb0 + 32);
   scan(s2, vb0 + 64);
   scan(s3, vb0 + 96);
-  m = fmaxf(m, xor_f(m, 32));
   argmax_merge(amv, ami, xor_f(amv, 32), xor_i(ami, 32));
+  // the half tile's largest z2: rounding is monotone and c2 > 0, so max_v (S_v c2) rounded
+  // equals (max_v S_v) c2 rounded
+  const float m = __fmul_rn(amv, c2);
   const bool writer = lane < 32;
   {
     float sv = lds_st->amv;
@@ -306,7 +307,7 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       for (int j = 0; j < 4; ++j) {
         const float z2 = __fmul_rn(sb[4 * q + j], c2);
         const float dz = __fsub_rn(z2, ref);
-        const float g2 = gumbel2_from_word(wd[j]);
+        const float g2 = gumbel2s_from_word(wd[j]);
         if (kMasked) {
           const bool ok = vb + j < V;
           const float pe = ok ? hw_exp2(dz) : 0.0f;

@@ -63,7 +63,7 @@ __device__ __forceinline__ void blk_softmax_gumbel(const f32x16& s, int vb0, int
         p = hw_exp2(dz);
         ls += p;
         as += p * dz;
-        argmax_merge(gv, gi, z2 + gumbel2_from_word(wd[j]), v);
+        argmax_merge(gv, gi, z2 + gumbel2s_from_word(wd[j]), v);
       }
       pv[j] = p;
     }
