@@ -95,6 +95,18 @@ def test_ragged_vocab_and_widths(V, d, n):
     _check(wl, seed=0xDEADBEEF12345, label="ragged")
 
 
+@pytest.mark.parametrize("n", [5, 12, 33])
+def test_canvas_rounds(n):
+    """Canvas counts that split into rounds of several sizes (the logits pass runs rounds of
+    up to 32 canvases, then the binary decomposition of the rest), commit canvases mixed in."""
+    wl = synth.workload("lite", V=1500, d=128, n_canvas=n, seed=11)
+    wl.temperature = np.linspace(0.6, 1.4, n).astype(np.float32)
+    wl.step = (np.arange(n, dtype=np.int32) * 7) % 5
+    wl.commit = (np.arange(n) % 3 == 1).astype(np.uint8)
+    rows = np.sort(np.random.default_rng(n).choice(wl.R, size=min(wl.R, 160), replace=False))
+    _check(wl, seed=77, rows=rows, label=f"rounds n={n}")
+
+
 def test_uniform_and_peaked_rows(path):
     """h = 0 rows: entropy = lse = ln V, argmax 0, selfcond = mean E.  Peaked rows: argmax =
     Gumbel = target, entropy ~ 0."""
