@@ -497,49 +497,48 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   }
 
   // compute the chunk in stage sc once every copy has landed; meanwhile copy chunk kn of the
-  // tile (eb, oe) into stage sn, which every wave finished reading before the barrier
-  auto chunk = [&](const char* sc, uint32_t sn, int kn, const char* eb, const uint32_t (&oe)[4]) {
+  // tile (eb, oe) into stage sn, which every wave finished reading before the barrier.  The
+  // last 16-wide step's MFMAs of each chunk run at the start of the next one, after its
+  // first fragment reads are issued (their operands are already in registers), so the read
+  // latency behind every barrier is covered by MFMA work.
+  u32x4 fa[2][4], fb[2][2];
+  auto last_step = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[1][mb], fb[1][nb], acc[mb][nb]);
+  };
+  auto chunk = [&](auto deferred, const char* sc, uint32_t sn, int kn, const char* eb,
+                   const uint32_t (&oe)[4]) {
     vm_wait<0>();
     __syncthreads();
     const lds_char* s = (const lds_char*)sc;
-    u32x4 fa[2][4], fb[2][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) fa[0][mb] = lds_read16(s + rdE[0] + 32 * kRow1 * mb);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow1 * nb);
+    if (decltype(deferred)::value) last_step();
     issue(kn, eb, oe, sn);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 3; ++ks) {
       const int cb = ks & 1;
-      if (ks < 3) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          fa[cb ^ 1][mb] = lds_read16(s + rdE[ks + 1] + 32 * kRow1 * mb);
+      for (int mb = 0; mb < 4; ++mb)
+        fa[cb ^ 1][mb] = lds_read16(s + rdE[ks + 1] + 32 * kRow1 * mb);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          fb[cb ^ 1][nb] = lds_read16(s + rdH[ks + 1] + 32 * kRow1 * nb);
-      }
+      for (int nb = 0; nb < 2; ++nb)
+        fb[cb ^ 1][nb] = lds_read16(s + rdH[ks + 1] + 32 * kRow1 * nb);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[cb][mb], fb[cb][nb], acc[mb][nb]);
     }
-    // order: the stage's first reads, then per 16-wide step its MFMAs interleaved with the
-    // next step's reads (and, in the first step, this wave's eight copies of the next chunk)
+    // order: the first step's reads, the previous chunk's last MFMAs, then per 16-wide step
+    // its MFMAs interleaved with the next step's reads
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    if (decltype(deferred)::value) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 3; ++q) {
 #pragma unroll
       for (int i = 0; i < 6; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -547,7 +546,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   const float c2 = kLog2e / g.a.temperature[c];
@@ -575,12 +573,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     const char* ebn;
     uint32_t oen[4];
     e_src(tt + ln.L < T ? tt + ln.L : tt, ebn, oen);
-    for (int kc = 0; kc < nk - 2; kc += 2) {
-      chunk(stg[0], sa[1], kc + 1, eb, oe);
-      chunk(stg[1], sa[0], kc + 2, eb, oe);
+    // chunk j is computed from stage j % 2 and copies chunk j + 1 into the other stage
+    chunk(std::false_type{}, stg[0], sa[1], 1, eb, oe);
+    for (int kc = 1; kc < nk - 1; kc += 2) {
+      chunk(std::true_type{}, stg[1], sa[0], kc + 1, eb, oe);
+      chunk(std::true_type{}, stg[0], sa[1], kc + 2, eb, oe);
     }
-    chunk(stg[0], sa[1], nk - 1, eb, oe);
-    chunk(stg[1], sa[0], 0, ebn, oen);
+    chunk(std::true_type{}, stg[1], sa[0], 0, ebn, oen);
+    last_step();
     eb = ebn;
 #pragma unroll
     for (int j = 0; j < 4; ++j) oe[j] = oen[j];
