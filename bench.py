@@ -4,8 +4,8 @@ A step = dg_vocab_pass + dg_accept_renoise over one batch of canvases, inputs re
 HBM.  Default workload: the batched serving step (32 canvases x 256 positions, V = 262144,
 d = 2816, 8 canvases commit).  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched|large_v|lite|tiny]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload batched|large_v|lite|tiny|full_loop] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -99,6 +99,40 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
                       f"{spent:.1f}s; bf16->fp64 widening of E ({widen_s:.1f}s) excluded"}
 
 
+def full_loop(args) -> int:
+    """The full denoise loop (8 canvases, up to 32 steps, stop per canvas on convergence):
+    value = canvas-positions processed / GPU time of the steps (hidden-state synthesis and
+    its upload excluded)."""
+    import numpy as np
+    import torch
+
+    from denoise_step_sampler_amd import runner, synth
+    wl = synth.workload("full_loop", seed=args.seed)
+    E_t = runner.bf16_tensor(wl.E)
+    log("[bench] full loop: warmup")
+    runner.run_loop(wl, args.seed, max_steps=max(1, args.warmup), E=E_t)
+    torch.cuda.synchronize()
+    log("[bench] full loop: timed run")
+    res = runner.run_loop(wl, args.seed, max_steps=32, E=E_t)
+    ms = float(np.mean(res.step_ms))
+    flops = 4.0 * res.positions * wl.V * wl.d   # logits + expectation, no commit canvases
+    out = {
+        "metric": "canvas-positions/sec per denoise step",
+        "value": res.positions_per_s, "unit": "canvas-positions/s",
+        "n_gpus": 1, "steps": res.steps_run, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full_loop", "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
+                   "d": wl.d, "max_steps": 32, "temperature": float(wl.temperature[0]),
+                   "entropy_budget": wl.budget, "confidence": wl.confidence,
+                   "stability": wl.stability},
+        "pct_bf16_mfma_peak": 100.0 * flops / (sum(res.step_ms) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "steps_to_converge": res.steps_to_converge.tolist(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +161,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.copy_probe:
         return copy_probe(args.copy_probe, 5)
+    if args.workload == "full_loop":
+        return full_loop(args)
     log(f"[bench] building inputs for workload {args.workload}")
     wl = synth.workload(args.workload, seed=args.seed)
     b = runner.from_workload(wl)

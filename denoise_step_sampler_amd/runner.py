@@ -106,3 +106,72 @@ def denoise_step(b: VocabBuffers, budget: float, confidence: float, stability: i
     """One step of the hot path: vocabulary pass, then accept/renoise/convergence."""
     vocab_pass(b, seed, stream)
     accept_renoise(b, budget, confidence, stability, seed, stream)
+
+
+@dataclass
+class LoopResult:
+    steps_run: int
+    steps_to_converge: np.ndarray   # [n_canvas] step after which the canvas converged, -1 if never
+    positions: int                  # sum over steps of active canvases x C
+    step_ms: list                   # GPU time of each step (vocabulary pass + accept/renoise)
+
+    @property
+    def positions_per_s(self) -> float:
+        return self.positions / (sum(self.step_ms) * 1e-3)
+
+
+def run_loop(wl, seed: int, max_steps: int = 32, stream=None, on_step=None,
+             E: Optional[torch.Tensor] = None) -> LoopResult:
+    """The full denoise loop of the full_loop workload: at step k the hidden states come from
+    synth.loop_hidden (signal 0.5 + 0.25 k, kept only at the positions accepted at step
+    k - 1), then one vocabulary pass and accept/renoise run on the canvases that have not
+    converged; a canvas leaves the batch once converged, and the loop ends when none is left
+    or after max_steps.  Hidden-state synthesis and its upload are outside the timed region.
+
+    on_step(k, b, canvases, state_in) is called after each step with the buffers, the
+    original canvas ids in the batch and the host copies of the sampler state the step
+    started from (prev_argmax, stable_count)."""
+    from . import synth
+    stream = stream if stream is not None else torch.cuda.current_stream()
+    n, C = wl.n_canvas, B.DG_CANVAS
+    E_t = bf16_tensor(wl.E) if E is None else E
+    active = np.arange(n)
+    prev = np.full(n * C, -1, np.int32)        # sampler state of every canvas (host copy)
+    cnt = np.zeros(n, np.int32)
+    accepted_prev = None
+    steps_to_converge = np.full(n, -1, np.int64)
+    positions, step_ms, b = 0, [], None
+    for k in range(max_steps):
+        if active.size == 0:
+            break
+        h_all = synth.loop_hidden(wl, k, accepted_prev)
+        rows = (active[:, None] * C + np.arange(C)[None, :]).reshape(-1)
+        if b is None or b.n_canvas != active.size:
+            b = allocate(active.size, wl.V, wl.d, E_t, bf16_tensor(h_all[rows]),
+                         wl.temperature[active], None, np.full(active.size, k, np.int32))
+            b.prev_argmax.copy_(torch.from_numpy(prev[rows]))
+            b.stable_count.copy_(torch.from_numpy(cnt[active]))
+        else:
+            b.h.copy_(bf16_tensor(h_all[rows]))
+            b.step.fill_(k)
+        state_in = (b.prev_argmax.cpu().numpy(), b.stable_count.cpu().numpy())
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        denoise_step(b, wl.budget, wl.confidence, wl.stability, seed, stream)
+        t1.record(stream)
+        t1.synchronize()
+        step_ms.append(t0.elapsed_time(t1))
+        positions += active.size * C
+        if on_step is not None:
+            on_step(k, b, active.copy(), state_in)
+        acc = b.accept_mask.cpu().numpy().astype(bool)
+        conv = b.converged.cpu().numpy().astype(bool)
+        accepted_prev = np.zeros(n * C, bool) if accepted_prev is None else accepted_prev.copy()
+        accepted_prev[rows] = acc
+        prev[rows] = b.prev_argmax.cpu().numpy()
+        cnt[active] = b.stable_count.cpu().numpy()
+        steps_to_converge[active[conv]] = k
+        active = active[~conv]
+    return LoopResult(steps_run=len(step_ms), steps_to_converge=steps_to_converge,
+                      positions=positions, step_ms=step_ms)
