@@ -87,12 +87,12 @@ __device__ __forceinline__ void vm_wait() {
 // ---------------------------------------------------------------------------------------
 // Schedule of the logits pass.  Canvases are taken in `order` (non-commit first) in rounds
 // of g = a power of two <= kRoundMax; a round gives each canvas L = 256 / g vocabulary
-// lanes, and lane l of a canvas processes tiles l, l + L, l + 2L, ...  The canvases of an
-// XCD read the same E tiles at about the same time, so each E line is fetched into its L2
-// once for all of them.  Workgroup b runs on XCD b % 8
-// (the dispatcher deals workgroups to the XCDs round-robin), slot b / 8:
-//   g >= 8: canvas k = 8 (slot % (g/8)) + xcd, lane = slot / (g/8)   (g/8 canvases per XCD)
-//   g <  8: canvas k = xcd % g,                lane = 32 (xcd / g) + slot
+// lanes, and lane l of a canvas processes tiles l, l + L, l + 2L, ...  Workgroup b runs on
+// XCD b % 8 (the dispatcher deals workgroups to the XCDs round-robin), slot b / 8.  Each
+// XCD holds c = min(g, 8) canvases with 32 / c lanes each, all walking the same tiles, so an
+// E tile crosses into the XCD's L2 once for c canvases and each canvas's h chunk once for
+// its 32 / c lanes; the XCDs of one canvas group split the vocabulary, so E is fetched from
+// beyond L2 once per group (g / c times in all).
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int round_size(int remaining, int gmax) {
   int g = gmax;
@@ -107,17 +107,15 @@ struct Lane {
 };
 
 __device__ __forceinline__ Lane lane_of(int b, int g) {
+  // c = min(g, 8) canvases share each XCD; the g / c groups of canvases each take 8 c / g
+  // XCDs, which split the vocabulary among them (XCD xi of a group: tiles = xi mod X).
   const int x = b & 7, s = b >> 3;
+  const int c = g < 8 ? g : 8;
+  const int G = g / c, X = 8 / G;
   Lane r;
   r.L = kWG / g;
-  if (g >= 8) {
-    const int per = g / 8;
-    r.k = 8 * (s % per) + x;
-    r.lane = s / per;
-  } else {
-    r.k = x % g;
-    r.lane = 32 * (x / g) + s;
-  }
+  r.k = (x % G) * c + s % c;
+  r.lane = x / G + X * (s / c);
   return r;
 }
 
