@@ -195,10 +195,10 @@ struct GemmK {
                       // [row / 16][v / 32], entry (row, v) at 8 (row % 16 + 16 ((v % 32) / 8))
                       // + v % 8 of its block; row = 256 pos + i
   int* ref;           // [n_half][R] integer references (base-2 units), row = 256 pos + i
-  float* st_m;        // [2 * kLanesMax][R] statistic partials (slot = 2 lane + half)
+  float* st_m;        // [R][2 * kLanesMax] statistic partials (slot = 2 lane + half)
   float* st_l;
   float* st_lb;
-  float* st_tm;       // [4][2 * kLanesMax][R] top-4 half-tile maxima (z2) and their entries
+  float* st_tm;       // [4][R][2 * kLanesMax] top-4 half-tile maxima (z2) and their entries
   int* st_tv;
   float* st_a;
   float* st_amv;
@@ -602,11 +602,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   // statistic partials of this (canvas, lane, half)
   if (lane < 32) {
     const int slot = 2 * ln.lane + vh;
-    const size_t o0 = (size_t)slot * R + (size_t)c * kTile + rloc0;
+    const size_t o0 = ((size_t)c * kTile + rloc0) * (2 * kLanesMax) + slot;
     const size_t plane = (size_t)2 * kLanesMax * R;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const size_t o = o0 + 32 * nb;
+      const size_t o = o0 + (size_t)32 * nb * (2 * kLanesMax);
       const LdsRowAcc* st = nb ? st1p : st0p;
       g.st_amv[o] = st->amv;
       g.st_ami[o] = st->ami;
@@ -949,14 +949,41 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
   int ami = 0x7FFFFFFF, gi = 0x7FFFFFFF;
   float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   int tv[4] = {0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
-  for (int s = lane; s < n_slot; s += 64) {
-    const size_t o = (size_t)s * R + r;
-    argmax_merge(amv, ami, g.st_amv[o], g.st_ami[o]);
-    if (heavy) {
-      lse_merge_b(m, l, a, lb, g.st_m[o], g.st_l[o], g.st_a[o], g.st_lb[o]);
-      argmax_merge(gv, gi, g.st_gv[o], g.st_gi[o]);
+  // up to four slots per lane at a time, their loads issued together (a single canvas has
+  // 512 slots a row)
+  for (int s0 = lane; s0 < n_slot; s0 += 256) {
+    float vm[4], vl[4], va[4], vlb[4], vamv[4], vgv[4], vtm[4][4];
+    int vami[4], vgi[4], vtv[4][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) top4_insert(tm, tv, g.st_tm[k * plane + o], g.st_tv[k * plane + o]);
+    for (int u = 0; u < 4; ++u) {
+      const int s = min(s0 + 64 * u, n_slot - 1);
+      const size_t o = (size_t)r * (2 * kLanesMax) + s;  // the slots of a row are contiguous
+      vamv[u] = g.st_amv[o];
+      vami[u] = g.st_ami[o];
+      if (heavy) {
+        vm[u] = g.st_m[o];
+        vl[u] = g.st_l[o];
+        va[u] = g.st_a[o];
+        vlb[u] = g.st_lb[o];
+        vgv[u] = g.st_gv[o];
+        vgi[u] = g.st_gi[o];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          vtm[u][k] = g.st_tm[k * plane + o];
+          vtv[u][k] = g.st_tv[k * plane + o];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + 64 * u >= n_slot) break;
+      argmax_merge(amv, ami, vamv[u], vami[u]);
+      if (heavy) {
+        lse_merge_b(m, l, a, lb, vm[u], vl[u], va[u], vlb[u]);
+        argmax_merge(gv, gi, vgv[u], vgi[u]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) top4_insert(tm, tv, vtm[u][k], vtv[u][k]);
+      }
     }
   }
 #pragma unroll
