@@ -454,16 +454,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
       oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
     }
   };
-  // copies of chunk kc of a tile whose E source is (eb, oe) into the stage at LDS address
-  // dst (inline-assembly DMA: the compiler would otherwise wait for every copy in flight
-  // before the next read of LDS, the stages it cannot tell apart)
-  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[4], uint32_t dst) {
+  // copies of chunk kc into the stage at LDS address dst: the E rows of a tile whose source
+  // is (eb, oe), and the canvas's h rows (inline-assembly DMA: the compiler would otherwise
+  // wait for every copy in flight before the next read of LDS, the stages it cannot tell
+  // apart)
+  auto issue_e = [&](int kc, const char* eb, const uint32_t (&oe)[4], uint32_t dst) {
     const uint32_t kb = (uint32_t)kc * (uint32_t)kRow1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(4 * w + j));
+  };
+  auto issue_h = [&](int kc, uint32_t dst) {
+    const uint32_t kb = (uint32_t)kc * (uint32_t)kRow1;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       dma_asm(hb + kb, offH[j], dst + (uint32_t)kHOff + 1024u * (uint32_t)(4 * w + j));
+  };
+  auto issue = [&](int kc, const char* eb, const uint32_t (&oe)[4], uint32_t dst) {
+    issue_e(kc, eb, oe, dst);
+    issue_h(kc, dst);
   };
   uint32_t sa[kNst1];  // LDS addresses of the stages
 #pragma unroll
@@ -516,10 +524,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow1 * nb);
     if (decltype(deferred)::value) last_step();
-    issue(kn, eb, oe, sn);
+    // the E copies first (they may miss in L2), the h copies (L2-resident) a step later
+    issue_e(kn, eb, oe, sn);
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int cb = ks & 1;
+      if (ks == 1) issue_h(kn, sn);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
         fa[cb ^ 1][mb] = lds_read16(s + rdE[ks + 1] + 32 * kRow1 * mb);
