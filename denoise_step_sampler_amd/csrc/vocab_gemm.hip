@@ -808,12 +808,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   for (int q = 0; q < kNst2; ++q) sa[q] = (uint32_t)(uintptr_t)(lds_char*)stg[q];
 
   // copies of chunk kc (clamped to the unit's last chunk: the copies issued past the end go
-  // to a stage nobody reads again)
-  auto issue = [&](int kc, uint32_t dst) {
+  // to a stage nobody reads again): the weights, and the E rows
+  auto issue_p = [&](int kc, uint32_t dst) {
     kc = min(kc, nkc - 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       dma_asm(pbase + ((size_t)j * nvb + kc) * 1024, offP, dst + 1024u * (uint32_t)(2 * w + j));
+  };
+  auto issue_e = [&](int kc, uint32_t dst) {
+    kc = min(kc, nkc - 1);
     // E rows past V - 1 (tail of the last tile, zero weights) read row V - 1
     const int vb = min(v00 + kc * kKC2, V - 1);
     const int lim = V - 1 - vb;
@@ -842,7 +845,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   auto chunk = [&](const char* sc, uint32_t sn, int kn, uint32_t shw) {
     vm_wait<2 * kCpw>();
     __syncthreads();
-    issue(kn, sn);
+    // the E copies at once (E may miss in L2), the weight copies halfway through the chunk
+    issue_e(kn, sn);
     uint32_t sh7[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) sh7[rb] = ((shw >> (8 * rb)) & 0xFFu) << 7;
@@ -859,6 +863,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
       fa[rb] = shift_down(lds_read16(sp + (4 * rw + rb) * 1024 + 16 * lane), sh7[rb]);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
+      if (cb == NCB / 2) issue_p(kn, sn);
       const u32x4 fb = e_frag(se, kPitchE, 0, ea ^ (32 * cb));
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
@@ -866,7 +871,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   };
 
 #pragma unroll
-  for (int q = 0; q < kNst2 - 1; ++q) issue(q, sa[q]);
+  for (int q = 0; q < kNst2 - 1; ++q) {
+    issue_e(q, sa[q]);
+    issue_p(q, sa[q]);
+  }
   const lds_char* shp = (const lds_char*)shb + 64 * rw + 4 * ar;
   for (int kc = 0; kc < nkc; kc += kNst2) {
     const uint32_t shw = lds_u32(shp + (kc >> 2) * kTile);  // half tile kc / 4
