@@ -8,6 +8,13 @@ Definitions followed (cited by page and section):
   sec. 3.2 eq. (5)).
 * tempered distribution  p = Softmax(S / T)  (Technical Report sec. 3.2 eq. (6);
   DiffusionGemma Explained, "Sampling" -> "Apply temperature").
+* optional final-logit soft cap: S is replaced by c tanh(S / c) before the temperature
+  (DiffusionGemma Explained, "Logit Softcapping" and the model's final-logits return); the
+  argmax token stays that of S (tanh is increasing, so the capped logits have the same
+  largest value at the same entries up to rounding; the plain reading keeps S's argmax).
+* temperature schedule: decode pass i of N uses t_i = t_max + (i / N)(t_min - t_max)
+  (DiffusionGemma Explained, "Sampling" -> "Apply temperature"; Technical Report sec. 3.3
+  anneals from 0.8 to 0.4).
 * lse = log sum_v exp(S_v / T); entropy H = -sum_v p_v log p_v = sum_v p_v (lse - z_v)
   (DiffusionGemma Explained, "Sampling" -> "Compute entropy").
 * argmax token: the smallest v attaining max S (deterministic prediction used by the
@@ -28,6 +35,7 @@ Decision margins (reported, used by the parity tests to exempt near-ties):
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -66,13 +74,16 @@ def _top2_margin(x: np.ndarray) -> float:
 def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
                     temperature_row: np.ndarray, commit_row: np.ndarray,
                     seed: int, step_row: np.ndarray, want_sc: bool = True,
-                    row_block: int = 64) -> RowResult:
+                    row_block: int = 64, softcap: Optional[float] = None) -> RowResult:
     """Oracle results for the listed global rows.
 
     E64            fp64 [V, d] (the widened bf16 embedding)
     h_bits         bf16 bits [R, d] of the whole batch (only ``rows`` are read)
     temperature_row, commit_row, step_row: per global row (indexable by row id)
+    softcap        None: z = S / T; c > 0: z = c tanh(S / c) / T
     """
+    if softcap is not None and not (softcap > 0 and math.isfinite(softcap)):
+        raise ValueError("softcap must be finite and > 0")
     rows = np.asarray(rows, dtype=np.int64)
     V, d = E64.shape
     n = rows.shape[0]
@@ -96,7 +107,7 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
             if commit_row[r]:
                 continue
             T = float(temperature_row[r])
-            z = s / T
+            z = (s if softcap is None else softcap * np.tanh(s / softcap)) / T
             m = z.max()
             lse[i] = m + np.log(np.sum(np.exp(z - m)))
             p = np.exp(z - lse[i])
@@ -109,6 +120,13 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
                 sc[i] = p @ E64
     return RowResult(rows=rows, lse=lse, entropy=ent, argmax=amax, gumbel=gtok, sc=sc,
                      mu_argmax=mu_a, mu_gumbel=mu_g)
+
+
+def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:
+    """Temperature of decode pass i of N (i = 0 .. N - 1): linear from t_max toward t_min."""
+    if not (N >= 1 and 0 <= i < N):
+        raise ValueError("need 0 <= i < N")
+    return t_max + (i / N) * (t_min - t_max)
 
 
 def per_row(values_per_canvas: np.ndarray, C: int) -> np.ndarray:

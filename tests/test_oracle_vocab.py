@@ -195,3 +195,97 @@ def test_argmax_tie_lowest_index():
     h = np.array([[2.0, 0.0]], dtype=np.float32)
     r = _run(synth.round_to_bf16(E), synth.round_to_bf16(h))
     assert r.argmax[0] == 3 and r.mu_argmax[0] == 0.0
+
+
+# --- final-logit soft cap and temperature schedule ---------------------------------------
+
+def _run_cap(E_bits, h_bits, c, T=1.0, seed=0, step=0, want_sc=True):
+    R = h_bits.shape[0]
+    return vp.vocab_pass_rows(vp.widen_bf16(E_bits), h_bits, np.arange(R), np.full(R, T),
+                              np.zeros(R, bool), seed, np.full(R, step), want_sc=want_sc,
+                              softcap=c)
+
+
+def test_softcap_large_cap_is_no_cap():
+    """c tanh(S / c) -> S as c grows: a cap far above every logit leaves all outputs."""
+    wl = synth.workload("tiny", V=700, d=64)
+    h = wl.h[:6]
+    a = _run(wl.E, h, T=0.8, seed=3, step=2)
+    b = _run_cap(wl.E, h, 1e7, T=0.8, seed=3, step=2)
+    assert np.allclose(a.lse, b.lse, atol=1e-9, rtol=0)
+    assert np.allclose(a.entropy, b.entropy, atol=1e-9, rtol=0)
+    assert np.allclose(a.sc, b.sc, atol=1e-9, rtol=0)
+    assert np.array_equal(a.argmax, b.argmax) and np.array_equal(a.gumbel, b.gumbel)
+
+
+@pytest.mark.parametrize("V,k,a,b,c,T", [(64, 3, 2.0, -1.0, 1.5, 1.0),
+                                         (5000, 17, 6.5, 0.25, 4.0, 0.8),
+                                         (300, 299, -3.0, 4.0, 30.0, 0.4)])
+def test_softcap_two_level_closed_form(V, k, a, b, c, T):
+    """Two logit levels, capped then tempered: z = c tanh(level / c) / T (tanh from mpmath)."""
+    Eb, hb = _two_level(V, k, a, b)
+    r = _run_cap(Eb, hb, c, T=T)
+    za = float(c * mpmath.tanh(mpmath.mpf(a) / c) / T)
+    zb = float(c * mpmath.tanh(mpmath.mpf(b) / c) / T)
+    Z = k * math.exp(za) + (V - k) * math.exp(zb)
+    pa, pb = math.exp(za) / Z, math.exp(zb) / Z
+    H = -(k * pa * math.log(pa) + (V - k) * pb * math.log(pb))
+    assert abs(r.lse[0] - math.log(Z)) < 1e-12 * max(1, abs(math.log(Z)))
+    assert abs(r.entropy[0] - H) < 1e-12
+    assert np.allclose(r.sc[0], [k * pa, (V - k) * pb], atol=1e-14)
+    assert r.argmax[0] == (0 if a >= b else k)
+
+
+def test_softcap_saturation_limit():
+    """Logits far beyond the cap saturate at +-c: the distribution becomes two-level, c / T on
+    the n+ tokens with S > 0 and -c / T on the rest, whatever S's magnitudes."""
+    V, c, T = 4000, 2.0, 0.7
+    rng = np.random.default_rng(11)
+    E = np.stack([rng.choice([-1.0, 1.0], V), rng.standard_normal(V)], axis=1)
+    E = synth.round_to_bf16(E.astype(np.float32))
+    h = synth.round_to_bf16(np.array([[4096.0, 1.0], [-2048.0, 3.0], [1024.0, -7.0]],
+                                     np.float32))
+    r = _run_cap(E, h, c, T=T)
+    S = vp.widen_bf16(h) @ vp.widen_bf16(E).T
+    assert np.abs(S).min() > 200 * c  # tanh(200) == 1 in fp64
+    for i in range(3):
+        npos = int(np.sum(S[i] > 0))
+        Z = npos * math.exp(c / T) + (V - npos) * math.exp(-c / T)
+        assert abs(r.lse[i] - math.log(Z)) < 1e-12 * abs(math.log(Z))
+        assert r.argmax[i] == int(np.argmax(S[i]))
+
+
+def test_softcap_bounds_lse_and_entropy():
+    """|z| <= c / T: ln V - c / T <= lse <= ln V + c / T, and H <= ln V; the argmax token is
+    S's argmax whatever the cap."""
+    wl = synth.workload("tiny", V=900, d=64)
+    h = synth.round_to_bf16(synth.bf16_to_f32(wl.h[:8]) * 50.0)
+    for c in (0.5, 3.0, 20.0):
+        r = _run_cap(wl.E, h, c, T=0.6)
+        lnV = math.log(900)
+        assert np.all(r.lse <= lnV + c / 0.6 + 1e-12)
+        assert np.all(r.lse >= lnV - c / 0.6 - 1e-12)
+        assert np.all(r.entropy <= lnV + 1e-12)
+        S = vp.widen_bf16(h) @ vp.widen_bf16(wl.E).T
+        assert np.array_equal(r.argmax, np.argmax(S, axis=1))
+
+
+def test_softcap_rejects_bad_values():
+    wl = synth.workload("tiny", V=64, d=16)
+    for c in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(ValueError):
+            _run_cap(wl.E, wl.h[:1], c)
+
+
+def test_temperature_schedule_endpoints():
+    """t_0 = t_max, linear steps of (t_min - t_max) / N, never reaching t_min; the default
+    anneal of the technical report runs from 0.8 toward 0.4."""
+    N = 32
+    ts = [vp.temperature_schedule(i, N, 0.8, 0.4) for i in range(N)]
+    assert ts[0] == 0.8
+    assert abs(ts[16] - 0.6) < 1e-15
+    assert abs(ts[-1] - (0.4 + 0.4 / N)) < 1e-15
+    assert all(b < a for a, b in zip(ts, ts[1:]))
+    assert np.allclose(np.diff(ts), -0.4 / N, atol=1e-15)
+    with pytest.raises(ValueError):
+        vp.temperature_schedule(N, N, 0.8, 0.4)
