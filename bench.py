@@ -109,11 +109,13 @@ def full_loop(args) -> int:
     from denoise_step_sampler_amd import runner, synth
     wl = synth.workload("full_loop", seed=args.seed)
     E_t = runner.bf16_tensor(wl.E)
+    sched = None if args.anneal is None else tuple(float(x) for x in args.anneal.split(","))
     log("[bench] full loop: warmup")
-    runner.run_loop(wl, args.seed, max_steps=max(1, args.warmup), E=E_t)
+    runner.run_loop(wl, args.seed, max_steps=max(1, args.warmup), E=E_t, softcap=args.softcap)
     torch.cuda.synchronize()
     log("[bench] full loop: timed run")
-    res = runner.run_loop(wl, args.seed, max_steps=32, E=E_t)
+    res = runner.run_loop(wl, args.seed, max_steps=32, E=E_t, schedule=sched,
+                          softcap=args.softcap)
     ms = float(np.mean(res.step_ms))
     flops = 4.0 * res.positions * wl.V * wl.d   # logits + expectation, no commit canvases
     out = {
@@ -123,7 +125,10 @@ def full_loop(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "full_loop", "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
-                   "d": wl.d, "max_steps": 32, "temperature": float(wl.temperature[0]),
+                   "d": wl.d, "max_steps": 32,
+                   "temperature": (float(wl.temperature[0]) if sched is None else
+                                   {"anneal_from": sched[0], "anneal_to": sched[1]}),
+                   "softcap": args.softcap,
                    "entropy_budget": wl.budget, "confidence": wl.confidence,
                    "stability": wl.stability},
         "pct_bf16_mfma_peak": 100.0 * flops / (sum(res.step_ms) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
@@ -144,6 +149,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
+    ap.add_argument("--softcap", type=float, default=None,
+                    help="final-logit soft cap c (logits c tanh(S / c)); default: none")
+    ap.add_argument("--anneal", default=None, metavar="TMAX,TMIN",
+                    help="full_loop only: linear temperature schedule over the 32 steps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -171,7 +180,7 @@ def main() -> int:
 
     def step(k):
         b.step.fill_(k)
-        runner.vocab_pass(b, seed, stream)
+        runner.vocab_pass(b, seed, stream, args.softcap)
         runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, stream)
 
     log(f"[bench] warmup {args.warmup}")
@@ -190,7 +199,7 @@ def main() -> int:
     for k in range(args.steps):
         b.step.fill_(args.warmup + k)
         ev[k][0].record(stream)
-        runner.vocab_pass(b, seed, stream)
+        runner.vocab_pass(b, seed, stream, args.softcap)
         ev[k][1].record(stream)
         runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, stream)
     t_end.record(stream)
@@ -211,9 +220,12 @@ def main() -> int:
            for _ in range(args.steps)]
     for k in range(args.steps):
         ev2[k][0].record(stream)
-        B.dg_vocab_pass(b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed,
-                        b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, None, b.workspace,
-                        stream=stream)
+        k1_args = (b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step,
+                   b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, None, b.workspace)
+        if args.softcap is None:
+            B.dg_vocab_pass(*k1_args, stream=stream)
+        else:
+            B.dg_vocab_pass_softcap(*k1_args, stream=stream, softcap=args.softcap)
         ev2[k][1].record(stream)
     torch.cuda.synchronize()
     k1_ms = float(np.mean([a.elapsed_time(z) for a, z in ev2]))
@@ -222,7 +234,8 @@ def main() -> int:
     flops = algorithmic_flops(wl)
     flops_k1 = 2.0 * wl.R * wl.V * wl.d
     ach_k1 = flops_k1 / (k1_ms * 1e-3) / 1e12
-    gemm_path = wl.d % 128 == 0 and os.environ.get("DG_VOCAB_PATH") is None
+    gemm_path = wl.d % 128 == 0 and (os.environ.get("DG_VOCAB_PATH") is None
+                                     or args.softcap is not None)
     positions = wl.R
     res = {
         "metric": "canvas-positions/sec per denoise step",
@@ -234,7 +247,8 @@ def main() -> int:
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
                    "d": wl.d, "commit_canvases": int(wl.commit.sum()),
-                   "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget},
+                   "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget,
+                   "softcap": args.softcap},
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "vocab_pass": {"avg_launch_ms": vp_avg, "algorithmic_flops": flops,
@@ -243,7 +257,9 @@ def main() -> int:
             "kernel": "k_gemm_logits" if gemm_path else "dg_vocab_pass (non-default path)",
             "bound": "mfma", "achieved": ach_k1, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": ach_k1 / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(args.workload) if gemm_path else None,
+            # the counters were taken on the uncapped kernel
+            "traffic": (measured_traffic(args.workload)
+                        if gemm_path and args.softcap is None else None),
             "algorithmic_flops_per_launch": flops_k1, "avg_launch_ms": k1_ms},
     }
     if not args.no_cpu_baseline:

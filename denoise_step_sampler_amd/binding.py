@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libdg.so")
 DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = range(5)
 DG_CANVAS = 256
 
-EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_accept_renoise", "dg_q_sample",
-            "dg_status_string", "dg_last_error")
+EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_vocab_pass_softcap",
+            "dg_accept_renoise", "dg_q_sample", "dg_status_string", "dg_last_error")
 
 
 class DGError(RuntimeError):
@@ -46,6 +46,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_vocab_pass_workspace_size.restype = SZ
     lib.dg_vocab_pass.argtypes = [P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P]
     lib.dg_vocab_pass.restype = I
+    lib.dg_vocab_pass_softcap.argtypes = [P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P,
+                                          F]
+    lib.dg_vocab_pass_softcap.restype = I
     lib.dg_accept_renoise.argtypes = [P, P, P, P, I, I, I, F, F, I, U64, P, P, P, P, P, P, P, P]
     lib.dg_accept_renoise.restype = I
     lib.dg_q_sample.argtypes = [P, I, I, I, P, U64, P, P]
@@ -99,11 +102,30 @@ def dg_vocab_pass(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: int, V: in
                   argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
                   selfcond: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
     """E, h: bf16 bit patterns as torch.int16/uint16 or torch.bfloat16."""
+    _vocab_pass(None, E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                argmax_tok, gumbel_tok, selfcond, workspace, stream)
+
+
+def dg_vocab_pass_softcap(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: int, V: int,
+                          d: int, temperature: torch.Tensor, commit: Optional[torch.Tensor],
+                          seed: int, step: torch.Tensor, lse: Optional[torch.Tensor],
+                          entropy: torch.Tensor, argmax_tok: torch.Tensor,
+                          gumbel_tok: torch.Tensor, selfcond: Optional[torch.Tensor],
+                          workspace: torch.Tensor, stream=None, softcap: float = 30.0) -> None:
+    """dg_vocab_pass on the soft-capped logits softcap * tanh(S / softcap)."""
+    _vocab_pass(float(softcap), E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse,
+                entropy, argmax_tok, gumbel_tok, selfcond, workspace, stream)
+
+
+def _vocab_pass(softcap, E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                argmax_tok, gumbel_tok, selfcond, workspace, stream) -> None:
     R = n_canvas * C
     lib = load()
     eb = _bf16_ptr(E, V * d, "E")
     hb = _bf16_ptr(h, R * d, "h")
-    st = lib.dg_vocab_pass(
+    fn = lib.dg_vocab_pass if softcap is None else lib.dg_vocab_pass_softcap
+    extra = () if softcap is None else (ctypes.c_float(softcap),)
+    st = fn(
         eb, hb, n_canvas, C, V, d,
         _ptr(temperature, torch.float32, n_canvas, "temperature"),
         _ptr(commit, torch.uint8, n_canvas, "commit"),
@@ -115,7 +137,7 @@ def dg_vocab_pass(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: int, V: in
         _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
         _ptr(selfcond, torch.float32, R * d, "selfcond"),
         _ptr(workspace, torch.uint8, None, "workspace"),
-        workspace.numel(), _stream(stream))
+        workspace.numel(), _stream(stream), *extra)
     _check(st)
 
 

@@ -104,24 +104,37 @@ size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d) {
   const dg_status s = check_vocab_shape(n_canvas, C, V, d);
   memcpy(g_err, keep, sizeof(g_err));
   if (s != DG_OK) return 0;
-  return plan_bytes(n_canvas, V, d);
+  // The soft-capped pass always runs on the two-GEMM path: size for whichever is larger.
+  size_t n = plan_bytes(n_canvas, V, d);
+  if (dg::gemm_supported(d)) {
+    const size_t g = dg::gemm_plan(n_canvas, V, d).bytes;
+    if (g > n) n = g;
+  }
+  return n;
 }
 
-dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
-                        const float* temperature, const uint8_t* commit, uint64_t seed,
-                        const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
-                        int32_t* gumbel_tok, float* selfcond, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
+                     const float* temperature, const uint8_t* commit, uint64_t seed,
+                     const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
+                     int32_t* gumbel_tok, float* selfcond, void* workspace,
+                     size_t workspace_bytes, void* stream, float softcap) {
   g_err[0] = 0;
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
     return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (softcap != 0.0f && !dg::gemm_supported(d))
+    return fail(DG_ERR_UNSUPPORTED, "the soft cap needs d %% 128 == 0 (d=%d)", d);
   if (!aligned16(E) || !aligned16(h))
     return fail(DG_ERR_INVALID_ARG, "E and h must be 16-byte aligned");
   if (selfcond && !aligned16(selfcond))
     return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
-  const size_t need = plan_bytes(n_canvas, V, d);
+  const size_t need =
+      softcap != 0.0f ? dg::gemm_plan(n_canvas, V, d).bytes : plan_bytes(n_canvas, V, d);
   if (!workspace || workspace_bytes < need)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -142,9 +155,10 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
   a.argmax_tok = argmax_tok;
   a.gumbel_tok = gumbel_tok;
   a.selfcond = selfcond;
+  a.softcap = softcap;
   int n_wg = 0;
   hipError_t e;
-  switch (pick_path(d, &n_wg)) {
+  switch (softcap != 0.0f ? kGemm : pick_path(d, &n_wg)) {
     case kGemm:
       e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, (hipStream_t)stream);
       break;
@@ -159,6 +173,32 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
   }
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
+                        const float* temperature, const uint8_t* commit, uint64_t seed,
+                        const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
+                        int32_t* gumbel_tok, float* selfcond, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, 0.0f);
+}
+
+dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
+                                int d, const float* temperature, const uint8_t* commit,
+                                uint64_t seed, const int32_t* step, float* lse, float* entropy,
+                                int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                float softcap) {
+  g_err[0] = 0;
+  if (!(softcap > 0.0f) || !isfinite(softcap))
+    return fail(DG_ERR_INVALID_ARG, "softcap must be finite and > 0");
+  return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

@@ -24,6 +24,7 @@ struct VocabArgs {
   int32_t* argmax_tok;
   int32_t* gumbel_tok;
   float* selfcond;
+  float softcap;  // > 0: z = softcap tanh(S / softcap) / T (two-GEMM path only); 0: z = S / T
 };
 
 // Workspace carve-up.

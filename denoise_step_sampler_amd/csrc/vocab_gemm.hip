@@ -229,11 +229,26 @@ struct GemmK {
 // registers are left to the logits and the noise.
 typedef __attribute__((address_space(3))) RowAcc LdsRowAcc;
 
-template <bool kHeavy>
+// Final-logit soft cap (DiffusionGemma Explained, "Logit Softcapping"): z2 = c tanh(S / c) c2
+// with c2 = log2(e) / T, evaluated as tanh(S inv_c) cz, cz = c c2 (one rounding of c c2 per
+// canvas).  tanhf is the device library's (relative error of a few ulp at every |S / c|,
+// saturating to +-1), so the capped logit keeps the accuracy of S near 0.
+struct SoftCap {
+  float inv_c, cz;
+};
+
+__device__ __forceinline__ float soft_cap_z2(float s, const SoftCap& sc) {
+#pragma clang fp contract(off)
+  return __fmul_rn(tanhf(__fmul_rn(s, sc.inv_c)), sc.cz);
+}
+
+// kCap: z2 = soft_cap_z2(S) in place of S c2; the argmax stays on S.
+template <bool kHeavy, bool kCap>
 __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, const f32x16& s2,
                                         const f32x16& s3, int vt0, int V, float c2,
-                                        uint32_t row, uint32_t step, uint32_t k0, uint32_t k1,
-                                        uint16_t* pt, int* ref_out, LdsRowAcc* lds_st) {
+                                        const SoftCap& cap, uint32_t row, uint32_t step,
+                                        uint32_t k0, uint32_t k1, uint16_t* pt, int* ref_out,
+                                        LdsRowAcc* lds_st) {
   // HIP contracts a * b - c into one fma by default, which would round dz once instead of
   // twice and break the bit-for-bit recomputation in the combine
 #pragma clang fp contract(off)
@@ -255,8 +270,11 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
   scan(s3, vb0 + 96);
   argmax_merge(amv, ami, xor_f(amv, 32), xor_i(ami, 32));
   // the half tile's largest z2: rounding is monotone and c2 > 0, so max_v (S_v c2) rounded
-  // equals (max_v S_v) c2 rounded
-  const float m = __fmul_rn(amv, c2);
+  // equals (max_v S_v) c2 rounded.  With the cap: the z2 of S's argmax, which the block loop
+  // recomputes bit for bit; tanh is increasing, so another entry can exceed it only by the
+  // rounding of tanhf, which leaves its 2^(z2 - ref) within an ulp of 1 (bf16 1.0)
+  const float m = !kCap ? __fmul_rn(amv, c2)
+                        : (amv == -INFINITY ? -INFINITY : soft_cap_z2(amv, cap));
   const bool writer = lane < 32;
   {
     float sv = lds_st->amv;
@@ -303,7 +321,7 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float z2 = __fmul_rn(sb[4 * q + j], c2);
+        const float z2 = kCap ? sb[4 * q + j] : __fmul_rn(sb[4 * q + j], c2);
         const float dz = __fsub_rn(z2, ref);
         const float g2 = gumbel2s_from_word(wd[j]);
         if (kMasked) {
@@ -338,6 +356,12 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
         case 1: sb = s1; break;
         case 2: sb = s2; break;
         default: sb = s3; break;
+      }
+      // capped z2 of the whole block first, so that tanhf's temporaries are dead before
+      // the noise's are live
+      if (kCap) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sb[i] = soft_cap_z2(sb[i], cap);
       }
       block(masked, sb, vb0 + 32 * mb, pt + 512 * mb);
     }
@@ -403,6 +427,7 @@ constexpr int kNst1 = 2;           // stages
 // so that the sixteen consecutive rows one ds_read_b128 pass serves fall on distinct banks.
 __device__ __forceinline__ int swz1(int r) { return (r >> 1) & 7; }
 
+template <bool kCap>
 __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   constexpr int kStage = 512 * kRow1;  // 256 E rows + 256 h rows
   constexpr int kHOff = kTile * kRow1;
@@ -557,6 +582,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   };
 
   const float c2 = kLog2e / g.a.temperature[c];
+  SoftCap cap{};
+  if (kCap) cap = SoftCap{1.0f / g.a.softcap, g.a.softcap * c2};
   const uint32_t step = (uint32_t)g.a.step[c];
   const uint32_t k0 = g.a.k0, k1 = g.a.k1;
   const int rloc0 = 64 * rq + fr;  // row (in the canvas) of block 0; block 1 is 32 rows on
@@ -597,15 +624,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
     const size_t vblk = (size_t)(vt0 >> 5) * 512;  // first 32-entry block of the half tile
     if (heavy) {
-      epi_row<true>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, row0, step, k0, k1,
-                    prow0 + vblk, rout0, st0p);
-      epi_row<true>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, row1, step, k0, k1,
-                    prow1 + vblk, rout0 + 32, st1p);
+      epi_row<true, kCap>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
+                          step, k0, k1, prow0 + vblk, rout0, st0p);
+      epi_row<true, kCap>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap, row1,
+                          step, k0, k1, prow1 + vblk, rout0 + 32, st1p);
     } else {
-      epi_row<false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, row0, step, 0, 0,
-                     prow0, rout0, st0p);
-      epi_row<false>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, row1, step, 0, 0,
-                     prow1, rout0 + 32, st1p);
+      epi_row<false, false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
+                            step, 0, 0, prow0, rout0, st0p);
+      epi_row<false, false>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap, row1,
+                            step, 0, 0, prow1, rout0 + 32, st1p);
     }
   }
   vm_wait<0>();
@@ -1216,7 +1243,12 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
                      pos, n_nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_logits, dim3((unsigned)(kWG * p.n_rounds)), dim3(512), 0, stream, g);
+  if (a.softcap != 0.0f)
+    hipLaunchKernelGGL(k_gemm_logits<true>, dim3((unsigned)(kWG * p.n_rounds)), dim3(512), 0,
+                       stream, g);
+  else
+    hipLaunchKernelGGL(k_gemm_logits<false>, dim3((unsigned)(kWG * p.n_rounds)), dim3(512), 0,
+                       stream, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.selfcond != nullptr) {

@@ -87,10 +87,22 @@ def from_workload(wl, want_selfcond: bool = True, device="cuda", E: Optional[tor
                     commit, wl.step, want_selfcond=want_selfcond, device=device)
 
 
-def vocab_pass(b: VocabBuffers, seed: int, stream=None) -> None:
-    B.dg_vocab_pass(b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step,
-                    b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace,
-                    stream=stream)
+def vocab_pass(b: VocabBuffers, seed: int, stream=None, softcap: Optional[float] = None) -> None:
+    """softcap: None for the plain logits, c > 0 for c tanh(S / c) before the temperature."""
+    args = (b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step, b.lse,
+            b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace)
+    if softcap is None:
+        B.dg_vocab_pass(*args, stream=stream)
+    else:
+        B.dg_vocab_pass_softcap(*args, stream=stream, softcap=softcap)
+
+
+def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:
+    """Temperature of decode pass i of N (0 <= i < N): linear from t_max toward t_min in steps
+    of (t_min - t_max) / N (DiffusionGemma Explained, "Sampling" -> "Apply temperature")."""
+    if not (N >= 1 and 0 <= i < N):
+        raise ValueError(f"decode pass {i} outside [0, {N})")
+    return t_max + (t_min - t_max) * (i / N)
 
 
 def accept_renoise(b: VocabBuffers, budget: float, confidence: float, stability: int, seed: int,
@@ -102,9 +114,9 @@ def accept_renoise(b: VocabBuffers, budget: float, confidence: float, stability:
 
 
 def denoise_step(b: VocabBuffers, budget: float, confidence: float, stability: int, seed: int,
-                 stream=None) -> None:
+                 stream=None, softcap: Optional[float] = None) -> None:
     """One step of the hot path: vocabulary pass, then accept/renoise/convergence."""
-    vocab_pass(b, seed, stream)
+    vocab_pass(b, seed, stream, softcap)
     accept_renoise(b, budget, confidence, stability, seed, stream)
 
 
@@ -121,7 +133,8 @@ class LoopResult:
 
 
 def run_loop(wl, seed: int, max_steps: int = 32, stream=None, on_step=None,
-             E: Optional[torch.Tensor] = None) -> LoopResult:
+             E: Optional[torch.Tensor] = None, schedule: Optional[tuple] = None,
+             softcap: Optional[float] = None) -> LoopResult:
     """The full denoise loop of the full_loop workload: at step k the hidden states come from
     synth.loop_hidden (signal 0.5 + 0.25 k, kept only at the positions accepted at step
     k - 1), then one vocabulary pass and accept/renoise run on the canvases that have not
@@ -130,7 +143,10 @@ def run_loop(wl, seed: int, max_steps: int = 32, stream=None, on_step=None,
 
     on_step(k, b, canvases, state_in) is called after each step with the buffers, the
     original canvas ids in the batch and the host copies of the sampler state the step
-    started from (prev_argmax, stable_count)."""
+    started from (prev_argmax, stable_count).
+    schedule: None keeps each canvas's workload temperature; (t_max, t_min) gives every
+    canvas temperature_schedule(k, max_steps, t_max, t_min) at step k.  softcap as in
+    vocab_pass."""
     from . import synth
     stream = stream if stream is not None else torch.cuda.current_stream()
     n, C = wl.n_canvas, B.DG_CANVAS
@@ -146,19 +162,22 @@ def run_loop(wl, seed: int, max_steps: int = 32, stream=None, on_step=None,
             break
         h_all = synth.loop_hidden(wl, k, accepted_prev)
         rows = (active[:, None] * C + np.arange(C)[None, :]).reshape(-1)
+        temp = (wl.temperature[active] if schedule is None else
+                np.full(active.size, temperature_schedule(k, max_steps, *schedule), np.float32))
         if b is None or b.n_canvas != active.size:
-            b = allocate(active.size, wl.V, wl.d, E_t, bf16_tensor(h_all[rows]),
-                         wl.temperature[active], None, np.full(active.size, k, np.int32))
+            b = allocate(active.size, wl.V, wl.d, E_t, bf16_tensor(h_all[rows]), temp, None,
+                         np.full(active.size, k, np.int32))
             b.prev_argmax.copy_(torch.from_numpy(prev[rows]))
             b.stable_count.copy_(torch.from_numpy(cnt[active]))
         else:
             b.h.copy_(bf16_tensor(h_all[rows]))
             b.step.fill_(k)
+            b.temperature.copy_(torch.from_numpy(np.asarray(temp, np.float32)))
         state_in = (b.prev_argmax.cpu().numpy(), b.stable_count.cpu().numpy())
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
-        denoise_step(b, wl.budget, wl.confidence, wl.stability, seed, stream)
+        denoise_step(b, wl.budget, wl.confidence, wl.stability, seed, stream, softcap)
         t1.record(stream)
         t1.synchronize()
         step_ms.append(t0.elapsed_time(t1))

@@ -93,6 +93,25 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
                         int32_t* gumbel_tok, float* selfcond, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* dg_vocab_pass_softcap -- dg_vocab_pass with the final-logit soft cap of the model's logits
+ * path applied before the temperature ([EXP] final logits: the raw logits are capped to
+ * (-softcap, softcap) by softcap * tanh(S / softcap), then divided by the temperature;
+ * [TR] sec. 3.3 temperature schedule, the temperature being the caller's per canvas):
+ *   z = softcap * tanh(S / softcap) / temperature[c]
+ * replaces z = S / temperature[c] in lse, entropy, the Gumbel-max sample and the
+ * self-conditioning weights; argmax_tok stays the smallest v attaining max S (the cap is
+ * increasing, so it is also the argmax of the capped logits).  All other arguments, layouts
+ * and outputs as dg_vocab_pass.
+ *  softcap      > 0 and finite ([host] scalar; the pages do not print its value).
+ * Runs on the default (two-GEMM) path: needs d % 128 == 0, else DG_ERR_UNSUPPORTED.
+ * Errors: as dg_vocab_pass; DG_ERR_INVALID_ARG for a softcap that is not finite and > 0. */
+dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
+                                int d, const float* temperature, const uint8_t* commit,
+                                uint64_t seed, const int32_t* step, float* lse, float* entropy,
+                                int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                float softcap);
+
 /* dg_accept_renoise -- per-canvas acceptance, renoising and convergence of one step.
  *
  * For a canvas that does not commit ([TR] sec. 3.3 "Entropy-bounded token refinement",

@@ -28,8 +28,9 @@ def _lib():
 
 def test_header_symbols_exported():
     decl = _declared()
-    assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_accept_renoise",
-                         "dg_q_sample", "dg_status_string", "dg_last_error"}
+    assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass",
+                         "dg_vocab_pass_softcap", "dg_accept_renoise", "dg_q_sample",
+                         "dg_status_string", "dg_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -120,3 +121,20 @@ def test_binding_refuses_missing_library(tmp_path):
             binding.load(str(tmp_path / "absent.so"))
     finally:
         binding._lib = saved
+
+
+def test_softcap_value_rejected_on_host():
+    """A soft cap that is not finite and > 0 is refused before any device work."""
+    import ctypes
+    lib = _lib()
+    f = lib.dg_vocab_pass_softcap
+    P = ctypes.c_void_p
+    f.argtypes = [P, P] + [ctypes.c_int] * 4 + [P, P, ctypes.c_uint64] + [P] * 7 + \
+        [ctypes.c_size_t, P, ctypes.c_float]
+    f.restype = ctypes.c_int
+    lib.dg_last_error.restype = ctypes.c_char_p
+    for c in (0.0, -2.0, float("inf"), float("nan")):
+        st = f(None, None, 1, 256, 4096, 256, None, None, 0, None, None, None, None, None, None,
+               None, 0, None, c)
+        assert st == 1, c
+        assert b"softcap" in lib.dg_last_error()

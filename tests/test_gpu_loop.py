@@ -31,7 +31,10 @@ def _gpu():
     yield
 
 
-def test_full_loop_reduced_every_step():
+@pytest.mark.parametrize("schedule,softcap", [(None, None), ((0.8, 0.4), 30.0)])
+def test_full_loop_reduced_every_step(schedule, softcap):
+    """Per-canvas temperatures, or the linear anneal from 0.8 toward 0.4 over the loop's steps
+    with the logits soft-capped at 30."""
     from denoise_step_sampler_amd import runner
     wl = synth.workload("full_loop", V=4096, d=256, seed=2)
     E64 = ovp.widen_bf16(wl.E)
@@ -44,9 +47,12 @@ def test_full_loop_reduced_every_step():
         rows = (canv[:, None] * C + np.arange(C)[None, :]).reshape(-1)
         h_bits = synth.loop_hidden(wl, k, check.acc_prev)[rows]
         step = np.full(n, k, np.int32)
-        T = np.repeat(wl.temperature[canv], C)
+        if schedule is None:
+            T = np.repeat(wl.temperature[canv], C)
+        else:
+            T = np.full(n * C, ovp.temperature_schedule(k, 10, *schedule))
         ref = ovp.vocab_pass_rows(E64, h_bits, np.arange(n * C), T, np.zeros(n * C, bool),
-                                  seed, np.repeat(step, C), want_sc=False)
+                                  seed, np.repeat(step, C), want_sc=False, softcap=softcap)
         out = {"lse": b.lse.cpu().numpy(), "entropy": b.entropy.cpu().numpy(),
                "argmax": b.argmax_tok.cpu().numpy(), "gumbel": b.gumbel_tok.cpu().numpy()}
         rep = compare_vocab(out, ref, np.zeros(n * C, bool))
@@ -72,10 +78,13 @@ def test_full_loop_reduced_every_step():
         check.acc_prev = a
 
     check.acc_prev = None
-    res = runner.run_loop(wl, seed, max_steps=10, on_step=check)
+    res = runner.run_loop(wl, seed, max_steps=10, on_step=check, schedule=schedule,
+                          softcap=softcap)
     for r in reports:
         _say("   ", r)
     assert res.steps_run == 10 and len(reports) == 10
+    if schedule is not None:
+        return
     # near-maximal entropies: one accepted position per canvas and step, nothing converges
     assert all(r["accepted"] == 8 for r in reports)
     assert np.all(res.steps_to_converge == -1)

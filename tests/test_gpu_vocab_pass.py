@@ -210,3 +210,61 @@ def test_batched_serving_step_sampled(large, path):
     cm = np.repeat(wl.commit.astype(bool), 256)
     assert np.all(np.isnan(b.entropy.cpu().numpy()[cm]))
     assert np.all(b.argmax_tok.cpu().numpy() >= 0)
+
+
+# --- final-logit soft cap ----------------------------------------------------------------
+
+def _check_cap(wl, seed, c, rows=None, E64=None, E_t=None, label=""):
+    from denoise_step_sampler_amd import runner
+    _say(f"[vocab_pass softcap={c}] {label} n={wl.n_canvas} V={wl.V} d={wl.d} seed={seed}")
+    b = runner.from_workload(wl, E=E_t)
+    runner.vocab_pass(b, seed, softcap=c)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.R) if rows is None else np.asarray(rows)
+    E64 = ovp.widen_bf16(wl.E) if E64 is None else E64
+    ref = ovp.vocab_pass_rows(E64, wl.h, rows, np.repeat(wl.temperature, wl.C),
+                              np.repeat(wl.commit.astype(bool), wl.C), seed,
+                              np.repeat(wl.step, wl.C), softcap=c)
+    rep = compare_vocab(_host(b, rows), ref, np.repeat(wl.commit.astype(bool), wl.C))
+    _say("   ", rep)
+    return b, rep
+
+
+@pytest.mark.parametrize("c,scale,V,d", [(5.0, 1.0, 5000, 256), (30.0, 1.0, 1000, 128),
+                                         (2.0, 8.0, 777, 384), (30.0, 3.0, 129, 256)])
+def test_softcap_parity(c, scale, V, d):
+    """Soft-capped logits against the oracle: a strong cap, a mild one, hidden states scaled
+    so that most logits saturate, ragged vocabularies, a commit canvas mixed in."""
+    wl = synth.workload("lite", V=V, d=d, n_canvas=3, seed=21)
+    wl.h = synth.round_to_bf16(synth.bf16_to_f32(wl.h) * np.float32(scale))
+    wl.temperature = np.array([0.4, 0.8, 1.0], np.float32)
+    wl.step = np.array([0, 3, 9], np.int32)
+    wl.commit = np.array([0, 1, 0], np.uint8)
+    _check_cap(wl, 0x5EED, c, label=f"c={c} x{scale}")
+
+
+def test_softcap_deterministic_and_differs_from_plain():
+    """Two capped runs agree bit for bit; a cap below the logits' range changes lse."""
+    from denoise_step_sampler_amd import runner
+    wl = synth.workload("lite", V=3000, d=256, n_canvas=2, seed=5)
+    outs = []
+    for c in (3.0, 3.0, None):
+        b = runner.from_workload(wl)
+        runner.vocab_pass(b, 9, softcap=c)
+        torch.cuda.synchronize()
+        outs.append(b)
+    for k in ("lse", "entropy", "argmax_tok", "gumbel_tok", "selfcond"):
+        x, y = getattr(outs[0], k).cpu().numpy(), getattr(outs[1], k).cpu().numpy()
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), k
+    assert np.array_equal(outs[0].argmax_tok.cpu().numpy(), outs[2].argmax_tok.cpu().numpy())
+    assert not np.allclose(outs[0].lse.cpu().numpy(), outs[2].lse.cpu().numpy())
+
+
+def test_softcap_batched_serving_step_sampled(large):
+    """The 32-canvas serving step at V = 262144, d = 2816 with a cap of 30, sampled rows."""
+    E, E_t, E64 = large
+    wl = synth.workload("batched", E=E)
+    rng = np.random.default_rng(2)
+    canv = [0, 3, 9, 30]
+    rows = np.sort(np.concatenate([c * 256 + rng.choice(256, 3, replace=False) for c in canv]))
+    _check_cap(wl, 3, 30.0, rows=rows, E64=E64, E_t=E_t, label="batched")
