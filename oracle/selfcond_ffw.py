@@ -21,7 +21,8 @@ res stay unrounded (plain reading: a fused implementation need not materialise t
 
 The first decode step has no previous prediction: sc = None gives res = 0, so
 out = rms_1(E[tok] s) (the MLP maps zero to zero).
-Rows of commit canvases are not computed (NaN).
+Rows of commit canvases are not computed (NaN), nor are rows whose token lies outside
+[0, V) (the pages never index the embedding out of range; such a row is NaN).
 """
 from __future__ import annotations
 
@@ -79,7 +80,8 @@ def selfcond_input(sc: Optional[np.ndarray], tokens: np.ndarray, E_bits: np.ndar
     s = math.sqrt(D)
     cm = np.zeros(R, bool) if commit_row is None else np.asarray(commit_row, bool)
     out = np.full((rows.size, D), np.nan)
-    keep = ~cm[rows]
+    tok_ok = (tokens >= 0) & (tokens < V)
+    keep = ~cm[rows] & tok_ok[rows]
     rk = rows[keep]
     if rk.size == 0:
         return out

@@ -121,3 +121,11 @@ def test_commit_rows_untouched():
     out = of.selfcond_input(np.ones((R, D)), np.arange(R), E, pre, Wg, Wu, Wd,
                             commit_row=np.array([0, 1, 1, 0], bool))
     assert np.all(np.isnan(out[1:3])) and not np.isnan(out[[0, 3]]).any()
+
+
+def test_out_of_range_tokens_give_nan_rows():
+    V, D, F = 30, 8, 8
+    E = synth.make_embedding(V, D, seed=6)
+    pre, Wg, Wu, Wd = _weights(D, F, 7)
+    out = of.selfcond_input(None, np.array([0, -1, V, 5]), E, pre, Wg, Wu, Wd)
+    assert np.all(np.isnan(out[1:3])) and not np.isnan(out[[0, 3]]).any()
