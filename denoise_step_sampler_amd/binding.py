@@ -20,7 +20,8 @@ DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = ra
 DG_CANVAS = 256
 
 EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_vocab_pass_softcap",
-            "dg_accept_renoise", "dg_q_sample", "dg_status_string", "dg_last_error")
+            "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
+            "dg_selfcond_input", "dg_status_string", "dg_last_error")
 
 
 class DGError(RuntimeError):
@@ -53,6 +54,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_accept_renoise.restype = I
     lib.dg_q_sample.argtypes = [P, I, I, I, P, U64, P, P]
     lib.dg_q_sample.restype = I
+    lib.dg_selfcond_input_workspace_size.argtypes = [I, I, I, I]
+    lib.dg_selfcond_input_workspace_size.restype = SZ
+    lib.dg_selfcond_input.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, P, SZ, P]
+    lib.dg_selfcond_input.restype = I
     lib.dg_status_string.argtypes = [I]
     lib.dg_status_string.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -182,4 +187,31 @@ def dg_q_sample(x0: torch.Tensor, n_canvas: int, C: int, V: int, kappa: torch.Te
         _ptr(kappa, torch.float32, n_canvas, "kappa"),
         ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
         _ptr(xt, torch.int32, R, "xt"), _stream(stream))
+    _check(st)
+
+
+def dg_selfcond_input_workspace_size(n_canvas: int, C: int, D: int, F: int) -> int:
+    return int(load().dg_selfcond_input_workspace_size(n_canvas, C, D, F))
+
+
+def dg_selfcond_input(sc: Optional[torch.Tensor], tokens: torch.Tensor, E: torch.Tensor,
+                      pre_norm: Optional[torch.Tensor], W_gate: Optional[torch.Tensor],
+                      W_up: Optional[torch.Tensor], W_down: Optional[torch.Tensor],
+                      commit: Optional[torch.Tensor], n_canvas: int, C: int, V: int, D: int,
+                      F: int, eps: float, out: torch.Tensor, workspace: torch.Tensor,
+                      stream=None) -> None:
+    """Weights and E as bf16 bits (int16/uint16) or torch.bfloat16; out likewise."""
+    R = n_canvas * C
+    lib = load()
+    opt = lambda t, n, name: None if t is None else _bf16_ptr(t, n, name)
+    st = lib.dg_selfcond_input(
+        _ptr(sc, torch.float32, R * D, "sc"),
+        _ptr(tokens, torch.int32, R, "tokens"),
+        _bf16_ptr(E, V * D, "E"),
+        opt(pre_norm, D, "pre_norm"), opt(W_gate, F * D, "W_gate"), opt(W_up, F * D, "W_up"),
+        opt(W_down, D * F, "W_down"),
+        _ptr(commit, torch.uint8, n_canvas, "commit"),
+        n_canvas, C, V, D, F, ctypes.c_float(eps),
+        _bf16_ptr(out, R * D, "out"),
+        _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
     _check(st)

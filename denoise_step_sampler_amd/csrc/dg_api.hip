@@ -81,6 +81,16 @@ dg_status check_vocab_shape(int n_canvas, int C, int V, int d) {
   return DG_OK;
 }
 
+dg_status check_ffw_shape(int n_canvas, int C, int D, int F) {
+  dg_status s = check_canvas(n_canvas, C);
+  if (s != DG_OK) return s;
+  if (D < 64 || D > 16384 || D % 64 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "D=%d: need a multiple of 64 in [64, 16384]", D);
+  if (F < 64 || F > 65536 || F % 64 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "F=%d: need a multiple of 64 in [64, 65536]", F);
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +251,58 @@ dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
   a.mean_entropy = mean_entropy;
   const hipError_t e = dg::accept_renoise_launch(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "accept/renoise launch");
+  return DG_OK;
+}
+
+size_t dg_selfcond_input_workspace_size(int n_canvas, int C, int D, int F) {
+  char keep[sizeof(g_err)];
+  memcpy(keep, g_err, sizeof(g_err));
+  const dg_status s = check_ffw_shape(n_canvas, C, D, F);
+  memcpy(g_err, keep, sizeof(g_err));
+  if (s != DG_OK) return 0;
+  return dg::ffw_plan(n_canvas, D, F).bytes;
+}
+
+dg_status dg_selfcond_input(const float* sc, const int32_t* tokens, const uint16_t* E,
+                            const uint16_t* pre_norm, const uint16_t* W_gate,
+                            const uint16_t* W_up, const uint16_t* W_down,
+                            const uint8_t* commit, int n_canvas, int C, int V, int D, int F,
+                            float eps, uint16_t* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_err[0] = 0;
+  dg_status s = check_ffw_shape(n_canvas, C, D, F);
+  if (s != DG_OK) return s;
+  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
+  if (!(eps >= 0.0f) || !isfinite(eps))
+    return fail(DG_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!tokens || !E || !out) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (sc && (!pre_norm || !W_gate || !W_up || !W_down))
+    return fail(DG_ERR_INVALID_ARG, "the MLP weights are NULL");
+  const void* ptrs[] = {sc, tokens, E, pre_norm, W_gate, W_up, W_down, out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(DG_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const dg::FfwPlan plan = dg::ffw_plan(n_canvas, D, F);
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                plan.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  dg::FfwArgs a{};
+  a.sc = sc;
+  a.tokens = tokens;
+  a.E = E;
+  a.pre_norm = pre_norm;
+  a.W_gate = W_gate;
+  a.W_up = W_up;
+  a.W_down = W_down;
+  a.commit = commit;
+  a.V = V;
+  a.D = D;
+  a.F = F;
+  a.eps = eps;
+  a.out = out;
+  const hipError_t e = dg::ffw_launch(a, plan, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "self-conditioning input launch");
   return DG_OK;
 }
 

@@ -136,4 +136,35 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float& a, float m2
   m = M;
 }
 
+// ---------------------------------------------------------------------------------------
+// LDS access and LDS DMA (global_load_lds_dwordx4: 64 lanes x 16 bytes = one 1 KB copy).
+// ---------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+
+
+// LDS DMA issued as inline assembly: the compiler does not see these copies, so it neither
+// waits for them before unrelated LDS reads (it cannot tell the two stages apart for the
+// transpose reads) nor counts them; the kernel waits for them explicitly (vm_wait) before the
+// barrier that publishes a stage.  base is wave-uniform, off per lane, dst the wave-uniform
+// LDS address of the 1 KB destination; the one-cycle nop covers the M0 -> LDS DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_asm(const void* base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(dst)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+
 }  // namespace dg

@@ -118,6 +118,28 @@ struct AcceptArgs {
 };
 hipError_t accept_renoise_launch(const AcceptArgs& a, hipStream_t stream);
 
+// Self-conditioning consumer (selfcond_ffw.hip).
+struct FfwArgs {
+  const float* sc;          // [R, D] or null (first decode step)
+  const int32_t* tokens;    // [R]
+  const uint16_t* E;        // [V, D]
+  const uint16_t* pre_norm; // [D]
+  const uint16_t* W_gate;   // [F, D]
+  const uint16_t* W_up;     // [F, D]
+  const uint16_t* W_down;   // [D, F]
+  const uint8_t* commit;    // [n_canvas] or null
+  int V, D, F;
+  float eps;
+  uint16_t* out;            // [R, D]
+};
+struct FfwPlan {
+  size_t R;
+  size_t off_x1, off_y, off_res;
+  size_t bytes;
+};
+FfwPlan ffw_plan(int n_canvas, int D, int F);
+hipError_t ffw_launch(const FfwArgs& a, const FfwPlan& p, void* workspace, hipStream_t stream);
+
 hipError_t q_sample_launch(const int32_t* x0, int n_canvas, int V, const float* kappa,
                            uint32_t k0, uint32_t k1, int32_t* xt, hipStream_t stream);
 

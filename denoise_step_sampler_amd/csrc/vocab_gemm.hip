@@ -47,7 +47,6 @@
 namespace dg {
 namespace {
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -57,32 +56,6 @@ constexpr int kLanesMax = 256;  // vocabulary lanes per canvas at most (one canv
 constexpr int kWG = 256;        // workgroups per round of the logits pass
 constexpr int kFacStride = 72;  // floats per row of the combine's weights
 constexpr int kRoundMax = 32;   // canvases per round of the logits pass (four per XCD)
-
-__device__ __forceinline__ u32x4 lds_read16(const lds_char* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
-}
-
-
-// LDS DMA issued as inline assembly: the compiler does not see these copies, so it neither
-// waits for them before unrelated LDS reads (it cannot tell the two stages apart for the
-// transpose reads) nor counts them; the kernel waits for them explicitly (vm_wait) before the
-// barrier that publishes a stage.  base is wave-uniform, off per lane, dst the wave-uniform
-// LDS address of the 1 KB destination; the one-cycle nop covers the M0 -> LDS DMA hazard.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_asm(const void* base, uint32_t off, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(dst)
-               : "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 
 // ---------------------------------------------------------------------------------------
 // Schedule of the logits pass.  Canvases are taken in `order` (non-commit first) in rounds

@@ -97,6 +97,40 @@ def vocab_pass(b: VocabBuffers, seed: int, stream=None, softcap: Optional[float]
         B.dg_vocab_pass_softcap(*args, stream=stream, softcap=softcap)
 
 
+@dataclass
+class FfwWeights:
+    """Device copies of the self-conditioning MLP (bf16 bits as int16)."""
+    D: int
+    F: int
+    pre_norm: torch.Tensor
+    W_gate: torch.Tensor
+    W_up: torch.Tensor
+    W_down: torch.Tensor
+    eps: float = 1e-6
+
+
+def ffw_weights(pre, Wg, Wu, Wd, eps: float = 1e-6, device="cuda") -> FfwWeights:
+    D, F = Wd.shape
+    return FfwWeights(D=D, F=F, pre_norm=bf16_tensor(pre, device), W_gate=bf16_tensor(Wg, device),
+                      W_up=bf16_tensor(Wu, device), W_down=bf16_tensor(Wd, device), eps=eps)
+
+
+def ffw_workspace(n_canvas: int, D: int, F: int, device="cuda") -> torch.Tensor:
+    n = B.dg_selfcond_input_workspace_size(n_canvas, B.DG_CANVAS, D, F)
+    if n == 0:
+        raise ValueError(f"unsupported shape n={n_canvas} D={D} F={F}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def selfcond_input(b: VocabBuffers, W: FfwWeights, out: torch.Tensor, workspace: torch.Tensor,
+                   first_step: bool = False, stream=None) -> None:
+    """The next step's input rows from b.selfcond and b.next_tokens (first_step: no
+    self-conditioning signal yet)."""
+    B.dg_selfcond_input(None if first_step else b.selfcond, b.next_tokens, b.E, W.pre_norm,
+                        W.W_gate, W.W_up, W.W_down, b.commit, b.n_canvas, b.C, b.V, b.d, W.F,
+                        W.eps, out, workspace, stream=stream)
+
+
 def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:
     """Temperature of decode pass i of N (0 <= i < N): linear from t_max toward t_min in steps
     of (t_min - t_max) / N (DiffusionGemma Explained, "Sampling" -> "Apply temperature")."""

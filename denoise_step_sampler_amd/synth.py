@@ -24,7 +24,7 @@ import numpy as np
 C_CANVAS = 256
 
 # purposes of the independent random streams
-_S_EMBED, _S_TARGET, _S_SCALE, _S_NOISE, _S_QS_X0, _S_QS_T = 1, 2, 3, 4, 5, 6
+_S_EMBED, _S_TARGET, _S_SCALE, _S_NOISE, _S_QS_X0, _S_QS_T, _S_FFW = 1, 2, 3, 4, 5, 6, 7
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -74,6 +74,28 @@ def make_hidden(E: np.ndarray, targets: np.ndarray, scale: np.ndarray, seed: int
         sc = sc * np.asarray(keep_signal, dtype=np.float32).reshape(R, 1)
     sig = bf16_to_f32(E[targets]) * sc
     return round_to_bf16(sig + noise)
+
+
+def make_ffw_weights(D: int, F: int, seed: int) -> Tuple[np.ndarray, ...]:
+    """Random bf16 weights of the self-conditioning MLP: pre-norm weight 1 + 0.1 N(0, 1) [D],
+    W_gate and W_up N(0, 1 / D) [F, D], W_down N(0, 1 / F) [D, F]."""
+    rng = np.random.default_rng([seed, _S_FFW, D, F])
+    pre = round_to_bf16((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    Wg = round_to_bf16((rng.standard_normal((F, D)) / math.sqrt(D)).astype(np.float32))
+    Wu = round_to_bf16((rng.standard_normal((F, D)) / math.sqrt(D)).astype(np.float32))
+    Wd = round_to_bf16((rng.standard_normal((D, F)) / math.sqrt(F)).astype(np.float32))
+    return pre, Wg, Wu, Wd
+
+
+def make_selfcond_rows(E: np.ndarray, R: int, seed: int, k: int = 4) -> np.ndarray:
+    """Stand-ins for self-conditioning rows: random convex mixtures (Dirichlet(1) weights) of
+    k random embedding rows, fp32 [R, d]; plus the tokens of the next canvas, uniform [R]."""
+    V, d = E.shape
+    rng = np.random.default_rng([seed, _S_FFW, R, V, d])
+    idx = rng.integers(0, V, size=(R, k))
+    wts = rng.dirichlet(np.ones(k), size=R).astype(np.float32)
+    rows = np.einsum("rk,rkd->rd", wts, bf16_to_f32(E[idx])).astype(np.float32)
+    return rows, rng.integers(0, V, size=R).astype(np.int32)
 
 
 def cosine_kappa(t: np.ndarray, T: int) -> np.ndarray:

@@ -154,6 +154,42 @@ dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
 dg_status dg_q_sample(const int32_t* x0, int n_canvas, int C, int V, const float* kappa,
                       uint64_t seed, int32_t* xt, void* stream);
 
+/* dg_selfcond_input_workspace_size -- bytes of workspace dg_selfcond_input needs ([host],
+ * pure): 256-byte aligned buffers for x1 [R, D] bf16, y [R, F] bf16 and res [R, D] fp32,
+ * R = n_canvas * C.  0 for an unsupported shape. */
+size_t dg_selfcond_input_workspace_size(int n_canvas, int C, int D, int F);
+
+/* dg_selfcond_input -- the next decode step's input rows: the renoised tokens' embeddings
+ * plus the self-conditioning signal, normalised ([EXP] "Self-conditioning" and the decode
+ * forward: the expectation P @ E scaled by sqrt(D), passed through the conditioning MLP,
+ * added to the scaled token embedding, RMS-normalised; the conditioning MLP is the gated
+ * GELU MLP of [EXP] "Mixture of Experts" with a weighted pre-norm; RMSNorm as in [EXP]
+ * "RMSNorm", eps added to the row norm; [TR] sec. 3.2 eq. (6) FFW(p_hat_0 E)):
+ *   cx  = sc * sqrt(D)
+ *   x1  = bf16(pre_norm * cx * sqrt(D) / (||cx||_2 + eps))
+ *   y   = bf16((x1 W_up^T) * GELU(x1 W_gate^T)),  GELU(x) = x (1 + erf(x / sqrt 2)) / 2
+ *   res = y W_down^T                                   (fp32)
+ *   out = bf16(x * sqrt(D) / (||x||_2 + eps)),  x = E[tokens] * sqrt(D) + res
+ * bf16 MFMA products with fp32 accumulation; norms and elementwise work in fp32.
+ *  sc        [R, D] fp32 (dg_vocab_pass's selfcond), or NULL on the first decode step: the
+ *            MLP maps zero to zero, so res = 0 and W_* and pre_norm are not read.
+ *  tokens    [R] int32 renoised tokens (dg_accept_renoise's next_tokens); a token outside
+ *            [0, V) gives a row of NaN.
+ *  E         [V, D] bf16 tied embedding.   pre_norm: [D] bf16 weight of the MLP's pre-norm.
+ *  W_gate, W_up [F, D] bf16; W_down [D, F] bf16 (rows are output features).
+ *  commit    [n_canvas] uint8 or NULL: the rows of a commit canvas are neither read nor
+ *            written.
+ *  C == 256; D % 64 == 0, 64 <= D <= 16384; F % 64 == 0, 64 <= F <= 65536; eps >= 0 finite.
+ *  out       [R, D] bf16 (may not alias any input).   Every pointer 16-byte aligned.
+ *  workspace of dg_selfcond_input_workspace_size bytes, 256-byte aligned.
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP. */
+dg_status dg_selfcond_input(const float* sc, const int32_t* tokens, const uint16_t* E,
+                            const uint16_t* pre_norm, const uint16_t* W_gate,
+                            const uint16_t* W_up, const uint16_t* W_down,
+                            const uint8_t* commit, int n_canvas, int C, int V, int D, int F,
+                            float eps, uint16_t* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Static text of a status code ([host]). */
 const char* dg_status_string(dg_status s);
 /* Message of the last error raised on the calling host thread ([host], thread-local; "" if

@@ -30,6 +30,7 @@ def test_header_symbols_exported():
     decl = _declared()
     assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass",
                          "dg_vocab_pass_softcap", "dg_accept_renoise", "dg_q_sample",
+                         "dg_selfcond_input_workspace_size", "dg_selfcond_input",
                          "dg_status_string", "dg_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
@@ -138,3 +139,34 @@ def test_softcap_value_rejected_on_host():
                None, 0, None, c)
         assert st == 1, c
         assert b"softcap" in lib.dg_last_error()
+
+
+def test_selfcond_input_workspace_and_validation_on_host():
+    """Workspace sizes of the self-conditioning consumer and its host-side refusals."""
+    import ctypes
+    lib = _lib()
+    ws = lib.dg_selfcond_input_workspace_size
+    ws.restype = ctypes.c_size_t
+    R, D, F = 2 * 256, 256, 512
+    n = ws(2, 256, D, F)
+    assert n >= R * D * 2 + R * F * 2 + R * D * 4 and n % 256 == 0
+    assert ws(2, 128, D, F) == 0          # C != 256
+    assert ws(2, 256, 96, F) == 0         # D % 64
+    assert ws(2, 256, D, 100) == 0        # F % 64
+    assert ws(0, 256, D, F) == 0
+    f = lib.dg_selfcond_input
+    P = ctypes.c_void_p
+    f.argtypes = [P] * 8 + [ctypes.c_int] * 5 + [ctypes.c_float, P, P, ctypes.c_size_t, P]
+    f.restype = ctypes.c_int
+    lib.dg_last_error.restype = ctypes.c_char_p
+    dummy = 4096  # never dereferenced: validation fails first
+    # eps < 0
+    assert f(None, dummy, dummy, None, None, None, None, None, 1, 256, 100, 64, 64, -1.0,
+             dummy, dummy, 1 << 30, None) == 1
+    # MLP weights missing while sc is given
+    assert f(dummy, dummy, dummy, None, None, None, None, None, 1, 256, 100, 64, 64, 1e-6,
+             dummy, dummy, 1 << 30, None) == 1
+    assert b"weights" in lib.dg_last_error()
+    # workspace too small
+    assert f(None, dummy, dummy, None, None, None, None, None, 1, 256, 100, 64, 64, 1e-6,
+             dummy, dummy, 16, None) == 3
