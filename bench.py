@@ -151,6 +151,9 @@ def main() -> int:
                     help="only run a plain device copy of MB MiB (counter calibration)")
     ap.add_argument("--softcap", type=float, default=None,
                     help="final-logit soft cap c (logits c tanh(S / c)); default: none")
+    ap.add_argument("--ffw-F", type=int, default=2816, metavar="F",
+                    help="hidden width of the self-conditioning MLP timed beside the step "
+                         "(0: skip)")
     ap.add_argument("--anneal", default=None, metavar="TMAX,TMIN",
                     help="full_loop only: linear temperature schedule over the 32 steps")
     args = ap.parse_args()
@@ -231,6 +234,31 @@ def main() -> int:
     k1_ms = float(np.mean([a.elapsed_time(z) for a, z in ev2]))
     log(f"[bench] logits kernel (pass without the expectation): {k1_ms:.3f} ms")
 
+    # the self-conditioning consumer (f2): the next step's input rows from this step's sc and
+    # renoised tokens, timed alone (it is not part of the step above)
+    ffw = None
+    if args.ffw_F > 0:
+        W = runner.ffw_weights(*synth.make_ffw_weights(wl.d, args.ffw_F, seed))
+        x_next = torch.empty((wl.R, wl.d), dtype=torch.int16, device=dev)
+        ws_f = runner.ffw_workspace(wl.n_canvas, wl.d, args.ffw_F)
+        for _ in range(2):
+            runner.selfcond_input(b, W, x_next, ws_f, stream=stream)
+        ev3 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            ev3[k][0].record(stream)
+            runner.selfcond_input(b, W, x_next, ws_f, stream=stream)
+            ev3[k][1].record(stream)
+        torch.cuda.synchronize()
+        f_ms = float(np.mean([a.elapsed_time(z) for a, z in ev3]))
+        R_nc = int((wl.commit == 0).sum()) * wl.C
+        f_flops = 6.0 * R_nc * wl.d * args.ffw_F
+        ffw = {"F": args.ffw_F, "avg_launch_ms": f_ms, "algorithmic_flops": f_flops,
+               "achieved_tflops": f_flops / (f_ms * 1e-3) / 1e12,
+               "frac_bf16_peak": f_flops / (f_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+        log(f"[bench] self-conditioning input (F={args.ffw_F}): {f_ms:.3f} ms")
+
     flops = algorithmic_flops(wl)
     flops_k1 = 2.0 * wl.R * wl.V * wl.d
     ach_k1 = flops_k1 / (k1_ms * 1e-3) / 1e12
@@ -262,6 +290,8 @@ def main() -> int:
                         if gemm_path and args.softcap is None else None),
             "algorithmic_flops_per_launch": flops_k1, "avg_launch_ms": k1_ms},
     }
+    if ffw is not None:
+        res["selfcond_input"] = ffw
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f}s of oracle work)")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
