@@ -98,3 +98,77 @@ def accept_renoise(entropy, argmax_tok, gumbel_tok, commit, n_canvas: int, C: in
         mu_conv[c] = abs(meanH[c] - confidence)
     return SamplerResult(next_tokens=nxt, accept=acc, converged=conv, mean_entropy=meanH,
                          prev_argmax=prev, stable_count=cnt, mu_accept=mu_acc, mu_conv=mu_conv)
+
+
+# ---------------------------------------------------------------------------------------
+# The DiffusionGemma-Lite sampler (DiffusionGemma-Lite, section 4.2 "The commit rule" and
+# section 4.4 "Entropy-bounded adaptive stopping"), a second sampler on the same vocabulary
+# pass outputs.
+#
+#   commit    = (argmax == prev_argmax) | (conf >= prev_conf)     unchanged-or-stronger
+#   new       = commit & ~committed                              frozen tokens stay
+#   x         = new ? x0_draw : (committed ? x : uniform token)  uncommitted: redrawn
+#   committed = committed | new;  prev_argmax = argmax;  prev_conf = conf
+#   final     = committed ? x : x0_draw                          the returned canvas
+#   adaptive stop: count = (mean H < threshold) ? count + 1 : 0, stopped when count >=
+#   stability_steps; stability_steps = 0 turns it off (never stopped: the fixed schedule).
+#
+# Readings: x0_draw is the row's Gumbel-max sample and conf the probability of its argmax
+# token, both under the step's tempered distribution; the uniform token comes from the
+# same renoise stream as accept_renoise; the state starts at prev_argmax = -1,
+# prev_conf = +inf, committed = 0 (no previous posterior: nothing commits at the first step).
+# ---------------------------------------------------------------------------------------
+@dataclass
+class LiteResult:
+    x: np.ndarray               # int64 [R] canvas after the step
+    committed: np.ndarray       # uint8 [R]
+    final: np.ndarray           # int64 [R]
+    prev_argmax: np.ndarray     # int64 [R]
+    prev_conf: np.ndarray       # fp64 [R]
+    stable_count: np.ndarray    # int64 [n]
+    converged: np.ndarray       # uint8 [n]
+    mean_entropy: np.ndarray    # fp64 [n]
+    mu_commit: np.ndarray       # fp64 [R]: |conf - prev_conf| where argmax changed, else inf
+    mu_stop: np.ndarray         # fp64 [n]: |mean H - threshold|
+
+
+def lite_step(entropy, argmax_tok, gumbel_tok, conf, n_canvas: int, C: int, V: int,
+              threshold: float, stability_steps: int, seed: int, step, x, prev_argmax,
+              prev_conf, committed, stable_count) -> LiteResult:
+    H = np.asarray(entropy, np.float64)
+    am = np.asarray(argmax_tok, np.int64)
+    gt = np.asarray(gumbel_tok, np.int64)
+    cf = np.asarray(conf, np.float64)
+    x = np.array(x, np.int64, copy=True)
+    pa = np.array(prev_argmax, np.int64, copy=True)
+    pc = np.array(prev_conf, np.float64, copy=True)
+    cm = np.array(committed, np.uint8, copy=True).astype(bool)
+    cnt = np.array(stable_count, np.int64, copy=True)
+    step = np.broadcast_to(np.asarray(step, np.int64), (n_canvas,))
+    R = n_canvas * C
+    final = np.zeros(R, np.int64)
+    conv = np.zeros(n_canvas, np.uint8)
+    meanH = np.zeros(n_canvas)
+    mu_c = np.full(R, np.inf)
+    mu_s = np.zeros(n_canvas)
+    for c in range(n_canvas):
+        rows = np.arange(c * C, (c + 1) * C)
+        same = am[rows] == pa[rows]
+        stronger = cf[rows] >= pc[rows]
+        new = (same | stronger) & ~cm[rows]
+        ren = philox.renoise_tokens(rows, V, seed, int(step[c]))
+        x[rows] = np.where(new, gt[rows], np.where(cm[rows], x[rows], ren))
+        cm[rows] |= new
+        final[rows] = np.where(cm[rows], x[rows], gt[rows])
+        with np.errstate(invalid="ignore"):
+            mu_c[rows] = np.where(same, np.inf, np.abs(cf[rows] - pc[rows]))
+        pa[rows] = am[rows]
+        pc[rows] = cf[rows]
+        meanH[c] = math.fsum(H[rows]) / C
+        mu_s[c] = abs(meanH[c] - threshold)
+        if stability_steps > 0:
+            cnt[c] = cnt[c] + 1 if meanH[c] < threshold else 0
+            conv[c] = 1 if cnt[c] >= stability_steps else 0
+    return LiteResult(x=x, committed=cm.astype(np.uint8), final=final, prev_argmax=pa,
+                      prev_conf=pc, stable_count=cnt, converged=conv, mean_entropy=meanH,
+                      mu_commit=mu_c, mu_stop=mu_s)

@@ -24,6 +24,8 @@ Definitions followed (cited by page and section):
   from the Philox layout in ``oracle.philox`` (vLLM blog, sampler section: the candidate
   token is argmax(logits / T + Gumbel noise); DiffusionGemma Explained, "Sampling": accepted
   positions take a sample of their distribution).
+* confidence of a row: the probability of its argmax token under the tempered (and capped)
+  distribution, p_{argmax} (the "conf" of the DiffusionGemma-Lite commit rule, section 4.2).
 * self-conditioning expectation sc = sum_v p_v E_v = p_hat_0 E (Technical Report sec. 3.2
   eq. (6), the argument of FFW; DiffusionGemma Explained, "Self-conditioning").
 
@@ -60,6 +62,7 @@ class RowResult:
     sc: Optional[np.ndarray]  # fp64 [n, d], NaN rows for commit rows
     mu_argmax: np.ndarray   # fp64 margins
     mu_gumbel: np.ndarray   # fp64 margins, inf for commit rows
+    conf: Optional[np.ndarray] = None  # fp64 probability of the argmax token, NaN for commit rows
 
 
 def _top2_margin(x: np.ndarray) -> float:
@@ -93,6 +96,7 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
     gtok = np.full(n, -1, dtype=np.int64)
     mu_a = np.zeros(n)
     mu_g = np.full(n, np.inf)
+    conf = np.full(n, np.nan)
     sc = np.full((n, d), np.nan) if want_sc else None
     for b0 in range(0, n, row_block):
         b1 = min(n, b0 + row_block)
@@ -112,6 +116,7 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
             lse[i] = m + np.log(np.sum(np.exp(z - m)))
             p = np.exp(z - lse[i])
             ent[i] = float(np.sum(p * (lse[i] - z)))
+            conf[i] = p[amax[i]]
             g = philox.gumbel_noise(r, V, seed, int(step_row[r]))
             y = z + g
             gtok[i] = int(np.argmax(y))
@@ -119,7 +124,7 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
             if want_sc:
                 sc[i] = p @ E64
     return RowResult(rows=rows, lse=lse, entropy=ent, argmax=amax, gumbel=gtok, sc=sc,
-                     mu_argmax=mu_a, mu_gumbel=mu_g)
+                     mu_argmax=mu_a, mu_gumbel=mu_g, conf=conf)
 
 
 def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:

@@ -1,0 +1,108 @@
+"""Pins of the DiffusionGemma-Lite sampler oracle (commit rule and entropy-only adaptive stop):
+hand-worked commit cases, monotonicity of the committed set and frozen tokens over random
+multi-step runs, the first step, a scripted stop counter, and the adaptive-off identity."""
+import os
+
+import numpy as np
+
+from oracle import philox
+from oracle import sampler as osm
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "lite_commit_cases.txt")
+
+
+def _cases():
+    rows = []
+    for ln in open(GOLD):
+        ln = ln.strip()
+        if not ln or ln.startswith("#"):
+            continue
+        a, b = ln.split("|")
+        am, pa, cf, pc, cm, x, dr = a.split()
+        xe, cme, fe = b.split()
+        rows.append((int(am), int(pa), float(cf), float(pc), int(cm), int(x), int(dr), xe,
+                     int(cme), int(fe)))
+    return rows
+
+
+def test_hand_worked_commit_cases():
+    cs = _cases()
+    C = len(cs)
+    V, seed, step = 1000, 17, 3
+    col = lambda k: np.array([c[k] for c in cs])
+    r = osm.lite_step(np.zeros(C), col(0), col(6), col(2), 1, C, V, 0.5, 2, seed, step,
+                      col(5), col(1), col(3), col(4), np.zeros(1, np.int64))
+    ren = philox.renoise_tokens(np.arange(C), V, seed, step)
+    for i, c in enumerate(cs):
+        want_x = ren[i] if c[7] == "R" else int(c[7])
+        assert r.x[i] == want_x, i
+        assert r.committed[i] == c[8], i
+        assert r.final[i] == c[9], i
+    assert np.array_equal(r.prev_argmax, col(0)) and np.array_equal(r.prev_conf, col(2))
+
+
+def test_commit_is_monotone_and_frozen():
+    rng = np.random.default_rng(5)
+    n, C, V = 3, 64, 50
+    x = rng.integers(0, V, n * C)
+    pa = np.full(n * C, -1)
+    pc = np.full(n * C, np.inf)
+    cm = np.zeros(n * C, np.uint8)
+    cnt = np.zeros(n, np.int64)
+    for k in range(12):
+        am = rng.integers(0, 4, n * C)              # few modes: argmax repeats often
+        conf = rng.random(n * C)
+        r = osm.lite_step(rng.random(n * C), am, rng.integers(0, V, n * C), conf, n, C, V,
+                          0.5, 2, 9, k, x, pa, pc, cm, cnt)
+        was = cm.astype(bool)
+        assert np.all(r.committed[was] == 1)                 # never un-commits
+        assert np.array_equal(r.x[was], x[was])              # frozen tokens unchanged
+        assert np.array_equal(r.final[r.committed == 1], r.x[r.committed == 1])
+        x, pa, pc, cm, cnt = r.x, r.prev_argmax, r.prev_conf, r.committed, r.stable_count
+    assert cm.sum() > 0
+
+
+def test_first_step_commits_nothing():
+    n, C, V = 2, 16, 300
+    rng = np.random.default_rng(1)
+    gt = rng.integers(0, V, n * C)
+    r = osm.lite_step(rng.random(n * C), rng.integers(0, V, n * C), gt, rng.random(n * C), n, C,
+                      V, 0.5, 2, 4, 0, np.zeros(n * C, np.int64), np.full(n * C, -1),
+                      np.full(n * C, np.inf), np.zeros(n * C, np.uint8), np.zeros(n, np.int64))
+    assert r.committed.sum() == 0
+    assert np.array_equal(r.x, philox.renoise_tokens(np.arange(n * C), V, 4, 0))
+    assert np.array_equal(r.final, gt)
+
+
+def test_scripted_stop_counter():
+    """Mean entropies 0.5, 0.1, 0.1, 0.3, 0.1, 0.1 against 0.2 with two steps required:
+    counts 0, 1, 2, 0, 1, 2 and stops at the third and sixth steps."""
+    C = 4
+    cnt = np.zeros(1, np.int64)
+    got_c, got_s = [], []
+    for k, m in enumerate([0.5, 0.1, 0.1, 0.3, 0.1, 0.1]):
+        r = osm.lite_step(np.full(C, m), np.zeros(C, np.int64), np.zeros(C, np.int64),
+                          np.zeros(C), 1, C, 10, 0.2, 2, 0, k, np.zeros(C, np.int64),
+                          np.full(C, -1), np.full(C, np.inf), np.zeros(C, np.uint8), cnt)
+        cnt = r.stable_count
+        got_c.append(int(cnt[0]))
+        got_s.append(int(r.converged[0]))
+    assert got_c == [0, 1, 2, 0, 1, 2]
+    assert got_s == [0, 0, 1, 0, 0, 1]
+
+
+def test_adaptive_off_is_the_fixed_schedule():
+    """stability_steps = 0: never stopped, counter untouched, and the step's tokens are the
+    same as with the stop switched on."""
+    rng = np.random.default_rng(3)
+    n, C, V = 2, 32, 100
+    args = (rng.random(n * C) * 0.01, rng.integers(0, V, n * C), rng.integers(0, V, n * C),
+            rng.random(n * C), n, C, V)
+    state = (rng.integers(0, V, n * C), rng.integers(0, V, n * C), rng.random(n * C),
+             (rng.random(n * C) < 0.3).astype(np.uint8), np.array([5, 7]))
+    on = osm.lite_step(*args, 0.2, 1, 8, 2, *state)
+    off = osm.lite_step(*args, 0.2, 0, 8, 2, *state)
+    assert np.all(on.converged == 1) and np.all(off.converged == 0)
+    assert np.array_equal(off.stable_count, [5, 7])
+    for k in ("x", "committed", "final", "prev_argmax", "prev_conf"):
+        assert np.array_equal(getattr(on, k), getattr(off, k)), k

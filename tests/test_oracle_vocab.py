@@ -289,3 +289,16 @@ def test_temperature_schedule_endpoints():
     assert np.allclose(np.diff(ts), -0.4 / N, atol=1e-15)
     with pytest.raises(ValueError):
         vp.temperature_schedule(N, N, 0.8, 0.4)
+
+
+def test_confidence_closed_forms():
+    """conf = p of the argmax token: 1 / V for equal logits, the top level's probability for
+    two-level logits."""
+    wl = synth.workload("tiny", V=500, d=32)
+    r = _run(wl.E, np.zeros((2, 32), np.uint16), T=0.7)
+    assert np.allclose(r.conf, 1.0 / 500, rtol=1e-12)
+    V, k, a, b, T = 400, 3, 3.0, 0.5, 0.8
+    Eb, hb = _two_level(V, k, a, b)
+    r = _run(Eb, hb, T=T)
+    Z = k * math.exp(a / T) + (V - k) * math.exp(b / T)
+    assert abs(r.conf[0] - math.exp(a / T) / Z) < 1e-14
