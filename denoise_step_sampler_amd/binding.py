@@ -21,7 +21,7 @@ DG_CANVAS = 256
 
 EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_vocab_pass_softcap",
             "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
-            "dg_selfcond_input", "dg_status_string", "dg_last_error")
+            "dg_selfcond_input", "dg_lite_step", "dg_status_string", "dg_last_error")
 
 
 class DGError(RuntimeError):
@@ -58,6 +58,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_selfcond_input_workspace_size.restype = SZ
     lib.dg_selfcond_input.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, P, P, SZ, P]
     lib.dg_selfcond_input.restype = I
+    lib.dg_lite_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, F, I, U64, P, P, P, P, P,
+                                 P, P, P, P, P, P]
+    lib.dg_lite_step.restype = I
     lib.dg_status_string.argtypes = [I]
     lib.dg_status_string.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -214,4 +217,33 @@ def dg_selfcond_input(sc: Optional[torch.Tensor], tokens: torch.Tensor, E: torch
         n_canvas, C, V, D, F, ctypes.c_float(eps),
         _bf16_ptr(out, R * D, "out"),
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream))
+    _check(st)
+
+
+def dg_lite_step(h: torch.Tensor, E: torch.Tensor, temperature: torch.Tensor, lse: torch.Tensor,
+                 entropy: torch.Tensor, argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                 n_canvas: int, C: int, V: int, d: int, softcap: float, entropy_threshold: float,
+                 stability_steps: int, seed: int, step: torch.Tensor, conf: torch.Tensor,
+                 x: torch.Tensor, prev_argmax: torch.Tensor, prev_conf: torch.Tensor,
+                 committed: torch.Tensor, stable_count: torch.Tensor,
+                 final_tokens: Optional[torch.Tensor], converged: torch.Tensor,
+                 mean_entropy: Optional[torch.Tensor], stream=None) -> None:
+    R = n_canvas * C
+    lib = load()
+    st = lib.dg_lite_step(
+        _bf16_ptr(h, R * d, "h"), _bf16_ptr(E, V * d, "E"),
+        _ptr(temperature, torch.float32, n_canvas, "temperature"),
+        _ptr(lse, torch.float32, R, "lse"), _ptr(entropy, torch.float32, R, "entropy"),
+        _ptr(argmax_tok, torch.int32, R, "argmax_tok"),
+        _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
+        n_canvas, C, V, d, ctypes.c_float(softcap), ctypes.c_float(entropy_threshold),
+        stability_steps, ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(step, torch.int32, n_canvas, "step"), _ptr(conf, torch.float32, R, "conf"),
+        _ptr(x, torch.int32, R, "x"), _ptr(prev_argmax, torch.int32, R, "prev_argmax"),
+        _ptr(prev_conf, torch.float32, R, "prev_conf"),
+        _ptr(committed, torch.uint8, R, "committed"),
+        _ptr(stable_count, torch.int32, n_canvas, "stable_count"),
+        _ptr(final_tokens, torch.int32, R, "final_tokens"),
+        _ptr(converged, torch.uint8, n_canvas, "converged"),
+        _ptr(mean_entropy, torch.float32, n_canvas, "mean_entropy"), _stream(stream))
     _check(st)

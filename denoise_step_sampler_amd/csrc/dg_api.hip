@@ -254,6 +254,57 @@ dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
   return DG_OK;
 }
 
+dg_status dg_lite_step(const uint16_t* h, const uint16_t* E, const float* temperature,
+                       const float* lse, const float* entropy, const int32_t* argmax_tok,
+                       const int32_t* gumbel_tok, int n_canvas, int C, int V, int d,
+                       float softcap, float entropy_threshold, int stability_steps,
+                       uint64_t seed, const int32_t* step, float* conf, int32_t* x,
+                       int32_t* prev_argmax, float* prev_conf, uint8_t* committed,
+                       int32_t* stable_count, int32_t* final_tokens, uint8_t* converged,
+                       float* mean_entropy, void* stream) {
+  g_err[0] = 0;
+  dg_status s = check_vocab_shape(n_canvas, C, V, d);
+  if (s != DG_OK) return s;
+  if (!h || !E || !temperature || !lse || !entropy || !argmax_tok || !gumbel_tok || !step ||
+      !conf || !x || !prev_argmax || !prev_conf || !committed || !stable_count || !converged)
+    return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(h) || !aligned16(E))
+    return fail(DG_ERR_INVALID_ARG, "h and E must be 16-byte aligned");
+  if (!(softcap >= 0.0f) || !isfinite(softcap))
+    return fail(DG_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+  if (!isfinite(entropy_threshold))
+    return fail(DG_ERR_INVALID_ARG, "entropy_threshold must be finite");
+  if (stability_steps < 0) return fail(DG_ERR_INVALID_ARG, "stability_steps must be >= 0");
+  dg::LiteArgs a{};
+  a.h = h;
+  a.E = E;
+  a.temperature = temperature;
+  a.lse = lse;
+  a.entropy = entropy;
+  a.argmax_tok = argmax_tok;
+  a.gumbel_tok = gumbel_tok;
+  a.R = n_canvas * C;
+  a.V = V;
+  a.d = d;
+  a.softcap = softcap;
+  a.threshold = entropy_threshold;
+  a.stability_steps = stability_steps;
+  split_seed(seed, &a.k0, &a.k1);
+  a.step = step;
+  a.conf = conf;
+  a.x = x;
+  a.prev_argmax = prev_argmax;
+  a.prev_conf = prev_conf;
+  a.committed = committed;
+  a.stable_count = stable_count;
+  a.final_tokens = final_tokens;
+  a.converged = converged;
+  a.mean_entropy = mean_entropy;
+  const hipError_t e = dg::lite_step_launch(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "lite sampler launch");
+  return DG_OK;
+}
+
 size_t dg_selfcond_input_workspace_size(int n_canvas, int C, int D, int F) {
   char keep[sizeof(g_err)];
   memcpy(keep, g_err, sizeof(g_err));

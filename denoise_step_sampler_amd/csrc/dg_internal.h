@@ -140,6 +140,33 @@ struct FfwPlan {
 FfwPlan ffw_plan(int n_canvas, int D, int F);
 hipError_t ffw_launch(const FfwArgs& a, const FfwPlan& p, void* workspace, hipStream_t stream);
 
+// DiffusionGemma-Lite sampler step (lite_sampler.hip).
+struct LiteArgs {
+  const uint16_t* h;
+  const uint16_t* E;
+  const float* temperature;
+  const float* lse;
+  const float* entropy;
+  const int32_t* argmax_tok;
+  const int32_t* gumbel_tok;
+  int R, V, d;
+  float softcap;      // 0: none
+  float threshold;
+  int stability_steps;  // 0: adaptive stop off
+  uint32_t k0, k1;
+  const int32_t* step;
+  float* conf;
+  int32_t* x;
+  int32_t* prev_argmax;
+  float* prev_conf;
+  uint8_t* committed;
+  int32_t* stable_count;
+  int32_t* final_tokens;
+  uint8_t* converged;
+  float* mean_entropy;
+};
+hipError_t lite_step_launch(const LiteArgs& a, hipStream_t stream);
+
 hipError_t q_sample_launch(const int32_t* x0, int n_canvas, int V, const float* kappa,
                            uint32_t k0, uint32_t k1, int32_t* xt, hipStream_t stream);
 

@@ -131,6 +131,45 @@ def selfcond_input(b: VocabBuffers, W: FfwWeights, out: torch.Tensor, workspace:
                         W.eps, out, workspace, stream=stream)
 
 
+@dataclass
+class LiteState:
+    """State and outputs of the DiffusionGemma-Lite sampler for a batch of canvases."""
+    x: torch.Tensor
+    prev_argmax: torch.Tensor
+    prev_conf: torch.Tensor
+    committed: torch.Tensor
+    stable_count: torch.Tensor
+    conf: torch.Tensor
+    final_tokens: torch.Tensor
+    converged: torch.Tensor
+    mean_entropy: torch.Tensor
+
+
+def lite_state(n_canvas: int, device="cuda") -> LiteState:
+    """The initial state: no previous posterior (prev_argmax -1, prev_conf +inf), nothing
+    committed, canvas tokens 0 (every position is redrawn at the first step)."""
+    R = n_canvas * B.DG_CANVAS
+    i32 = dict(dtype=torch.int32, device=device)
+    return LiteState(x=torch.zeros(R, **i32), prev_argmax=torch.full((R,), -1, **i32),
+                     prev_conf=torch.full((R,), float("inf"), dtype=torch.float32, device=device),
+                     committed=torch.zeros(R, dtype=torch.uint8, device=device),
+                     stable_count=torch.zeros(n_canvas, **i32),
+                     conf=torch.empty(R, dtype=torch.float32, device=device),
+                     final_tokens=torch.empty(R, **i32),
+                     converged=torch.zeros(n_canvas, dtype=torch.uint8, device=device),
+                     mean_entropy=torch.empty(n_canvas, dtype=torch.float32, device=device))
+
+
+def lite_step(b: VocabBuffers, s: LiteState, threshold: float, stability_steps: int, seed: int,
+              softcap: Optional[float] = None, stream=None) -> None:
+    """The Lite sampler on the outputs of the vocabulary pass in b."""
+    B.dg_lite_step(b.h, b.E, b.temperature, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok,
+                   b.n_canvas, b.C, b.V, b.d, 0.0 if softcap is None else softcap, threshold,
+                   stability_steps, seed, b.step, s.conf, s.x, s.prev_argmax, s.prev_conf,
+                   s.committed, s.stable_count, s.final_tokens, s.converged, s.mean_entropy,
+                   stream=stream)
+
+
 def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:
     """Temperature of decode pass i of N (0 <= i < N): linear from t_max toward t_min in steps
     of (t_min - t_max) / N (DiffusionGemma Explained, "Sampling" -> "Apply temperature")."""

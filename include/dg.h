@@ -143,6 +143,40 @@ dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
                             uint8_t* accept_mask, uint8_t* converged, float* mean_entropy,
                             void* stream);
 
+/* dg_lite_step -- the DiffusionGemma-Lite sampler step, a second sampler on the vocabulary
+ * pass outputs ([LITE] sec. 4.2 "The commit rule", sec. 4.4 "Entropy-bounded adaptive
+ * stopping").  Per row r of canvas c, with conf_r the probability of the argmax token under
+ * the step's tempered distribution, exp(z_am - lse_r), z_am = cap(h_r . E[am]) / T_c
+ * (cap(S) = softcap tanh(S / softcap), or S when softcap == 0):
+ *   commit = (argmax_tok == prev_argmax) || (conf >= prev_conf)   (unchanged-or-stronger)
+ *   fresh  = commit && !committed                                 (frozen tokens stay)
+ *   x      = fresh ? gumbel_tok : committed ? x : uniform token of the renoise counter
+ *            (r, step[c]);  committed |= fresh;  prev_argmax = argmax_tok;  prev_conf = conf
+ *   final_tokens = committed ? x : gumbel_tok                       (the returned canvas)
+ * and per canvas the fp64 mean entropy m: with stability_steps > 0, stable_count = m <
+ * entropy_threshold ? stable_count + 1 : 0 and converged = stable_count >= stability_steps;
+ * with stability_steps == 0 (adaptive stop off) converged = 0 and stable_count is untouched.
+ * Initial state (no previous posterior, nothing commits at the first step): prev_argmax = -1,
+ * prev_conf = +inf, committed = 0, stable_count = 0.
+ *  h, E, temperature, lse, entropy, argmax_tok, gumbel_tok: the vocabulary pass's inputs and
+ *            outputs of the step (lse, entropy, gumbel_tok of every row must be written: no
+ *            commit canvases); softcap: the value given to dg_vocab_pass_softcap, else 0.
+ *  entropy_threshold finite; stability_steps >= 0.
+ *  conf      [R] fp32 out.   x, prev_argmax [R] int32 in/out; prev_conf [R] fp32 in/out;
+ *  committed [R] uint8 in/out; stable_count [n_canvas] in/out; final_tokens [R] out or NULL;
+ *  converged [n_canvas] uint8 out; mean_entropy [n_canvas] fp32 out or NULL.
+ *  h and E 16-byte aligned.  An argmax outside [0, V) gives conf = NaN (never commits by the
+ *  confidence test).
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+dg_status dg_lite_step(const uint16_t* h, const uint16_t* E, const float* temperature,
+                       const float* lse, const float* entropy, const int32_t* argmax_tok,
+                       const int32_t* gumbel_tok, int n_canvas, int C, int V, int d,
+                       float softcap, float entropy_threshold, int stability_steps,
+                       uint64_t seed, const int32_t* step, float* conf, int32_t* x,
+                       int32_t* prev_argmax, float* prev_conf, uint8_t* committed,
+                       int32_t* stable_count, int32_t* final_tokens, uint8_t* converged,
+                       float* mean_entropy, void* stream);
+
 /* dg_q_sample -- closed-form forward corruption ([TR] sec. 2.1.1 eq. (1); [LITE] forward
  * process, one draw, never iterating the chain): row r of canvas c keeps x0[r] iff
  * (w0 >> 8) < floor(kappa[c] * 2^24), else takes the uniform token of w1, with (w0, w1)

@@ -1,0 +1,91 @@
+"""The DiffusionGemma-Lite sampler through the C ABI: several denoise steps of vocabulary pass +
+dg_lite_step on the GPU against the oracle's vocabulary pass + lite_step, each side carrying
+its own state from the same initial state.  Hidden states of step k keep the signal at the
+positions the oracle had committed (so both sides see the same inputs).  Every step's
+confidences (|delta| <= 2e-3 |ref| + 1e-6), commit masks, canvas tokens, returned canvas,
+stop counters and flags must agree bit for bit, except decisions whose oracle margin is below
+1e-4 (|conf - prev_conf| for the commit test, |mean H - threshold| for the stop test,
+argmax / Gumbel margins): the comparison stops at the first such decision that differs,
+after which the two trajectories may legitimately part."""
+import sys
+
+import numpy as np
+import pytest
+
+from denoise_step_sampler_amd import synth
+from oracle import sampler as osm
+from oracle import vocab_pass as ovp
+from parity import MARGIN
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+C = 256
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from denoise_step_sampler_amd import binding
+    binding.load()
+    yield
+
+
+@pytest.mark.parametrize("softcap,stability,thr", [(None, 2, 7.5), (20.0, 0, 6.0)])
+def test_lite_sampler_loop(softcap, stability, thr):
+    """Stop switched on with a threshold between the canvases' mean entropies (two canvases
+    stop), and switched off with a soft cap."""
+    from denoise_step_sampler_amd import runner
+    wl = synth.workload("full_loop", V=4096, d=256, n_canvas=4, seed=3)
+    n, V, d = 4, wl.V, wl.d
+    wl.temperature = np.linspace(0.6, 1.0, n).astype(np.float32)
+    E64 = ovp.widen_bf16(wl.E)
+    E_t = runner.bf16_tensor(wl.E)
+    seed, steps = 12, 8
+    st = runner.lite_state(n)
+    o = dict(x=np.zeros(n * C, np.int64), pa=np.full(n * C, -1), pc=np.full(n * C, np.inf),
+             cm=np.zeros(n * C, np.uint8), cnt=np.zeros(n, np.int64))
+    b = None
+    compared = 0
+    for k in range(steps):
+        h = synth.loop_hidden(wl, k, o["cm"].astype(bool) if k else None)
+        if b is None:
+            b = runner.allocate(n, V, d, E_t, runner.bf16_tensor(h), wl.temperature, None,
+                                np.full(n, k, np.int32))
+        else:
+            b.h.copy_(runner.bf16_tensor(h))
+            b.step.fill_(k)
+        runner.vocab_pass(b, seed, softcap=softcap)
+        runner.lite_step(b, st, thr, stability, seed, softcap=softcap)
+        torch.cuda.synchronize()
+        ref = ovp.vocab_pass_rows(E64, h, np.arange(n * C), np.repeat(wl.temperature, C),
+                                  np.zeros(n * C, bool), seed, np.full(n * C, k), want_sc=False,
+                                  softcap=softcap)
+        r = osm.lite_step(ref.entropy, ref.argmax, ref.gumbel, ref.conf, n, C, V, thr,
+                          stability, seed, k, o["x"], o["pa"], o["pc"], o["cm"], o["cnt"])
+        conf = st.conf.cpu().numpy()
+        assert np.all(np.abs(conf - ref.conf) <= 2e-3 * ref.conf + 1e-6), f"step {k}: conf"
+        tie = ((ref.mu_argmax < MARGIN) | (ref.mu_gumbel < MARGIN) | (r.mu_commit < MARGIN) |
+               np.repeat(r.mu_stop < MARGIN, C))
+        got = dict(x=st.x.cpu().numpy(), committed=st.committed.cpu().numpy(),
+                   final=st.final_tokens.cpu().numpy(), prev_argmax=st.prev_argmax.cpu().numpy())
+        diff = np.zeros(n * C, bool)
+        for key in got:
+            diff |= got[key] != getattr(r, key)
+        cdiff = (st.stable_count.cpu().numpy() != r.stable_count) | \
+                (st.converged.cpu().numpy() != r.converged)
+        if (diff & tie).any() or (cdiff & (r.mu_stop < MARGIN)).any():
+            _say(f"   step {k}: a margin-exempt decision differs; stopping the comparison")
+            break
+        assert not diff.any(), f"step {k}: rows {np.nonzero(diff)[0][:8]} differ"
+        assert not cdiff.any(), f"step {k}: stop counter differs"
+        compared += 1
+        _say(f"   step {k}: committed {int(r.committed.sum())}, mean H "
+             f"{np.round(r.mean_entropy, 3).tolist()}, stopped {r.converged.tolist()}")
+        o = dict(x=r.x, pa=r.prev_argmax, pc=r.prev_conf, cm=r.committed, cnt=r.stable_count)
+    assert compared >= 4
