@@ -21,7 +21,9 @@ DG_CANVAS = 256
 
 EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_vocab_pass_softcap",
             "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
-            "dg_selfcond_input", "dg_lite_step", "dg_status_string", "dg_last_error")
+            "dg_selfcond_input", "dg_lite_step", "dg_quantize_embedding_fp8",
+            "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8", "dg_status_string",
+            "dg_last_error")
 
 
 class DGError(RuntimeError):
@@ -61,6 +63,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_lite_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, F, I, U64, P, P, P, P, P,
                                  P, P, P, P, P, P]
     lib.dg_lite_step.restype = I
+    lib.dg_quantize_embedding_fp8.argtypes = [P, I, I, P, P, P]
+    lib.dg_quantize_embedding_fp8.restype = I
+    lib.dg_vocab_pass_fp8_workspace_size.argtypes = [I, I, I, I]
+    lib.dg_vocab_pass_fp8_workspace_size.restype = SZ
+    lib.dg_vocab_pass_fp8.argtypes = [P, P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P,
+                                      F]
+    lib.dg_vocab_pass_fp8.restype = I
     lib.dg_status_string.argtypes = [I]
     lib.dg_status_string.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -246,4 +255,42 @@ def dg_lite_step(h: torch.Tensor, E: torch.Tensor, temperature: torch.Tensor, ls
         _ptr(final_tokens, torch.int32, R, "final_tokens"),
         _ptr(converged, torch.uint8, n_canvas, "converged"),
         _ptr(mean_entropy, torch.float32, n_canvas, "mean_entropy"), _stream(stream))
+    _check(st)
+
+
+def dg_quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, codes: torch.Tensor,
+                              row_exp: torch.Tensor, stream=None) -> None:
+    lib = load()
+    _check(lib.dg_quantize_embedding_fp8(_bf16_ptr(E, V * d, "E"), V, d,
+                                         _ptr(codes, torch.uint8, V * d, "codes"),
+                                         _ptr(row_exp, torch.int32, V, "row_exp"),
+                                         _stream(stream)))
+
+
+def dg_vocab_pass_fp8_workspace_size(n_canvas: int, C: int, V: int, d: int) -> int:
+    return int(load().dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d))
+
+
+def dg_vocab_pass_fp8(codes: torch.Tensor, row_exp: torch.Tensor, h: torch.Tensor, n_canvas: int,
+                      C: int, V: int, d: int, temperature: torch.Tensor,
+                      commit: Optional[torch.Tensor], seed: int, step: torch.Tensor,
+                      lse: Optional[torch.Tensor], entropy: torch.Tensor,
+                      argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                      selfcond: Optional[torch.Tensor], workspace: torch.Tensor, stream=None,
+                      softcap: float = 0.0) -> None:
+    R = n_canvas * C
+    lib = load()
+    st = lib.dg_vocab_pass_fp8(
+        _ptr(codes, torch.uint8, V * d, "codes"), _ptr(row_exp, torch.int32, V, "row_exp"),
+        _bf16_ptr(h, R * d, "h"), n_canvas, C, V, d,
+        _ptr(temperature, torch.float32, n_canvas, "temperature"),
+        _ptr(commit, torch.uint8, n_canvas, "commit"),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(step, torch.int32, n_canvas, "step"), _ptr(lse, torch.float32, R, "lse"),
+        _ptr(entropy, torch.float32, R, "entropy"),
+        _ptr(argmax_tok, torch.int32, R, "argmax_tok"),
+        _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
+        _ptr(selfcond, torch.float32, R * d, "selfcond"),
+        _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream),
+        ctypes.c_float(softcap))
     _check(st)

@@ -49,6 +49,11 @@ Path pick_path(int d, int* n_wg) {
   return dg::gemm_supported(d) ? kGemm : kSplit;
 }
 
+// Bytes of the two-GEMM workspace before the FP8 pass's dequantised rows.
+size_t fp8_offset(int n_canvas, int V, int d) {
+  return (dg::gemm_plan(n_canvas, V, d).bytes + 255) & ~(size_t)255;
+}
+
 size_t plan_bytes(int n_canvas, int V, int d) {
   int n_wg = 0;
   switch (pick_path(d, &n_wg)) {
@@ -131,20 +136,22 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
                      const float* temperature, const uint8_t* commit, uint64_t seed,
                      const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
-                     size_t workspace_bytes, void* stream, float softcap) {
-  g_err[0] = 0;
+                     size_t workspace_bytes, void* stream, float softcap,
+                     bool force_gemm = false) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
     return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (softcap != 0.0f && !dg::gemm_supported(d))
-    return fail(DG_ERR_UNSUPPORTED, "the soft cap needs d %% 128 == 0 (d=%d)", d);
+  if (softcap != 0.0f) force_gemm = true;
+  if (force_gemm && !dg::gemm_supported(d))
+    return fail(DG_ERR_UNSUPPORTED, "the soft cap and the FP8 embedding need d %% 128 == 0 (d=%d)",
+                d);
   if (!aligned16(E) || !aligned16(h))
     return fail(DG_ERR_INVALID_ARG, "E and h must be 16-byte aligned");
   if (selfcond && !aligned16(selfcond))
     return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
   const size_t need =
-      softcap != 0.0f ? dg::gemm_plan(n_canvas, V, d).bytes : plan_bytes(n_canvas, V, d);
+      force_gemm ? dg::gemm_plan(n_canvas, V, d).bytes : plan_bytes(n_canvas, V, d);
   if (!workspace || workspace_bytes < need)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -168,7 +175,7 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.softcap = softcap;
   int n_wg = 0;
   hipError_t e;
-  switch (softcap != 0.0f ? kGemm : pick_path(d, &n_wg)) {
+  switch (force_gemm ? kGemm : pick_path(d, &n_wg)) {
     case kGemm:
       e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, (hipStream_t)stream);
       break;
@@ -194,6 +201,7 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
                         const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
                         int32_t* gumbel_tok, float* selfcond, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, 0.0f);
 }
@@ -209,6 +217,59 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
     return fail(DG_ERR_INVALID_ARG, "softcap must be finite and > 0");
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap);
+}
+
+size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {
+  char keep[sizeof(g_err)];
+  memcpy(keep, g_err, sizeof(g_err));
+  const dg_status s = check_vocab_shape(n_canvas, C, V, d);
+  memcpy(g_err, keep, sizeof(g_err));
+  if (s != DG_OK || !dg::gemm_supported(d)) return 0;
+  return fp8_offset(n_canvas, V, d) + (((size_t)V * d * 2 + 255) & ~(size_t)255);
+}
+
+dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
+                                    int32_t* row_exp, void* stream) {
+  g_err[0] = 0;
+  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
+  if (d < 64 || d > DG_MAX_D || d % 64 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 64 in [64, %d]", d, DG_MAX_D);
+  if (!E || !codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(E) || !aligned16(codes))
+    return fail(DG_ERR_INVALID_ARG, "E and codes must be 16-byte aligned");
+  const hipError_t e = dg::fp8_quantize_launch(E, V, d, codes, row_exp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  return DG_OK;
+}
+
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const uint16_t* h,
+                            int n_canvas, int C, int V, int d, const float* temperature,
+                            const uint8_t* commit, uint64_t seed, const int32_t* step,
+                            float* lse, float* entropy, int32_t* argmax_tok,
+                            int32_t* gumbel_tok, float* selfcond, void* workspace,
+                            size_t workspace_bytes, void* stream, float softcap) {
+  g_err[0] = 0;
+  dg_status s = check_vocab_shape(n_canvas, C, V, d);
+  if (s != DG_OK) return s;
+  if (!dg::gemm_supported(d))
+    return fail(DG_ERR_UNSUPPORTED, "the FP8 embedding needs d %% 128 == 0 (d=%d)", d);
+  if (!codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(codes)) return fail(DG_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
+    return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
+  const size_t need = dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  // the dequantised rows (exact bf16) go to the end of the workspace, the pass uses the rest
+  const size_t off = fp8_offset(n_canvas, V, d);
+  uint16_t* Eq = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + off);
+  const hipError_t e = dg::fp8_dequantize_launch(codes, row_exp, V, d, Eq, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 dequantize launch");
+  return vocab_pass(Eq, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, workspace, off, stream, softcap, true);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

@@ -167,6 +167,12 @@ struct LiteArgs {
 };
 hipError_t lite_step_launch(const LiteArgs& a, hipStream_t stream);
 
+// FP8 embedding (fp8.hip): E4M3 codes with one power-of-two scale per row.
+hipError_t fp8_quantize_launch(const uint16_t* E, int V, int d, uint8_t* codes, int32_t* kexp,
+                               hipStream_t stream);
+hipError_t fp8_dequantize_launch(const uint8_t* codes, const int32_t* kexp, int V, int d,
+                                 uint16_t* E, hipStream_t stream);
+
 hipError_t q_sample_launch(const int32_t* x0, int n_canvas, int V, const float* kappa,
                            uint32_t k0, uint32_t k1, int32_t* xt, hipStream_t stream);
 

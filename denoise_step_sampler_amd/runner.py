@@ -170,6 +170,36 @@ def lite_step(b: VocabBuffers, s: LiteState, threshold: float, stability_steps: 
                    stream=stream)
 
 
+@dataclass
+class Fp8Embedding:
+    """The FP8 form of an embedding on the device: E4M3 codes and per-row exponents."""
+    codes: torch.Tensor
+    row_exp: torch.Tensor
+
+
+def quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, stream=None) -> Fp8Embedding:
+    f = Fp8Embedding(codes=torch.empty(V * d, dtype=torch.uint8, device=E.device),
+                     row_exp=torch.empty(V, dtype=torch.int32, device=E.device))
+    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.row_exp, stream=stream)
+    return f
+
+
+def fp8_workspace(n_canvas: int, V: int, d: int, device="cuda") -> torch.Tensor:
+    n = B.dg_vocab_pass_fp8_workspace_size(n_canvas, B.DG_CANVAS, V, d)
+    if n == 0:
+        raise ValueError(f"unsupported shape n={n_canvas} V={V} d={d}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def vocab_pass_fp8(b: VocabBuffers, f: Fp8Embedding, workspace: torch.Tensor, seed: int,
+                   stream=None, softcap: Optional[float] = None) -> None:
+    """The vocabulary pass on the FP8 embedding f (b.E is not read)."""
+    B.dg_vocab_pass_fp8(f.codes, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+                        b.commit, seed, b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok,
+                        b.selfcond, workspace, stream=stream,
+                        softcap=0.0 if softcap is None else softcap)
+
+
 def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:
     """Temperature of decode pass i of N (0 <= i < N): linear from t_max toward t_min in steps
     of (t_min - t_max) / N (DiffusionGemma Explained, "Sampling" -> "Apply temperature")."""

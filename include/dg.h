@@ -112,6 +112,35 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 float softcap);
 
+/* dg_quantize_embedding_fp8 -- the tied embedding as FP8 ([VLLM] ships an FP8 checkpoint with
+ * quantised weights; the pages give no scale scheme): OCP E4M3 codes (bias 7, largest finite
+ * 448, no infinities) with one power-of-two scale 2^k per row,
+ *   k_v = the smallest integer >= -117 with max_j |E_vj| <= 448 * 2^k_v (-117 for a zero row)
+ *   codes_vj = the E4M3 value nearest to E_vj / 2^k_v, ties to the even code (zero -> 0x00).
+ * A power-of-two scale makes every dequantised value 2^k * value(code) an exact bf16 number.
+ *  E        [V, d] bf16, finite, |E| < 2^127.   d % 64 == 0, 64 <= d <= DG_MAX_D.
+ *  codes    [V, d] uint8 out;  row_exp [V] int32 out.  E and codes 16-byte aligned.
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
+                                    int32_t* row_exp, void* stream);
+
+/* dg_vocab_pass_fp8_workspace_size -- bytes of workspace dg_vocab_pass_fp8 needs ([host],
+ * pure): the two-GEMM workspace plus V * d bf16 for the dequantised rows.  0 if unsupported. */
+size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d);
+
+/* dg_vocab_pass_fp8 -- dg_vocab_pass (dg_vocab_pass_softcap when softcap > 0) on the FP8
+ * embedding (codes, row_exp) of dg_quantize_embedding_fp8: the embedding is
+ * E~_vj = 2^row_exp[v] * value(codes_vj), dequantised exactly to bf16 into the workspace,
+ * then the logits, statistics, samples and self-conditioning expectation are those of E~.
+ * Runs on the two-GEMM path (d % 128 == 0, else DG_ERR_UNSUPPORTED).  softcap: 0 (none) or
+ * finite > 0.  Other arguments, outputs and errors as dg_vocab_pass; codes 16-byte aligned. */
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const uint16_t* h,
+                            int n_canvas, int C, int V, int d, const float* temperature,
+                            const uint8_t* commit, uint64_t seed, const int32_t* step,
+                            float* lse, float* entropy, int32_t* argmax_tok,
+                            int32_t* gumbel_tok, float* selfcond, void* workspace,
+                            size_t workspace_bytes, void* stream, float softcap);
+
 /* dg_accept_renoise -- per-canvas acceptance, renoising and convergence of one step.
  *
  * For a canvas that does not commit ([TR] sec. 3.3 "Entropy-bounded token refinement",

@@ -31,7 +31,8 @@ def test_header_symbols_exported():
     assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass",
                          "dg_vocab_pass_softcap", "dg_accept_renoise", "dg_q_sample",
                          "dg_selfcond_input_workspace_size", "dg_selfcond_input",
-                         "dg_lite_step",
+                         "dg_lite_step", "dg_quantize_embedding_fp8",
+                         "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8",
                          "dg_status_string", "dg_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout

@@ -29,8 +29,9 @@ def test_rounding_ties_and_round_trip():
 
 
 def test_row_exponent_boundaries():
-    a = np.array([448.0, 448.0000001, 224.0, 224.0000001, 1.0, 0.0, 448.0 * 2.0 ** -20])
-    assert list(fp8.row_exponent(a)) == [0, 1, -1, 0, -8, -127, -20]
+    a = np.array([448.0, 448.0000001, 224.0, 224.0000001, 1.0, 0.0, 448.0 * 2.0 ** -20,
+                  2.0 ** -120])
+    assert list(fp8.row_exponent(a)) == [0, 1, -1, 0, -8, -117, -20, -117]
 
 
 def test_quantized_rows_error_and_bf16_exactness():
@@ -38,12 +39,16 @@ def test_quantized_rows_error_and_bf16_exactness():
     Ef = synth.bf16_to_f32(E).astype(np.float64)
     Ef[7] = 0.0
     Ef[8] *= 1e-30
+    Ef[9] *= 2.0 ** -140          # below the exponent floor: coarser codes, still exact
     q, k = fp8.quantize_rows(Ef)
     D = fp8.dequantize_rows(q, k)
     amax = np.max(np.abs(Ef), axis=1)
     for v in range(300):
         if amax[v] == 0:
             assert np.all(D[v] == 0)
+            continue
+        if k[v] == fp8.K_MIN:
+            assert amax[v] <= 448.0 * 2.0 ** k[v]
             continue
         # the row's largest entry lands in (224, 448] times the row scale (its code in
         # [224, 448]: values just above 224 round down to it)
