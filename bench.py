@@ -149,6 +149,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB MiB (counter calibration)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="run the step on the FP8 form of the embedding (dg_vocab_pass_fp8)")
     ap.add_argument("--softcap", type=float, default=None,
                     help="final-logit soft cap c (logits c tanh(S / c)); default: none")
     ap.add_argument("--ffw-F", type=int, default=2816, metavar="F",
@@ -180,10 +182,19 @@ def main() -> int:
     b = runner.from_workload(wl)
     stream = torch.cuda.current_stream()
     seed = args.seed
+    if args.fp8:
+        f8 = runner.quantize_embedding_fp8(b.E, wl.V, wl.d, stream=stream)
+        ws8 = runner.fp8_workspace(wl.n_canvas, wl.V, wl.d)
+
+    def vocab(k_stream):
+        if args.fp8:
+            runner.vocab_pass_fp8(b, f8, ws8, seed, k_stream, args.softcap)
+        else:
+            runner.vocab_pass(b, seed, k_stream, args.softcap)
 
     def step(k):
         b.step.fill_(k)
-        runner.vocab_pass(b, seed, stream, args.softcap)
+        vocab(stream)
         runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, stream)
 
     log(f"[bench] warmup {args.warmup}")
@@ -202,7 +213,7 @@ def main() -> int:
     for k in range(args.steps):
         b.step.fill_(args.warmup + k)
         ev[k][0].record(stream)
-        runner.vocab_pass(b, seed, stream, args.softcap)
+        vocab(stream)
         ev[k][1].record(stream)
         runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, stream)
     t_end.record(stream)
@@ -225,7 +236,10 @@ def main() -> int:
         ev2[k][0].record(stream)
         k1_args = (b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step,
                    b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, None, b.workspace)
-        if args.softcap is None:
+        if args.fp8:
+            B.dg_vocab_pass_fp8(f8.codes, f8.row_exp, *k1_args[1:-1], ws8, stream=stream,
+                                softcap=args.softcap or 0.0)
+        elif args.softcap is None:
             B.dg_vocab_pass(*k1_args, stream=stream)
         else:
             B.dg_vocab_pass_softcap(*k1_args, stream=stream, softcap=args.softcap)
@@ -276,7 +290,8 @@ def main() -> int:
         "config": {"workload": args.workload, "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
                    "d": wl.d, "commit_canvases": int(wl.commit.sum()),
                    "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget,
-                   "softcap": args.softcap},
+                   "softcap": args.softcap,
+                   "embedding": "fp8-e4m3, power-of-two row scales" if args.fp8 else "bf16"},
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "vocab_pass": {"avg_launch_ms": vp_avg, "algorithmic_flops": flops,
@@ -287,7 +302,7 @@ def main() -> int:
             "unit": "TFLOP/s", "frac": ach_k1 / PEAK_BF16_TFLOPS,
             # the counters were taken on the uncapped kernel
             "traffic": (measured_traffic(args.workload)
-                        if gemm_path and args.softcap is None else None),
+                        if gemm_path and args.softcap is None and not args.fp8 else None),
             "algorithmic_flops_per_launch": flops_k1, "avg_launch_ms": k1_ms},
     }
     if ffw is not None:
