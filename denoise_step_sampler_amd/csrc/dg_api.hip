@@ -137,7 +137,8 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
                      const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
                      size_t workspace_bytes, void* stream, float softcap,
-                     bool force_gemm = false) {
+                     bool force_gemm = false, const uint8_t* E8 = nullptr,
+                     const int32_t* E_exp = nullptr) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
@@ -173,6 +174,8 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.gumbel_tok = gumbel_tok;
   a.selfcond = selfcond;
   a.softcap = softcap;
+  a.E8 = E8;
+  a.E_exp = E_exp;
   int n_wg = 0;
   hipError_t e;
   switch (force_gemm ? kGemm : pick_path(d, &n_wg)) {
@@ -254,7 +257,8 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const 
   if (!dg::gemm_supported(d))
     return fail(DG_ERR_UNSUPPORTED, "the FP8 embedding needs d %% 128 == 0 (d=%d)", d);
   if (!codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(codes)) return fail(DG_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (!aligned16(codes) || !aligned16(row_exp))
+    return fail(DG_ERR_INVALID_ARG, "codes and row_exp must be 16-byte aligned");
   if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
     return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
   const size_t need = dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d);
@@ -263,13 +267,17 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const 
                 need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  // the dequantised rows (exact bf16) go to the end of the workspace, the pass uses the rest
+  // the logits pass streams the codes; the expectation pass reads the dequantised rows (exact
+  // bf16), written to the end of the workspace only when the expectation is asked for
   const size_t off = fp8_offset(n_canvas, V, d);
   uint16_t* Eq = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + off);
-  const hipError_t e = dg::fp8_dequantize_launch(codes, row_exp, V, d, Eq, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "fp8 dequantize launch");
+  if (selfcond != nullptr) {
+    const hipError_t e = dg::fp8_dequantize_launch(codes, row_exp, V, d, Eq, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fp8 dequantize launch");
+  }
   return vocab_pass(Eq, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
-                    argmax_tok, gumbel_tok, selfcond, workspace, off, stream, softcap, true);
+                    argmax_tok, gumbel_tok, selfcond, workspace, off, stream, softcap, true, codes,
+                    row_exp);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

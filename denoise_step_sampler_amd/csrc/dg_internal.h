@@ -25,6 +25,11 @@ struct VocabArgs {
   int32_t* gumbel_tok;
   float* selfcond;
   float softcap;  // > 0: z = softcap tanh(S / softcap) / T (two-GEMM path only); 0: z = S / T
+  // FP8 embedding for the logits pass (two-GEMM path): E4M3 codes [V, d] and row exponents
+  // [V], E = 2^E_exp[v] * value(codes); null: the logits pass reads E.  The expectation pass
+  // always reads E (bf16), which must then hold the same values.
+  const uint8_t* E8;
+  const int32_t* E_exp;
 };
 
 // Workspace carve-up.

@@ -49,6 +49,7 @@ namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 256;      // vocabulary tile of the logits pass (and rows per canvas)
 constexpr int kHalf = 128;      // granularity of the weight references
@@ -400,12 +401,26 @@ constexpr int kNst1 = 2;           // stages
 // so that the sixteen consecutive rows one ds_read_b128 pass serves fall on distinct banks.
 __device__ __forceinline__ int swz1(int r) { return (r >> 1) & 7; }
 
-template <bool kCap>
+// Eight E4M3 codes (two words) widened to eight bf16 (exact; v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1), in order.
+__device__ __forceinline__ u32x4 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
+#define DG_CV(w, hi) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi))
+  return u32x4{DG_CV(w0, false), DG_CV(w0, true), DG_CV(w1, false), DG_CV(w1, true)};
+#undef DG_CV
+}
+
+// kF8: E arrives as E4M3 codes with a power-of-two scale per row (g.a.E8, g.a.E_exp).  The
+// codes are staged as 64-byte rows; one 16-byte read gives a lane the codes of two 16-wide K
+// steps, widened to bf16 in registers; the h fragments use the same permutation of K within
+// the chunk (step 2 j + t, lane half f: K = 32 j + 16 f + 8 t + 0..7), and the accumulator of
+// entry v is scaled by 2^E_exp[v] before the epilogue (exact).
+template <bool kCap, bool kF8>
 __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
-  constexpr int kStage = 512 * kRow1;  // 256 E rows + 256 h rows
-  constexpr int kHOff = kTile * kRow1;
+  constexpr int kERow = kF8 ? kKC1 : kRow1;    // bytes of one staged E row
+  constexpr int kHOff = kTile * kERow;         // 256 E rows, then 256 h rows
+  constexpr int kStage = kHOff + kTile * kRow1;
   __shared__ __attribute__((aligned(1024))) char stg[kNst1][kStage];
-  const uint16_t* E = g.a.E;
+  const char* Eb = kF8 ? reinterpret_cast<const char*>(g.a.E8) : reinterpret_cast<const char*>(g.a.E);
   const uint16_t* h = g.a.h;
   const int V = g.a.V, d = g.a.d, n_canvas = g.a.n_canvas;
   const int t = threadIdx.x, lane = t & 63, fr = lane & 31, fh = lane >> 5;
@@ -428,28 +443,42 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   uint32_t rdE[4], rdH[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    rdE[ks] = (uint32_t)((128 * vh + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
-    rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
+    if (kF8) {
+      // code rows: 16-byte segment q of row r at q ^ ((r >> 2) & 3); reads j = 0, 1
+      rdE[ks] = (uint32_t)((128 * vh + fr) * kERow + 16 * (((2 * (ks & 1) + fh)) ^ ((fr >> 2) & 3)));
+      rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 +
+                           16 * ((4 * (ks >> 1) + 2 * fh + (ks & 1)) ^ sw));
+    } else {
+      rdE[ks] = (uint32_t)((128 * vh + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
+      rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 + 16 * ((2 * ks + fh) ^ sw));
+    }
   }
   // DMA: a copy moves 8 staged rows (1 KB); lane -> row 8 j + lane / 8, slot lane % 8,
   // global segment slot ^ swz1(row).  Wave w copies E rows and h rows [32 w, 32 w + 32) of
   // the stage, four copies each.  Sources: a wave-uniform base plus a 32-bit lane offset.
   const int dlrow = lane >> 3;
   const uint32_t pitch = 2u * (uint32_t)d;
+  const uint32_t epitch = kF8 ? (uint32_t)d : pitch;
   uint32_t offH[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     offH[j] = (uint32_t)(8 * j + dlrow) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
   const char* hb = reinterpret_cast<const char*>(h) + ((size_t)c * kTile + 32 * w) * pitch;
   // E rows of the wave's block of tile tt, clamped to V - 1: base row and lane offsets
+  // (code rows: two copies of 16 rows, lane -> row 16 j + lane / 4, segment lane % 4)
   auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[4]) {
     const int r0 = tt * kTile + 32 * w;
     const int rb = min(r0, V - 1);
-    eb = reinterpret_cast<const char*>(E) + (size_t)rb * pitch;
+    eb = Eb + (size_t)rb * epitch;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int rv = min(r0 + 8 * j + dlrow, V - 1);
-      oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
+      if (kF8) {
+        const int rv = min(r0 + 16 * (j & 1) + (lane >> 2), V - 1);
+        oe[j] = (uint32_t)(rv - rb) * epitch + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+      } else {
+        const int rv = min(r0 + 8 * j + dlrow, V - 1);
+        oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
+      }
     }
   };
   // copies of chunk kc into the stage at LDS address dst: the E rows of a tile whose source
@@ -457,9 +486,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   // wait for every copy in flight before the next read of LDS, the stages it cannot tell
   // apart)
   auto issue_e = [&](int kc, const char* eb, const uint32_t (&oe)[4], uint32_t dst) {
-    const uint32_t kb = (uint32_t)kc * (uint32_t)kRow1;
+    const uint32_t kb = (uint32_t)kc * (uint32_t)kERow;
+    if (kF8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(4 * w + j));
+      for (int j = 0; j < 2; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(2 * w + j));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma_asm(eb + kb, oe[j], dst + 1024u * (uint32_t)(4 * w + j));
+    }
   };
   auto issue_h = [&](int kc, uint32_t dst) {
     const uint32_t kb = (uint32_t)kc * (uint32_t)kRow1;
@@ -512,8 +546,48 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[1][mb], fb[1][nb], acc[mb][nb]);
   };
+  u32x4 c8[4];  // kF8: the codes of two K steps (E row block mb)
+  auto chunk8 = [&](auto deferred, const char* sc, uint32_t sn, int kn, const char* eb,
+                    const uint32_t (&oe)[4]) {
+    vm_wait<0>();
+    __syncthreads();
+    const lds_char* s = (const lds_char*)sc;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) c8[mb] = lds_read16(s + rdE[0] + 32 * kERow * mb);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) fb[0][nb] = lds_read16(s + rdH[0] + 32 * kRow1 * nb);
+    if (decltype(deferred)::value) last_step();
+    issue_e(kn, eb, oe, sn);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa[0][mb] = e4m3x8_bf16(c8[mb][0], c8[mb][1]);
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const int cb = ks & 1;
+      if (ks == 1) issue_h(kn, sn);
+      if (ks == 1) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) c8[mb] = lds_read16(s + rdE[1] + 32 * kERow * mb);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        fb[cb ^ 1][nb] = lds_read16(s + rdH[ks + 1] + 32 * kRow1 * nb);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[cb][mb], fb[cb][nb], acc[mb][nb]);
+      // A of step ks + 1: the other half of the codes in hand (ks even), or the next read's
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        fa[cb ^ 1][mb] = (ks & 1) ? e4m3x8_bf16(c8[mb][0], c8[mb][1])
+                                  : e4m3x8_bf16(c8[mb][2], c8[mb][3]);
+    }
+  };
   auto chunk = [&](auto deferred, const char* sc, uint32_t sn, int kn, const char* eb,
                    const uint32_t (&oe)[4]) {
+    if constexpr (kF8) {
+      chunk8(deferred, sc, sn, kn, eb, oe);
+      return;
+    }
     vm_wait<0>();
     __syncthreads();
     const lds_char* s = (const lds_char*)sc;
@@ -594,6 +668,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     for (int j = 0; j < 4; ++j) oe[j] = oen[j];
     // ---- epilogue of tile tt
     const int vt0 = tt * kTile + kHalf * vh;
+    if constexpr (kF8) {
+      // S = 2^E_exp[v] (sum h q): the lane's entries vt0 + 32 mb + 8 q + 4 (lane / 32) + 0..3
+      const int vl = vt0 + 4 * fh;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int vb = vl + 32 * mb + 8 * q;
+          int ke[4];
+          if (vt0 + kHalf <= V) {
+            const i32x4v k4 = *reinterpret_cast<const i32x4v*>(g.a.E_exp + vb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ke[j] = k4[j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ke[j] = g.a.E_exp[min(vb + j, V - 1)];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              acc[mb][nb][4 * q + j] = __builtin_amdgcn_ldexpf(acc[mb][nb][4 * q + j], ke[j]);
+        }
+    }
     int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
     const size_t vblk = (size_t)(vt0 >> 5) * 512;  // first 32-entry block of the half tile
     if (heavy) {
@@ -1216,12 +1314,17 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
                      pos, n_nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.softcap != 0.0f)
-    hipLaunchKernelGGL(k_gemm_logits<true>, dim3((unsigned)(kWG * p.n_rounds)), dim3(512), 0,
-                       stream, g);
-  else
-    hipLaunchKernelGGL(k_gemm_logits<false>, dim3((unsigned)(kWG * p.n_rounds)), dim3(512), 0,
-                       stream, g);
+  const dim3 grid1((unsigned)(kWG * p.n_rounds));
+  if (a.E8 != nullptr) {
+    if (a.softcap != 0.0f)
+      hipLaunchKernelGGL((k_gemm_logits<true, true>), grid1, dim3(512), 0, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm_logits<false, true>), grid1, dim3(512), 0, stream, g);
+  } else if (a.softcap != 0.0f) {
+    hipLaunchKernelGGL((k_gemm_logits<true, false>), grid1, dim3(512), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((k_gemm_logits<false, false>), grid1, dim3(512), 0, stream, g);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.selfcond != nullptr) {

@@ -130,10 +130,14 @@ size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d);
 
 /* dg_vocab_pass_fp8 -- dg_vocab_pass (dg_vocab_pass_softcap when softcap > 0) on the FP8
  * embedding (codes, row_exp) of dg_quantize_embedding_fp8: the embedding is
- * E~_vj = 2^row_exp[v] * value(codes_vj), dequantised exactly to bf16 into the workspace,
- * then the logits, statistics, samples and self-conditioning expectation are those of E~.
+ * E~_vj = 2^row_exp[v] * value(codes_vj), and the logits, statistics, samples and
+ * self-conditioning expectation are those of E~ (the logits pass streams the codes and scales
+ * each entry's sum by 2^row_exp[v], exact; the expectation pass, when selfcond is given,
+ * reads E~ dequantised exactly to bf16 into the workspace).  Results equal those of
+ * dg_vocab_pass on E~ up to the order of the fp32 accumulation within a K chunk.
  * Runs on the two-GEMM path (d % 128 == 0, else DG_ERR_UNSUPPORTED).  softcap: 0 (none) or
- * finite > 0.  Other arguments, outputs and errors as dg_vocab_pass; codes 16-byte aligned. */
+ * finite > 0.  Other arguments, outputs and errors as dg_vocab_pass; codes and row_exp
+ * 16-byte aligned. */
 dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,

@@ -1,7 +1,9 @@
 """The FP8 embedding through the C ABI: the quantiser's codes and exponents bit for bit against
 the oracle's, the vocabulary pass on the FP8 embedding against the oracle's pass on the
-oracle's dequantised rows, and bit-for-bit agreement with dg_vocab_pass on those rows (the
-power-of-two scales make the dequantised rows exact bf16 numbers)."""
+oracle's dequantised rows, and agreement with dg_vocab_pass on those rows (the power-of-two
+scales make the dequantised rows exact bf16 numbers; the logits pass on the codes sums the
+K positions of a chunk in another order, so the two agree to fp32 accumulation rounding)."""
+
 import sys
 
 import numpy as np
@@ -29,6 +31,22 @@ def _gpu():
     from denoise_step_sampler_amd import binding
     binding.load()
     yield
+
+
+def _agree(a, b, nc):
+    """Two passes over the same embedding values: tokens equal but for near-ties, statistics
+    within fp32 accumulation rounding, expectation rows within the 2e-3 bar."""
+    am = a.argmax_tok.cpu().numpy() == b.argmax_tok.cpu().numpy()
+    gm = (a.gumbel_tok.cpu().numpy() == b.gumbel_tok.cpu().numpy())[nc]
+    assert am.mean() > 0.999 and gm.mean() > 0.99, (am.mean(), gm.mean())
+    for key in ("lse", "entropy"):
+        x, y = getattr(a, key).cpu().numpy()[nc], getattr(b, key).cpu().numpy()[nc]
+        assert np.allclose(x, y, rtol=1e-4, atol=1e-6), key
+    if a.selfcond is not None:
+        x, y = a.selfcond.cpu().numpy()[nc], b.selfcond.cpu().numpy()[nc]
+        rel = np.linalg.norm(x - y, axis=1) / np.linalg.norm(y, axis=1)
+        assert rel.max() < 2e-3, rel.max()
+    return float(am.mean()), float(gm.mean())
 
 
 def _special_embedding(V, d, seed):
@@ -87,18 +105,23 @@ def test_fp8_vocab_pass_parity_and_bf16_identity(softcap):
            "argmax": b.argmax_tok.cpu().numpy(), "gumbel": b.gumbel_tok.cpu().numpy(),
            "sc": b.selfcond.cpu().numpy()}
     _say("   ", compare_vocab(out, ref, np.repeat(wl.commit.astype(bool), C)))
-    # the bf16 pass on the dequantised rows gives the same bits
+    # the bf16 pass on the dequantised rows
     b2 = runner.from_workload(wl, E=runner.bf16_tensor(Eq_bits))
     runner.vocab_pass(b2, seed, softcap=softcap)
     torch.cuda.synchronize()
-    for key in ("lse", "entropy", "argmax_tok", "gumbel_tok", "selfcond"):
-        x, y = getattr(b, key).cpu().numpy(), getattr(b2, key).cpu().numpy()
+    _say("    agreement with the bf16 pass:", _agree(b, b2, np.repeat(wl.commit == 0, C)))
+    # without the expectation the pass needs no dequantised copy
+    b3 = runner.from_workload(wl, want_selfcond=False)
+    runner.vocab_pass_fp8(b3, f, ws, seed, softcap=softcap)
+    torch.cuda.synchronize()
+    for key in ("lse", "entropy", "argmax_tok", "gumbel_tok"):
+        x, y = getattr(b, key).cpu().numpy(), getattr(b3, key).cpu().numpy()
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), key
 
 
 def test_fp8_full_size_batched():
     """V = 262144, d = 2816, 32 canvases: quantiser rows against the oracle on a sample, and the
-    FP8 pass bit for bit equal to the bf16 pass on the dequantised rows."""
+    FP8 pass against the bf16 pass on the dequantised rows."""
     from denoise_step_sampler_amd import runner
     _say("[vocab_pass_fp8] generating V=262144 d=2816 embedding")
     E = synth.make_embedding(262144, 2816, seed=0)
@@ -121,6 +144,4 @@ def test_fp8_full_size_batched():
     del Eq
     runner.vocab_pass(b2, 5)
     torch.cuda.synchronize()
-    for key in ("lse", "entropy", "argmax_tok", "gumbel_tok", "selfcond"):
-        x, y = getattr(b, key).cpu().numpy(), getattr(b2, key).cpu().numpy()
-        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), key
+    _say("    agreement with the bf16 pass:", _agree(b, b2, np.repeat(wl.commit == 0, C)))
