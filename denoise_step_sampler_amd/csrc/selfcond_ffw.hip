@@ -208,52 +208,66 @@ struct FfwRows {
   uint16_t* out;          // [R, D]
 };
 
-// x1 = bf16(w cx sqrt(D) / (||cx|| + eps)), cx = sc sqrt(D); one workgroup per row.
+// x1 = bf16(w cx sqrt(D) / (||cx|| + eps)), cx = sc sqrt(D); one workgroup per row, four
+// entries per thread and step (16-byte loads of sc, 8-byte loads of the weight and stores).
 __global__ __launch_bounds__(256) void k_ffw_prenorm(FfwRows a) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   if (a.commit != nullptr && a.commit[r / kRowsPerCanvas]) return;
-  const float* src = a.sc + (size_t)r * a.D;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.sc + (size_t)r * a.D);
+  const int n4 = a.D / 4;
   float ss = 0.0f;
-  for (int k = threadIdx.x; k < a.D; k += 256) {
-    const float cx = src[k] * a.scale;
-    ss += cx * cx;
+  for (int k = threadIdx.x; k < n4; k += 256) {
+    const f32x4 x = src[k] * a.scale;
+    ss += (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
   }
   const float n = sqrtf(block_sum256(ss, red));
   const float f = a.scale / (n + a.eps);
-  for (int k = threadIdx.x; k < a.D; k += 256) {
-    const float cx = src[k] * a.scale;
-    const float wv = __uint_as_float((uint32_t)a.pre_norm[k] << 16);
-    a.x1[(size_t)r * a.D + k] = (uint16_t)f32_to_bf16_bits(wv * (cx * f));
+  const u32x2* wp = reinterpret_cast<const u32x2*>(a.pre_norm);
+  u32x2* dst = reinterpret_cast<u32x2*>(a.x1 + (size_t)r * a.D);
+  for (int k = threadIdx.x; k < n4; k += 256) {
+    const f32x4 x = src[k] * a.scale;
+    const u32x2 w = wp[k];
+    const uint32_t lo = f32_to_bf16_bits(bf16_lo(w[0]) * (x[0] * f)) |
+                        (f32_to_bf16_bits(bf16_hi(w[0]) * (x[1] * f)) << 16);
+    const uint32_t hi = f32_to_bf16_bits(bf16_lo(w[1]) * (x[2] * f)) |
+                        (f32_to_bf16_bits(bf16_hi(w[1]) * (x[3] * f)) << 16);
+    dst[k] = u32x2{lo, hi};
   }
 }
 
-// out = bf16(x sqrt(D) / (||x|| + eps)), x = E[tok] sqrt(D) + res; one workgroup per row.  A
-// token outside [0, V) gives a row of NaN.
+// out = bf16(x sqrt(D) / (||x|| + eps)), x = E[tok] sqrt(D) + res; one workgroup per row, four
+// entries per thread and step.  A token outside [0, V) gives a row of NaN.
 __global__ __launch_bounds__(256) void k_ffw_out(FfwRows a) {
   __shared__ float red[4];
   const int r = blockIdx.x;
   if (a.commit != nullptr && a.commit[r / kRowsPerCanvas]) return;
   const int tok = a.tokens[r];
-  uint16_t* dst = a.out + (size_t)r * a.D;
+  const int n4 = a.D / 4;
+  u32x2* dst = reinterpret_cast<u32x2*>(a.out + (size_t)r * a.D);
   if (tok < 0 || tok >= a.V) {
-    for (int k = threadIdx.x; k < a.D; k += 256) dst[k] = 0x7FC0;
+    for (int k = threadIdx.x; k < n4; k += 256) dst[k] = u32x2{0x7FC07FC0u, 0x7FC07FC0u};
     return;
   }
-  const uint16_t* e = a.E + (size_t)tok * a.D;
-  const float* rs = a.res ? a.res + (size_t)r * a.D : nullptr;
-  float ss = 0.0f;
-  for (int k = threadIdx.x; k < a.D; k += 256) {
-    float x = __uint_as_float((uint32_t)e[k] << 16) * a.scale;
+  const u32x2* e = reinterpret_cast<const u32x2*>(a.E + (size_t)tok * a.D);
+  const f32x4* rs = a.res ? reinterpret_cast<const f32x4*>(a.res + (size_t)r * a.D) : nullptr;
+  auto load = [&](int k) {
+    const u32x2 w = e[k];
+    f32x4 x = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])} * a.scale;
     if (rs) x += rs[k];
-    ss += x * x;
+    return x;
+  };
+  float ss = 0.0f;
+  for (int k = threadIdx.x; k < n4; k += 256) {
+    const f32x4 x = load(k);
+    ss += (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
   }
   const float n = sqrtf(block_sum256(ss, red));
   const float f = a.scale / (n + a.eps);
-  for (int k = threadIdx.x; k < a.D; k += 256) {
-    float x = __uint_as_float((uint32_t)e[k] << 16) * a.scale;
-    if (rs) x += rs[k];
-    dst[k] = (uint16_t)f32_to_bf16_bits(x * f);
+  for (int k = threadIdx.x; k < n4; k += 256) {
+    const f32x4 x = load(k) * f;
+    dst[k] = u32x2{f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16),
+                   f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16)};
   }
 }
 
