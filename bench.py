@@ -92,8 +92,16 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
         rows_done += rows.size
         k += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    cpu_model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": rows_done / spent, "unit": "canvas-positions/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"{rows_done} non-commit positions (rows) of the {wl.name} workload, full vocabulary "
                       f"(logits, softmax, entropy, argmax, Gumbel, selfcond), fp64 numpy, "
                       f"{spent:.1f}s; bf16->fp64 widening of E ({widen_s:.1f}s) excluded"}
@@ -273,6 +281,30 @@ def main() -> int:
                "frac_bf16_peak": f_flops / (f_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
         log(f"[bench] self-conditioning input (F={args.ffw_F}): {f_ms:.3f} ms")
 
+    # the latency-bound pieces, timed alone: accept/renoise of this batch, and q_sample on the
+    # 64 x 256 training-corruption shape (V = 50,257)
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, z in evs:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(z) for a, z in evs]
+
+    ar_ms = timed(lambda: runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed,
+                                                stream))
+    qw = synth.qsample_workload()
+    x0_t = torch.from_numpy(qw.x0).to(dev)
+    kap_t = torch.from_numpy(qw.kappa).to(dev)
+    xt_t = torch.empty_like(x0_t)
+    qs_ms = timed(lambda: B.dg_q_sample(x0_t, qw.n_canvas, 256, qw.V, kap_t, seed, xt_t,
+                                        stream=stream))
+
     flops = algorithmic_flops(wl)
     flops_k1 = 2.0 * wl.R * wl.V * wl.d
     ach_k1 = flops_k1 / (k1_ms * 1e-3) / 1e12
@@ -291,11 +323,18 @@ def main() -> int:
                    "d": wl.d, "commit_canvases": int(wl.commit.sum()),
                    "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget,
                    "softcap": args.softcap,
-                   "embedding": "fp8-e4m3, power-of-two row scales" if args.fp8 else "bf16"},
+                   "embedding": "fp8-e4m3, power-of-two row scales" if args.fp8 else "bf16",
+                   "caches": "warm: no L2 / MALL flush between steps"},
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "vocab_pass": {"avg_launch_ms": vp_avg, "algorithmic_flops": flops,
-                       "achieved_tflops": flops / (vp_avg * 1e-3) / 1e12},
+                       "achieved_tflops": flops / (vp_avg * 1e-3) / 1e12,
+                       "p10_p50_p90_ms": [float(x) for x in np.percentile(vp_ms, [10, 50, 90])]},
+        "accept_renoise": {"median_us": 1e3 * float(np.median(ar_ms)),
+                           "p10_p90_us": [1e3 * float(x) for x in np.percentile(ar_ms, [10, 90])]},
+        "q_sample": {"shape": f"{qw.n_canvas}x256, V={qw.V}",
+                     "median_us": 1e3 * float(np.median(qs_ms)),
+                     "tokens_per_s": qw.n_canvas * 256 / (float(np.median(qs_ms)) * 1e-3)},
         "roofline": {
             "kernel": "k_gemm_logits" if gemm_path else "dg_vocab_pass (non-default path)",
             "bound": "mfma", "achieved": ach_k1, "peak": PEAK_BF16_TFLOPS,
