@@ -49,7 +49,9 @@ class SamplerResult:
 
 def accept_renoise(entropy, argmax_tok, gumbel_tok, commit, n_canvas: int, C: int, V: int,
                    budget: float, confidence: float, stability: int, seed: int, step,
-                   prev_argmax, stable_count) -> SamplerResult:
+                   prev_argmax, stable_count, canvas_ids=None) -> SamplerResult:
+    """canvas_ids: the batch-wide indices of the n_canvas canvases given (default 0..n-1); the
+    renoise counter of a position is its batch-wide row, canvas_id * C + position."""
     H = np.asarray(entropy, dtype=np.float64)
     am = np.asarray(argmax_tok, dtype=np.int64)
     gt = np.asarray(gumbel_tok, dtype=np.int64)
@@ -81,7 +83,8 @@ def accept_renoise(entropy, argmax_tok, gumbel_tok, commit, n_canvas: int, C: in
             before += h[i]
         a = prefix <= budget
         acc[rows] = a.astype(np.uint8)
-        ren = philox.renoise_tokens(rows, V, seed, int(step[c]))
+        cid = c if canvas_ids is None else int(canvas_ids[c])
+        ren = philox.renoise_tokens(np.arange(cid * C, (cid + 1) * C), V, seed, int(step[c]))
         nxt[rows] = np.where(a, gt[rows], ren)
         same = bool(np.all(am[rows] == prev[rows]))
         cnt[c] = cnt[c] + 1 if same else 0
