@@ -75,6 +75,7 @@ struct GemmPlan {
   int n_units;      // expectation units (flat mapping)
   int flat;         // 1: flat unit mapping
   int gmax;         // largest canvas round of the logits pass
+  int st_stride;    // statistic slots per row
   size_t off_small, off_P, off_ref, off_st, off_accp, off_accM, off_fac;
   size_t bytes;
 };

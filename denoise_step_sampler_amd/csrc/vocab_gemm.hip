@@ -53,7 +53,6 @@ typedef int i32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 256;      // vocabulary tile of the logits pass (and rows per canvas)
 constexpr int kHalf = 128;      // granularity of the weight references
-constexpr int kLanesMax = 256;  // vocabulary lanes per canvas at most (one canvas per GPU)
 constexpr int kWG = 256;        // workgroups per round of the logits pass
 constexpr int kFacStride = 72;  // floats per row of the combine's weights
 constexpr int kRoundMax = 32;   // canvases per round of the logits pass (four per XCD)
@@ -169,10 +168,10 @@ struct GemmK {
                       // [row / 16][v / 32], entry (row, v) at 8 (row % 16 + 16 ((v % 32) / 8))
                       // + v % 8 of its block; row = 256 pos + i
   int* ref;           // [n_half][R] integer references (base-2 units), row = 256 pos + i
-  float* st_m;        // [R][2 * kLanesMax] statistic partials (slot = 2 lane + half)
+  float* st_m;        // [R][st_stride] statistic partials (slot = 2 lane + half)
   float* st_l;
   float* st_lb;
-  float* st_tm;       // [4][R][2 * kLanesMax] top-4 half-tile maxima (z2) and their entries
+  float* st_tm;       // [4][R][st_stride] top-4 half-tile maxima (z2) and their entries
   int* st_tv;
   float* st_a;
   float* st_amv;
@@ -190,6 +189,7 @@ struct GemmK {
   int n_colblk;       // d / (32 ncb)
   int flat;           // expectation units mapped flat (1) or pair-per-XCD (0)
   int gmax;           // largest round of the logits pass (canvases)
+  int st_stride;      // statistic slots per row: 2 x the most lanes any canvas gets
 };
 
 // Per-lane epilogue of one row (32-row block of this wave) over the wave's 128 entries: the
@@ -710,11 +710,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   // statistic partials of this (canvas, lane, half)
   if (lane < 32) {
     const int slot = 2 * ln.lane + vh;
-    const size_t o0 = ((size_t)c * kTile + rloc0) * (2 * kLanesMax) + slot;
-    const size_t plane = (size_t)2 * kLanesMax * R;
+    const size_t o0 = ((size_t)c * kTile + rloc0) * (size_t)g.st_stride + slot;
+    const size_t plane = (size_t)g.st_stride * R;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const size_t o = o0 + (size_t)32 * nb * (2 * kLanesMax);
+      const size_t o = o0 + (size_t)32 * nb * (size_t)g.st_stride;
       const LdsRowAcc* st = nb ? st1p : st0p;
       g.st_amv[o] = st->amv;
       g.st_ami[o] = st->ami;
@@ -1060,7 +1060,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
   const bool heavy = p < *g.n_nc_p;
   const int L = lanes_at(p, n_canvas, g.gmax);
   const int n_slot = 2 * min(L, g.n_tiles);
-  const size_t plane = (size_t)2 * kLanesMax * R;
+  const size_t plane = (size_t)g.st_stride * R;
   float m = -INFINITY, l = 0.0f, a = 0.0f, lb = 0.0f, amv = -INFINITY, gv = -INFINITY;
   int ami = 0x7FFFFFFF, gi = 0x7FFFFFFF;
   float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int s = min(s0 + 64 * u, n_slot - 1);
-      const size_t o = (size_t)r * (2 * kLanesMax) + s;  // the slots of a row are contiguous
+      const size_t o = (size_t)r * (size_t)g.st_stride + s;  // a row's slots are contiguous
       vamv[u] = g.st_amv[o];
       vami[u] = g.st_ami[o];
       if (heavy) {
@@ -1253,6 +1253,13 @@ GemmPlan gemm_plan(int n_canvas, int V, int d) {
   pick_selfcond_tiling(n_canvas, p.n_tiles, d, &p.ncb, &p.n_range, &p.flat);
   p.n_colblk = d / (32 * p.ncb);
   p.gmax = kRoundMax;
+  {
+    // the smallest round: kRoundMax while whole rounds remain, else the lowest set bit of the
+    // remainder; its canvases get the most lanes, 256 / size (used up to the tile count)
+    const int rem = n_canvas % p.gmax;
+    const int gmin = rem ? (rem & -rem) : p.gmax;
+    p.st_stride = 2 * min(kWG / gmin, p.n_tiles);
+  }
   p.n_rounds = n_canvas / p.gmax + __builtin_popcount((unsigned)(n_canvas % p.gmax));
   p.n_units_xcd = ((n_canvas * p.n_range + 7) / 8) * p.n_colblk;
   p.n_units = n_canvas * p.n_range * p.n_colblk;
@@ -1264,7 +1271,7 @@ GemmPlan gemm_plan(int n_canvas, int V, int d) {
   p.off_ref = off;
   off += al256g((size_t)2 * p.n_tiles * p.R * 4);
   p.off_st = off;
-  off += 16 * al256g((size_t)2 * kLanesMax * p.R * 4);  // 8 statistics + 4 x (top z2, entry)
+  off += 16 * al256g((size_t)p.st_stride * p.R * 4);  // 8 statistics + 4 x (top z2, entry)
   p.off_accp = off;
   off += al256g((size_t)p.n_range * p.R * d * 4);
   p.off_accM = off;
@@ -1289,7 +1296,7 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   g.n_nc_p = n_nc;
   g.P = reinterpret_cast<uint16_t*>(b + p.off_P);
   g.ref = reinterpret_cast<int*>(b + p.off_ref);
-  const size_t st = al256g((size_t)2 * kLanesMax * p.R * 4);
+  const size_t st = al256g((size_t)p.st_stride * p.R * 4);
   g.st_m = reinterpret_cast<float*>(b + p.off_st + 0 * st);
   g.st_l = reinterpret_cast<float*>(b + p.off_st + 1 * st);
   g.st_a = reinterpret_cast<float*>(b + p.off_st + 2 * st);
@@ -1310,6 +1317,7 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   g.n_colblk = p.n_colblk;
   g.flat = p.flat;
   g.gmax = p.gmax;
+  g.st_stride = p.st_stride;
   hipLaunchKernelGGL(k_gemm_init, dim3(1), dim3(256), 0, stream, a.commit, a.n_canvas, order,
                      pos, n_nc);
   hipError_t e = hipGetLastError();

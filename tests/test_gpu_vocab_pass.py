@@ -268,3 +268,48 @@ def test_softcap_batched_serving_step_sampled(large):
     canv = [0, 3, 9, 30]
     rows = np.sort(np.concatenate([c * 256 + rng.choice(256, 3, replace=False) for c in canv]))
     _check_cap(wl, 3, 30.0, rows=rows, E64=E64, E_t=E_t, label="batched")
+
+
+# --- maximum sizes ------------------------------------------------------------------------
+
+def test_maximum_width():
+    """d = DG_MAX_D = 8192 with a ragged vocabulary and a commit canvas, every row."""
+    wl = synth.workload("lite", V=700, d=8192, n_canvas=2, seed=13)
+    wl.commit = np.array([0, 1], np.uint8)
+    wl.temperature = np.array([0.7, 1.0], np.float32)
+    _check(wl, seed=21, label="d=8192")
+
+
+def test_maximum_canvases_with_sampler():
+    """n = DG_MAX_CANVASES = 4096 canvases (1,048,576 rows), every third one committing: the
+    vocabulary pass on every row of four canvases, first, middle, commit and last, and the
+    accept/renoise step of those canvases against the oracle."""
+    from denoise_step_sampler_amd import runner
+    from oracle import sampler as osm
+    from parity import compare_sampler
+    n, V, d = 4096, 300, 128
+    wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=17)
+    wl.commit = (np.arange(n) % 3 == 2).astype(np.uint8)
+    wl.step = (np.arange(n) % 7).astype(np.int32)
+    seed = 99
+    _say(f"[vocab_pass] n={n} V={V} d={d}")
+    b = runner.from_workload(wl)
+    runner.vocab_pass(b, seed)
+    runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed)
+    torch.cuda.synchronize()
+    canv = np.array([0, 2047, 2048, 4095])
+    assert wl.commit[2048] == 1 and wl.commit[2047] == 0
+    rows = (canv[:, None] * 256 + np.arange(256)[None, :]).reshape(-1)
+    ref, cm = _oracle(wl, rows, seed)
+    _say("   ", compare_vocab(_host(b, rows), ref, cm))
+    # the sampler on the oracle's values for the same canvases (as one batch of four)
+    sref = osm.accept_renoise(ref.entropy, ref.argmax, ref.gumbel, wl.commit[canv], 4, 256, V,
+                              wl.budget, wl.confidence, wl.stability, seed, wl.step[canv],
+                              np.full(4 * 256, -1), np.zeros(4, np.int64), canvas_ids=canv)
+    got = {"next_tokens": b.next_tokens.cpu().numpy()[rows],
+           "accept": b.accept_mask.cpu().numpy()[rows],
+           "converged": b.converged.cpu().numpy()[canv],
+           "mean_entropy": b.mean_entropy.cpu().numpy()[canv],
+           "prev_argmax": b.prev_argmax.cpu().numpy()[rows],
+           "stable_count": b.stable_count.cpu().numpy()[canv]}
+    _say("   ", compare_sampler(got, sref, wl.commit[canv], 256))
