@@ -7,7 +7,9 @@ used here: the tied embedding is stored as OCP FP8 E4M3 (sign, 4 exponent bits w
 3 mantissa bits, no infinities, 0x7F / 0xFF NaN, largest finite 448) with one scale 2^k per
 row, the row's largest |E| mapped to at most 448:
 
-  k_v = the smallest integer with max_j |E_vj| <= 448 * 2^k_v   (k_v = -127 for a zero row)
+  k_v = the smallest integer with max_j |E_vj| <= 448 * 2^k_v, at least -117
+        (a zero row gets -117; the floor keeps every nonzero dequantised value a normal
+        fp32 / bf16 number, at least 2^-9 * 2^-117 = 2^-126)
   q_vj = E4M3 nearest to E_vj / 2^k_v (ties to the even code)
   E~_vj = 2^k_v * value(q_vj)
 
@@ -61,19 +63,22 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     return np.where((x < 0) & (c != 0), c | 0x80, c).astype(np.uint8)
 
 
+K_MIN = -117
+
+
 def row_exponent(row_amax: np.ndarray) -> np.ndarray:
-    """Smallest k with amax <= 448 * 2^k (-127 for a zero row)."""
+    """Smallest k >= K_MIN with amax <= 448 * 2^k."""
     out = np.empty(row_amax.shape, np.int64)
     for i, a in enumerate(np.asarray(row_amax, np.float64)):
         if a == 0:
-            out[i] = -127
+            out[i] = K_MIN
             continue
         k = math.ceil(math.log2(a / E4M3_MAX))
         while a > E4M3_MAX * 2.0 ** k:        # guard the logarithm's rounding
             k += 1
         while a <= E4M3_MAX * 2.0 ** (k - 1):
             k -= 1
-        out[i] = k
+        out[i] = max(k, K_MIN)
     return out
 
 
