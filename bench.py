@@ -245,7 +245,7 @@ def main() -> int:
         k1_args = (b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step,
                    b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, None, b.workspace)
         if args.fp8:
-            B.dg_vocab_pass_fp8(f8.codes, f8.row_exp, *k1_args[1:-1], ws8, stream=stream,
+            B.dg_vocab_pass_fp8(f8.codes, f8.codesT, f8.row_exp, *k1_args[1:-1], ws8, stream=stream,
                                 softcap=args.softcap or 0.0)
         elif args.softcap is None:
             B.dg_vocab_pass(*k1_args, stream=stream)

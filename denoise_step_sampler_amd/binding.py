@@ -63,12 +63,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_lite_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, F, I, U64, P, P, P, P, P,
                                  P, P, P, P, P, P]
     lib.dg_lite_step.restype = I
-    lib.dg_quantize_embedding_fp8.argtypes = [P, I, I, P, P, P]
+    lib.dg_quantize_embedding_fp8.argtypes = [P, I, I, P, P, P, P]
     lib.dg_quantize_embedding_fp8.restype = I
     lib.dg_vocab_pass_fp8_workspace_size.argtypes = [I, I, I, I]
     lib.dg_vocab_pass_fp8_workspace_size.restype = SZ
-    lib.dg_vocab_pass_fp8.argtypes = [P, P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P,
-                                      F]
+    lib.dg_vocab_pass_fp8.argtypes = [P, P, P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ,
+                                      P, F]
     lib.dg_vocab_pass_fp8.restype = I
     lib.dg_status_string.argtypes = [I]
     lib.dg_status_string.restype = ctypes.c_char_p
@@ -258,11 +258,18 @@ def dg_lite_step(h: torch.Tensor, E: torch.Tensor, temperature: torch.Tensor, ls
     _check(st)
 
 
+def fp8_pitch(V: int) -> int:
+    """Row pitch of the transposed FP8 codes (DG_FP8_PITCH)."""
+    return (V + 255) // 256 * 256
+
+
 def dg_quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, codes: torch.Tensor,
-                              row_exp: torch.Tensor, stream=None) -> None:
+                              codesT: Optional[torch.Tensor], row_exp: torch.Tensor,
+                              stream=None) -> None:
     lib = load()
     _check(lib.dg_quantize_embedding_fp8(_bf16_ptr(E, V * d, "E"), V, d,
                                          _ptr(codes, torch.uint8, V * d, "codes"),
+                                         _ptr(codesT, torch.uint8, d * fp8_pitch(V), "codesT"),
                                          _ptr(row_exp, torch.int32, V, "row_exp"),
                                          _stream(stream)))
 
@@ -271,7 +278,8 @@ def dg_vocab_pass_fp8_workspace_size(n_canvas: int, C: int, V: int, d: int) -> i
     return int(load().dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d))
 
 
-def dg_vocab_pass_fp8(codes: torch.Tensor, row_exp: torch.Tensor, h: torch.Tensor, n_canvas: int,
+def dg_vocab_pass_fp8(codes: torch.Tensor, codesT: Optional[torch.Tensor], row_exp: torch.Tensor,
+                      h: torch.Tensor, n_canvas: int,
                       C: int, V: int, d: int, temperature: torch.Tensor,
                       commit: Optional[torch.Tensor], seed: int, step: torch.Tensor,
                       lse: Optional[torch.Tensor], entropy: torch.Tensor,
@@ -281,7 +289,9 @@ def dg_vocab_pass_fp8(codes: torch.Tensor, row_exp: torch.Tensor, h: torch.Tenso
     R = n_canvas * C
     lib = load()
     st = lib.dg_vocab_pass_fp8(
-        _ptr(codes, torch.uint8, V * d, "codes"), _ptr(row_exp, torch.int32, V, "row_exp"),
+        _ptr(codes, torch.uint8, V * d, "codes"),
+        _ptr(codesT, torch.uint8, d * fp8_pitch(V), "codesT"),
+        _ptr(row_exp, torch.int32, V, "row_exp"),
         _bf16_ptr(h, R * d, "h"), n_canvas, C, V, d,
         _ptr(temperature, torch.float32, n_canvas, "temperature"),
         _ptr(commit, torch.uint8, n_canvas, "commit"),

@@ -49,6 +49,11 @@ Path pick_path(int d, int* n_wg) {
   return dg::gemm_supported(d) ? kGemm : kSplit;
 }
 
+// Largest batch for which the FP8 pass streams the transposed codes through the expectation
+// pass (measured: one canvas 0.84 ms against 0.90 on bf16 rows and 1.27 on the dequantised
+// copy; 32 canvases 19.6 ms against 19.3 on the copy).
+constexpr int kFp8StreamMaxCanvases = 4;
+
 // Bytes of the two-GEMM workspace before the FP8 pass's dequantised rows.
 size_t fp8_offset(int n_canvas, int V, int d) {
   return (dg::gemm_plan(n_canvas, V, d).bytes + 255) & ~(size_t)255;
@@ -138,7 +143,7 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
                      size_t workspace_bytes, void* stream, float softcap,
                      bool force_gemm = false, const uint8_t* E8 = nullptr,
-                     const int32_t* E_exp = nullptr) {
+                     const int32_t* E_exp = nullptr, const uint8_t* E8T = nullptr) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
@@ -176,6 +181,8 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.softcap = softcap;
   a.E8 = E8;
   a.E_exp = E_exp;
+  a.E8T = E8T;
+  a.E8T_pitch = dg::fp8_transposed_pitch(V);
   int n_wg = 0;
   hipError_t e;
   switch (force_gemm ? kGemm : pick_path(d, &n_wg)) {
@@ -232,20 +239,25 @@ size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {
 }
 
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
-                                    int32_t* row_exp, void* stream) {
+                                    uint8_t* codesT, int32_t* row_exp, void* stream) {
   g_err[0] = 0;
   if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
   if (d < 64 || d > DG_MAX_D || d % 64 != 0)
     return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 64 in [64, %d]", d, DG_MAX_D);
   if (!E || !codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(E) || !aligned16(codes))
-    return fail(DG_ERR_INVALID_ARG, "E and codes must be 16-byte aligned");
-  const hipError_t e = dg::fp8_quantize_launch(E, V, d, codes, row_exp, (hipStream_t)stream);
+  if (!aligned16(E) || !aligned16(codes) || (codesT && !aligned16(codesT)))
+    return fail(DG_ERR_INVALID_ARG, "E, codes and codesT must be 16-byte aligned");
+  hipError_t e = dg::fp8_quantize_launch(E, V, d, codes, row_exp, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  if (codesT) {
+    e = dg::fp8_transpose_launch(codes, V, d, codesT, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fp8 transpose launch");
+  }
   return DG_OK;
 }
 
-dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const uint16_t* h,
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint8_t* codesT, const int32_t* row_exp,
+                            const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,
                             float* lse, float* entropy, int32_t* argmax_tok,
@@ -257,8 +269,8 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const 
   if (!dg::gemm_supported(d))
     return fail(DG_ERR_UNSUPPORTED, "the FP8 embedding needs d %% 128 == 0 (d=%d)", d);
   if (!codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(codes) || !aligned16(row_exp))
-    return fail(DG_ERR_INVALID_ARG, "codes and row_exp must be 16-byte aligned");
+  if (!aligned16(codes) || !aligned16(row_exp) || (codesT && !aligned16(codesT)))
+    return fail(DG_ERR_INVALID_ARG, "codes, codesT and row_exp must be 16-byte aligned");
   if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
     return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
   const size_t need = dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d);
@@ -267,17 +279,20 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const 
                 need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  // the logits pass streams the codes; the expectation pass reads the dequantised rows (exact
-  // bf16), written to the end of the workspace only when the expectation is asked for
+  // the logits pass streams the codes.  The expectation pass streams the transposed codes for
+  // batches of up to four canvases (E comes from HBM for each: half the bytes, no copy);
+  // larger batches share E through L2 and run faster on the dequantised rows (exact bf16),
+  // written to the end of the workspace when the expectation is asked for
+  if (n_canvas > kFp8StreamMaxCanvases) codesT = nullptr;
   const size_t off = fp8_offset(n_canvas, V, d);
   uint16_t* Eq = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + off);
-  if (selfcond != nullptr) {
+  if (selfcond != nullptr && codesT == nullptr) {
     const hipError_t e = dg::fp8_dequantize_launch(codes, row_exp, V, d, Eq, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "fp8 dequantize launch");
   }
   return vocab_pass(Eq, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, off, stream, softcap, true, codes,
-                    row_exp);
+                    row_exp, selfcond != nullptr ? codesT : nullptr);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

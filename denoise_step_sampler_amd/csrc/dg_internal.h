@@ -30,6 +30,11 @@ struct VocabArgs {
   // always reads E (bf16), which must then hold the same values.
   const uint8_t* E8;
   const int32_t* E_exp;
+  // with E8: the transposed codes [d][pitch] for the expectation pass (then E is not read and
+  // the logits pass stores the weights scaled by 2^E_exp[v]), or null (the expectation pass
+  // reads E, the dequantised rows)
+  const uint8_t* E8T;
+  int E8T_pitch;
 };
 
 // Workspace carve-up.
@@ -178,6 +183,10 @@ hipError_t fp8_quantize_launch(const uint16_t* E, int V, int d, uint8_t* codes, 
                                hipStream_t stream);
 hipError_t fp8_dequantize_launch(const uint8_t* codes, const int32_t* kexp, int V, int d,
                                  uint16_t* E, hipStream_t stream);
+// Transposed codes for the expectation pass: [d][fp8_transposed_pitch(V)], zero past V.
+inline int fp8_transposed_pitch(int V) { return (V + 255) / 256 * 256; }
+hipError_t fp8_transpose_launch(const uint8_t* codes, int V, int d, uint8_t* codesT,
+                                hipStream_t stream);
 
 hipError_t q_sample_launch(const int32_t* x0, int n_canvas, int V, const float* kappa,
                            uint32_t k0, uint32_t k1, int32_t* xt, hipStream_t stream);

@@ -112,7 +112,44 @@ __global__ __launch_bounds__(256) void k_fp8_dequantize(const uint8_t* codes, co
   dst[1] = o1;
 }
 
+// codesT[k][v] = codes[v][k] for a 64 x 64 block of (v, k) per workgroup, through LDS; the
+// rows of codesT have pitch vp (a multiple of 256), entries v >= V are written as 0.
+__global__ __launch_bounds__(256) void k_fp8_transpose(const uint8_t* codes, int V, int d, int vp,
+                                                       uint8_t* codesT) {
+  __shared__ uint8_t tile[64][64 + 16];
+  const int v0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 2, q = t & 3;  // row v0 + r, 16 bytes q of its 64
+    u32x4 x = u32x4{0, 0, 0, 0};
+    if (v0 + r < V) x = *reinterpret_cast<const u32x4*>(codes + (size_t)(v0 + r) * d + k0 + 16 * q);
+#pragma unroll
+    for (int b = 0; b < 16; ++b) tile[r][16 * q + b] = (uint8_t)(x[b >> 2] >> (8 * (b & 3)));
+  }
+  __syncthreads();
+  {
+    const int kk = t >> 2, q = t & 3;  // row k0 + kk of codesT, entries v0 + 16 q .. + 15
+    u32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w |= (uint32_t)tile[16 * q + 4 * j + b][kk] << (8 * b);
+      y[j] = w;
+    }
+    *reinterpret_cast<u32x4*>(codesT + (size_t)(k0 + kk) * vp + v0 + 16 * q) = y;
+  }
+}
+
 }  // namespace
+
+hipError_t fp8_transpose_launch(const uint8_t* codes, int V, int d, uint8_t* codesT,
+                                hipStream_t stream) {
+  const int vp = fp8_transposed_pitch(V);
+  hipLaunchKernelGGL(k_fp8_transpose, dim3((unsigned)(vp / 64), (unsigned)(d / 64)), dim3(256), 0,
+                     stream, codes, V, d, vp, codesT);
+  return hipGetLastError();
+}
 
 hipError_t fp8_quantize_launch(const uint16_t* E, int V, int d, uint8_t* codes, int32_t* kexp,
                                hipStream_t stream) {

@@ -217,12 +217,14 @@ __device__ __forceinline__ float soft_cap_z2(float s, const SoftCap& sc) {
 }
 
 // kCap: z2 = soft_cap_z2(S) in place of S c2; the argmax stays on S.
-template <bool kHeavy, bool kCap>
+// kScaleP: the stored weights are 2^pexp[v] times the bf16 weights (exact; the expectation
+// pass then multiplies them by the FP8 codes), the normaliser sums the unscaled ones.
+template <bool kHeavy, bool kCap, bool kScaleP = false>
 __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, const f32x16& s2,
                                         const f32x16& s3, int vt0, int V, float c2,
                                         const SoftCap& cap, uint32_t row, uint32_t step,
                                         uint32_t k0, uint32_t k1, uint16_t* pt, int* ref_out,
-                                        LdsRowAcc* lds_st) {
+                                        LdsRowAcc* lds_st, const int32_t* pexp = nullptr) {
   // HIP contracts a * b - c into one fma by default, which would round dz once instead of
   // twice and break the bit-for-bit recomputation in the combine
 #pragma clang fp contract(off)
@@ -315,7 +317,24 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       }
       const uint32_t w01 = pack_bf16x2(pv[0], pv[1]), w23 = pack_bf16x2(pv[2], pv[3]);
       lsb = add_bf16x2(add_bf16x2(lsb, w01), w23);
-      *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
+      if constexpr (kScaleP) {
+        int ke[4];
+        if constexpr (kMasked) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ke[j] = pexp[min(vb + j, V - 1)];
+        } else {
+          const i32x4v k4 = *reinterpret_cast<const i32x4v*>(pexp + vb);  // vb % 4 == 0
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ke[j] = k4[j];
+        }
+        const uint32_t x01 = pack_bf16x2(__builtin_amdgcn_ldexpf(pv[0], ke[0]),
+                                         __builtin_amdgcn_ldexpf(pv[1], ke[1]));
+        const uint32_t x23 = pack_bf16x2(__builtin_amdgcn_ldexpf(pv[2], ke[2]),
+                                         __builtin_amdgcn_ldexpf(pv[3], ke[3]));
+        *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{x01, x23};
+      } else {
+        *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
+      }
     }
   };
   const bool full = vt0 + kHalf <= V;
@@ -694,7 +713,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     }
     int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
     const size_t vblk = (size_t)(vt0 >> 5) * 512;  // first 32-entry block of the half tile
-    if (heavy) {
+    if (kF8 && heavy && g.a.E8T != nullptr) {
+      epi_row<true, kCap, true>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap,
+                                row0, step, k0, k1, prow0 + vblk, rout0, st0p, g.a.E_exp);
+      epi_row<true, kCap, true>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap,
+                                row1, step, k0, k1, prow1 + vblk, rout0 + 32, st1p, g.a.E_exp);
+    } else if (heavy) {
       epi_row<true, kCap>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
                           step, k0, k1, prow0 + vblk, rout0, st0p);
       epi_row<true, kCap>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap, row1,
@@ -818,14 +842,18 @@ __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
 // kMaxUnitTiles vocabulary tiles (its exponent shifts fit in LDS).
 constexpr int kMaxUnitTiles = 64;
 
-template <int NCB>
+// kF8: E arrives as the transposed FP8 codes (g.a.E8T, [d][pitch]) and the weights were
+// stored scaled by 2^E_exp[v]: the stage holds BN column rows of 32 codes (32 bytes each, the
+// two 16-byte halves swapped on rows with bit 3 set), a B fragment is one 8-byte read (the 8
+// codes of one column) widened to bf16 in registers.
+template <int NCB, bool kF8 = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int BN = 32 * NCB;            // columns of a unit
-  constexpr int kPitchE = 2 * BN;         // bytes of one staged E row
+  constexpr int kPitchE = 2 * BN;         // bytes of one staged E row (bf16)
   constexpr int kKC2 = 32;                // K chunk (vocabulary entries) per stage
   constexpr int kNst2 = 4;                // stages: copies run three chunks ahead
   constexpr int kPB = kTile * 2 * kKC2;   // weights: 16 fragment blocks of 1 KB (16 KB)
-  constexpr int kEB = kKC2 * kPitchE;     // E: 32 rows x BN columns
+  constexpr int kEB = kF8 ? BN * kKC2 : kKC2 * kPitchE;  // E: 32 rows x BN columns
   constexpr int kStage = kPB + kEB;
   constexpr int kNE = kEB / 1024;         // E copies per stage (2 NCB)
   constexpr int kNEw = kNE >= 8 ? kNE / 8 : 1;  // E copies per wave (waves >= kNE repeat one)
@@ -913,8 +941,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     for (int j = 0; j < 2; ++j)
       dma_asm(pbase + ((size_t)j * nvb + kc) * 1024, offP, dst + 1024u * (uint32_t)(2 * w + j));
   };
+  // kF8: copy e moves the 32 column rows 32 e + lane / 2 of the stage, 16 bytes each; the
+  // transposed codes are zero up to the padded width, so no row needs clamping
+  const uint32_t off8 = (uint32_t)(lane >> 1) * (uint32_t)(kF8 ? g.a.E8T_pitch : 0) +
+                        16u * (uint32_t)((lane & 1) ^ ((lane >> 4) & 1));
   auto issue_e = [&](int kc, uint32_t dst) {
     kc = min(kc, nkc - 1);
+    if constexpr (kF8) {
+      const int v0 = v00 + kc * kKC2;
+#pragma unroll
+      for (int m = 0; m < kNEw; ++m) {
+        const int e = ew + 8 * m;
+        const uint8_t* eb8 =
+            g.a.E8T + (size_t)(u.j * BN + 32 * e) * (size_t)g.a.E8T_pitch + (size_t)v0;
+        dma_asm(eb8, off8, dst + (uint32_t)kPB + 1024u * (uint32_t)e);
+      }
+      return;
+    }
     // E rows past V - 1 (tail of the last tile, zero weights) read row V - 1
     const int vb = min(v00 + kc * kKC2, V - 1);
     const int lim = V - 1 - vb;
@@ -962,7 +1005,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       if (cb == NCB / 2) issue_p(kn, sn);
-      const u32x4 fb = e_frag(se, kPitchE, 0, ea ^ (32 * cb));
+      u32x4 fb;
+      if constexpr (kF8) {
+        // column row 16 NCB cw + 16 cb + i, codes 8 g .. 8 g + 7 (g = lane / 16)
+        const int r8 = 16 * NCB * cw + 16 * cb + (lane & 15);
+        const int gq = lane >> 4;
+        const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+            se + r8 * 32 + 16 * ((gq >> 1) ^ (((lane & 15) >> 3) & 1)) + 8 * (gq & 1));
+        fb = e4m3x8_bf16(x[0], x[1]);
+      } else {
+        fb = e_frag(se, kPitchE, 0, ea ^ (32 * cb));
+      }
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
     }
@@ -1184,10 +1237,23 @@ __global__ __launch_bounds__(256) void k_gemm_sc(GemmK g) {
   }
   for (; s < nr; ++s) acc += fr[s] * src[(size_t)s * stride];
   const int* vi = reinterpret_cast<const int*>(fr) + 68;
-  const uint16_t* E = g.a.E;
+  if (g.a.E8 != nullptr && g.a.E8T != nullptr) {
+    // E from the FP8 codes: 2^E_exp[v] value(code), exact
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    acc += fr[64 + k] * __uint_as_float((uint32_t)E[(size_t)vi[k] * d + col] << 16);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t code = g.a.E8[(size_t)vi[k] * d + col];
+      const float ev = __builtin_amdgcn_ldexpf(
+          bf16_lo(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                                   code, 1.0f, false))),
+          g.a.E_exp[vi[k]]);
+      acc += fr[64 + k] * ev;
+    }
+  } else {
+    const uint16_t* E = g.a.E;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc += fr[64 + k] * __uint_as_float((uint32_t)E[(size_t)vi[k] * d + col] << 16);
+  }
   g.a.selfcond[(size_t)r * d + col] = acc;
 }
 
@@ -1337,10 +1403,26 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   if (e != hipSuccess) return e;
   if (a.selfcond != nullptr) {
     const dim3 grid((unsigned)(p.flat ? p.n_units : 8 * p.n_units_xcd));
+    const bool f8 = a.E8 != nullptr && a.E8T != nullptr;
     switch (p.ncb) {
-      case 8: hipLaunchKernelGGL(k_gemm_selfcond<8>, grid, dim3(512), 0, stream, g); break;
-      case 4: hipLaunchKernelGGL(k_gemm_selfcond<4>, grid, dim3(512), 0, stream, g); break;
-      default: hipLaunchKernelGGL(k_gemm_selfcond<2>, grid, dim3(512), 0, stream, g); break;
+      case 8:
+        if (f8)
+          hipLaunchKernelGGL((k_gemm_selfcond<8, true>), grid, dim3(512), 0, stream, g);
+        else
+          hipLaunchKernelGGL((k_gemm_selfcond<8, false>), grid, dim3(512), 0, stream, g);
+        break;
+      case 4:
+        if (f8)
+          hipLaunchKernelGGL((k_gemm_selfcond<4, true>), grid, dim3(512), 0, stream, g);
+        else
+          hipLaunchKernelGGL((k_gemm_selfcond<4, false>), grid, dim3(512), 0, stream, g);
+        break;
+      default:
+        if (f8)
+          hipLaunchKernelGGL((k_gemm_selfcond<2, true>), grid, dim3(512), 0, stream, g);
+        else
+          hipLaunchKernelGGL((k_gemm_selfcond<2, false>), grid, dim3(512), 0, stream, g);
+        break;
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -172,15 +172,20 @@ def lite_step(b: VocabBuffers, s: LiteState, threshold: float, stability_steps: 
 
 @dataclass
 class Fp8Embedding:
-    """The FP8 form of an embedding on the device: E4M3 codes and per-row exponents."""
+    """The FP8 form of an embedding on the device: E4M3 codes, their transpose (or None) and
+    per-row exponents."""
     codes: torch.Tensor
+    codesT: Optional[torch.Tensor]
     row_exp: torch.Tensor
 
 
-def quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, stream=None) -> Fp8Embedding:
+def quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, stream=None,
+                           transposed: bool = True) -> Fp8Embedding:
     f = Fp8Embedding(codes=torch.empty(V * d, dtype=torch.uint8, device=E.device),
+                     codesT=(torch.empty(d * B.fp8_pitch(V), dtype=torch.uint8, device=E.device)
+                             if transposed else None),
                      row_exp=torch.empty(V, dtype=torch.int32, device=E.device))
-    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.row_exp, stream=stream)
+    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.codesT, f.row_exp, stream=stream)
     return f
 
 
@@ -194,7 +199,7 @@ def fp8_workspace(n_canvas: int, V: int, d: int, device="cuda") -> torch.Tensor:
 def vocab_pass_fp8(b: VocabBuffers, f: Fp8Embedding, workspace: torch.Tensor, seed: int,
                    stream=None, softcap: Optional[float] = None) -> None:
     """The vocabulary pass on the FP8 embedding f (b.E is not read)."""
-    B.dg_vocab_pass_fp8(f.codes, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+    B.dg_vocab_pass_fp8(f.codes, f.codesT, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
                         b.commit, seed, b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok,
                         b.selfcond, workspace, stream=stream,
                         softcap=0.0 if softcap is None else softcap)

@@ -119,26 +119,33 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
  *   codes_vj = the E4M3 value nearest to E_vj / 2^k_v, ties to the even code (zero -> 0x00).
  * A power-of-two scale makes every dequantised value 2^k * value(code) an exact bf16 number.
  *  E        [V, d] bf16, finite, |E| < 2^127.   d % 64 == 0, 64 <= d <= DG_MAX_D.
- *  codes    [V, d] uint8 out;  row_exp [V] int32 out.  E and codes 16-byte aligned.
+ *  codes    [V, d] uint8 out;  row_exp [V] int32 out.
+ *  codesT   [d, DG_FP8_PITCH(V)] uint8 out, or NULL: the transposed codes the expectation pass
+ *           reads (codesT[k][v] = codes[v][k], zero for v >= V).
+ *  E, codes and codesT 16-byte aligned.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+#define DG_FP8_PITCH(V) ((((V) + 255) / 256) * 256)
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
-                                    int32_t* row_exp, void* stream);
+                                    uint8_t* codesT, int32_t* row_exp, void* stream);
 
 /* dg_vocab_pass_fp8_workspace_size -- bytes of workspace dg_vocab_pass_fp8 needs ([host],
  * pure): the two-GEMM workspace plus V * d bf16 for the dequantised rows.  0 if unsupported. */
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d);
 
 /* dg_vocab_pass_fp8 -- dg_vocab_pass (dg_vocab_pass_softcap when softcap > 0) on the FP8
- * embedding (codes, row_exp) of dg_quantize_embedding_fp8: the embedding is
+ * embedding (codes, codesT, row_exp) of dg_quantize_embedding_fp8: the embedding is
  * E~_vj = 2^row_exp[v] * value(codes_vj), and the logits, statistics, samples and
- * self-conditioning expectation are those of E~ (the logits pass streams the codes and scales
- * each entry's sum by 2^row_exp[v], exact; the expectation pass, when selfcond is given,
- * reads E~ dequantised exactly to bf16 into the workspace).  Results equal those of
- * dg_vocab_pass on E~ up to the order of the fp32 accumulation within a K chunk.
+ * self-conditioning expectation are those of E~.  The logits pass streams the codes and
+ * scales each entry's sum by 2^row_exp[v] (exact).  With codesT and n_canvas <= 4 the
+ * expectation pass streams the transposed codes against weights stored scaled by
+ * 2^row_exp[v] (exact); otherwise (codesT == NULL, or larger batches, which share E through
+ * L2) and with selfcond given it reads E~ dequantised exactly to bf16 into the workspace.
+ * Results equal those of dg_vocab_pass on E~ up to the order of fp32 accumulation.
  * Runs on the two-GEMM path (d % 128 == 0, else DG_ERR_UNSUPPORTED).  softcap: 0 (none) or
  * finite > 0.  Other arguments, outputs and errors as dg_vocab_pass; codes and row_exp
  * 16-byte aligned. */
-dg_status dg_vocab_pass_fp8(const uint8_t* codes, const int32_t* row_exp, const uint16_t* h,
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint8_t* codesT, const int32_t* row_exp,
+                            const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,
                             float* lse, float* entropy, int32_t* argmax_tok,

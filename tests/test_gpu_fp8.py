@@ -60,10 +60,10 @@ def _special_embedding(V, d, seed):
     return synth.round_to_bf16(E.astype(np.float32))
 
 
-def _quantize_gpu(E_bits, V, d):
+def _quantize_gpu(E_bits, V, d, transposed=True):
     from denoise_step_sampler_amd import runner
     E_t = runner.bf16_tensor(E_bits)
-    f = runner.quantize_embedding_fp8(E_t, V, d)
+    f = runner.quantize_embedding_fp8(E_t, V, d, transposed=transposed)
     torch.cuda.synchronize()
     return f, f.codes.cpu().numpy().reshape(V, d), f.row_exp.cpu().numpy()
 
@@ -76,23 +76,30 @@ def test_quantizer_bit_exact():
     assert np.array_equal(k, k_ref), np.nonzero(k != k_ref)[0][:8]
     bad = np.argwhere(codes != q_ref)
     assert bad.size == 0, [(int(r), int(c), int(codes[r, c]), int(q_ref[r, c])) for r, c in bad[:8]]
+    # the transposed codes: [d][pitch], zero past V
+    f, _, _ = _quantize_gpu(E, V, d)
+    pitch = (V + 255) // 256 * 256
+    qT = f.codesT.cpu().numpy().reshape(d, pitch)
+    assert np.array_equal(qT[:, :V], q_ref.T) and np.all(qT[:, V:] == 0)
 
 
-@pytest.mark.parametrize("softcap", [None, 15.0])
-def test_fp8_vocab_pass_parity_and_bf16_identity(softcap):
+@pytest.mark.parametrize("softcap,transposed", [(None, True), (15.0, True), (None, False)])
+def test_fp8_vocab_pass_parity_and_bf16_identity(softcap, transposed):
+    """The pass on the codes (transposed codes for the expectation, or its dequantised copy)
+    against the oracle on the dequantised rows and against the bf16 pass on them."""
     from denoise_step_sampler_amd import runner
     V, d, n = 5000, 256, 3
     wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=9)
     wl.commit = np.array([0, 1, 0], np.uint8)
     wl.temperature = np.array([0.5, 0.8, 1.1], np.float32)
-    f, codes, k = _quantize_gpu(wl.E, V, d)
+    f, codes, k = _quantize_gpu(wl.E, V, d, transposed)
     q_ref, k_ref = of8.quantize_rows(ovp.widen_bf16(wl.E))
     assert np.array_equal(codes, q_ref) and np.array_equal(k, k_ref)
     Eq = of8.dequantize_rows(q_ref, k_ref)              # the oracle's dequantised rows
     Eq_bits = synth.round_to_bf16(Eq.astype(np.float32))
     assert np.array_equal(ovp.widen_bf16(Eq_bits), Eq)  # exact in bf16
     seed = 0xF8
-    _say(f"[vocab_pass_fp8] softcap={softcap} n={n} V={V} d={d}")
+    _say(f"[vocab_pass_fp8] softcap={softcap} transposed={transposed} n={n} V={V} d={d}")
     b = runner.from_workload(wl)
     ws = runner.fp8_workspace(n, V, d)
     runner.vocab_pass_fp8(b, f, ws, seed, softcap=softcap)
@@ -120,8 +127,9 @@ def test_fp8_vocab_pass_parity_and_bf16_identity(softcap):
 
 
 def test_fp8_full_size_batched():
-    """V = 262144, d = 2816, 32 canvases: quantiser rows against the oracle on a sample, and the
-    FP8 pass against the bf16 pass on the dequantised rows."""
+    """V = 262144, d = 2816: quantiser rows against the oracle on a sample, and the FP8 pass
+    against the bf16 pass on the dequantised rows, for 32 canvases (expectation on the
+    dequantised copy) and for one canvas (expectation on the transposed codes)."""
     from denoise_step_sampler_amd import runner
     _say("[vocab_pass_fp8] generating V=262144 d=2816 embedding")
     E = synth.make_embedding(262144, 2816, seed=0)
@@ -145,3 +153,13 @@ def test_fp8_full_size_batched():
     runner.vocab_pass(b2, 5)
     torch.cuda.synchronize()
     _say("    agreement with the bf16 pass:", _agree(b, b2, np.repeat(wl.commit == 0, C)))
+    # one canvas: the expectation pass streams the transposed codes
+    E_q = b2.E
+    del b, b2
+    wl1 = synth.workload("large_v", E=E)
+    c1 = runner.from_workload(wl1)
+    runner.vocab_pass_fp8(c1, f, runner.fp8_workspace(1, V, d), 7)
+    c2 = runner.from_workload(wl1, E=E_q)
+    runner.vocab_pass(c2, 7)
+    torch.cuda.synchronize()
+    _say("    one canvas, streamed codes:", _agree(c1, c2, np.ones(C, bool)))
