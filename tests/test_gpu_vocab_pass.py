@@ -313,3 +313,13 @@ def test_maximum_canvases_with_sampler():
            "prev_argmax": b.prev_argmax.cpu().numpy()[rows],
            "stable_count": b.stable_count.cpu().numpy()[canv]}
     _say("   ", compare_sampler(got, sref, wl.commit[canv], 256))
+
+
+@pytest.mark.parametrize("scale,T", [(1.0, 0.02), (1.0, 50.0), (20.0, 0.4), (0.0, 0.3)])
+def test_extreme_temperatures_and_logit_ranges(scale, T):
+    """Very sharp (T = 0.02: z spans thousands of nats) and very flat (T = 50) distributions,
+    logits twenty times the usual range, and all-zero hidden states, against the oracle."""
+    wl = synth.workload("lite", V=3000, d=256, n_canvas=2, seed=31)
+    wl.h = synth.round_to_bf16(synth.bf16_to_f32(wl.h) * np.float32(scale))
+    wl.temperature = np.full(2, T, np.float32)
+    _check(wl, seed=4, label=f"x{scale} T={T}")
