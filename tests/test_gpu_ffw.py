@@ -118,3 +118,10 @@ def test_selfcond_input_full_size_sampled():
     rows = np.array([0, 1, 127, 128, 255, 256, 4000, 4095, 4096, 6143, 8064, 8191])
     got, ref, _, _ = _run(32, 262144, 2816, 2816, seed=0, rows=rows, E=E, E_t=E_t)
     _compare(got, ref, "full size")
+
+
+@pytest.mark.parametrize("D,F", [(16384, 128), (128, 65536)])
+def test_selfcond_input_maximum_widths(D, F):
+    """The largest widths the entry point accepts: D = 16384 and F = 65536."""
+    got, ref, _, _ = _run(1, 97, D, F, seed=D % 97 + F % 89)
+    _compare(got, ref, f"D={D} F={F}")
