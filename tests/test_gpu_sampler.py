@@ -175,3 +175,49 @@ def test_whole_step_tiny_workload():
     assert np.array_equal(nxt[same], ref.next_tokens[same])
     _say("   accepted:", int(acc.sum()), "exempt:", int(ex.sum()))
     assert acc.sum() == 1
+
+
+def test_step_captured_in_a_hip_graph():
+    """The vocabulary pass and accept/renoise queue only kernels on the caller's stream (no
+    allocation, memset or synchronisation), so a step can be captured in a HIP graph: three
+    replays, with eager state resets between them, reproduce the eager step bit for bit."""
+    from denoise_step_sampler_amd import runner
+    wl = synth.workload("lite", V=5000, d=256, n_canvas=3, seed=2)
+    wl.commit = np.array([0, 1, 0], np.uint8)
+    b = runner.from_workload(wl)
+    keys = ("lse", "entropy", "argmax_tok", "gumbel_tok", "selfcond", "next_tokens",
+            "accept_mask", "converged", "prev_argmax", "stable_count", "mean_entropy")
+
+    def reset():
+        b.prev_argmax.fill_(-1)
+        b.stable_count.zero_()
+
+    def step():
+        runner.denoise_step(b, wl.budget, wl.confidence, wl.stability, 5,
+                            stream=torch.cuda.current_stream())
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = {k: getattr(b, k).clone() for k in keys}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        reset()
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        reset()
+        for k in ("lse", "entropy", "selfcond", "mean_entropy"):
+            getattr(b, k).fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            x, y = getattr(b, k).cpu().numpy(), ref[k].cpu().numpy()
+            if x.dtype == np.float32:
+                x, y = x.view(np.uint32), y.view(np.uint32)
+            assert np.array_equal(x, y), k
