@@ -61,8 +61,22 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 // u near 1 included (measured on gfx950 against fp64), so the large Gumbel values that
 // decide the sample keep full relative precision.
 __device__ __forceinline__ float gumbel2s_from_word(uint32_t x) {
-  const float u = ((float)(x >> 9) + 0.5f) * 0x1p-23f;
+  // (x >> 9) 2^-23 + 2^-24 in one fma: every term is exact, so the value is the same
+  const float u = __builtin_fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);
   return -hw_log2(-hw_log2(u));
+}
+
+// a * b and a - b, each rounded on its own.  The device library's __fmul_rn / __fsub_rn are
+// plain operators compiled where contraction is allowed, so a product followed by a
+// difference would become one fma (one rounding) whatever pragma surrounds the call; these
+// carry no contraction permission, so the pair keeps both roundings.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float sub_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a - b;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -213,7 +213,7 @@ struct SoftCap {
 
 __device__ __forceinline__ float soft_cap_z2(float s, const SoftCap& sc) {
 #pragma clang fp contract(off)
-  return __fmul_rn(tanhf(__fmul_rn(s, sc.inv_c)), sc.cz);
+  return mul_rn(tanhf(mul_rn(s, sc.inv_c)), sc.cz);
 }
 
 // kCap: z2 = soft_cap_z2(S) in place of S c2; the argmax stays on S.
@@ -226,7 +226,8 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
                                         uint32_t k0, uint32_t k1, uint16_t* pt, int* ref_out,
                                         LdsRowAcc* lds_st, const int32_t* pexp = nullptr) {
   // HIP contracts a * b - c into one fma by default, which would round dz once instead of
-  // twice and break the bit-for-bit recomputation in the combine
+  // twice and break the bit-for-bit recomputation in the combine (mul_rn / sub_rn keep the
+  // two roundings)
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int vb0 = vt0 + 4 * (lane >> 5);
@@ -249,7 +250,7 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
   // equals (max_v S_v) c2 rounded.  With the cap: the z2 of S's argmax, which the block loop
   // recomputes bit for bit; tanh is increasing, so another entry can exceed it only by the
   // rounding of tanhf, which leaves its 2^(z2 - ref) within an ulp of 1 (bf16 1.0)
-  const float m = !kCap ? __fmul_rn(amv, c2)
+  const float m = !kCap ? mul_rn(amv, c2)
                         : (amv == -INFINITY ? -INFINITY : soft_cap_z2(amv, cap));
   const bool writer = lane < 32;
   {
@@ -297,20 +298,20 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float z2 = kCap ? sb[4 * q + j] : __fmul_rn(sb[4 * q + j], c2);
-        const float dz = __fsub_rn(z2, ref);
+        const float z2 = kCap ? sb[4 * q + j] : mul_rn(sb[4 * q + j], c2);
+        const float dz = sub_rn(z2, ref);
         const float g2 = gumbel2s_from_word(wd[j]);
         if (kMasked) {
           const bool ok = vb + j < V;
           const float pe = ok ? hw_exp2(dz) : 0.0f;
           ls += pe;
-          as += pe * (ok ? dz : 0.0f);
+          as = __builtin_fmaf(pe, ok ? dz : 0.0f, as);
           argmax_next(gv, gi, ok ? z2 + g2 : -INFINITY, vb + j);
           pv[j] = pe;
         } else {
           const float pe = hw_exp2(dz);
           ls += pe;
-          as += pe * dz;
+          as = __builtin_fmaf(pe, dz, as);
           argmax_next(gv, gi, z2 + g2, vb + j);  // entries in increasing order
           pv[j] = pe;
         }
@@ -1183,7 +1184,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
     cf[k] = 0.0f;
     if (tm[k] != -INFINITY) {
       const float ref = fminf(fmaxf(ceilf(tm[k]), -16777216.0f), 16777216.0f);
-      const float w = hw_exp2(__fsub_rn(tm[k], ref));
+      const float w = hw_exp2(sub_rn(tm[k], ref));
       const float wr = __uint_as_float(f32_to_bf16_bits(w) << 16);
       cf[k] = (w - wr) * hw_exp2(ref - m);
     }
