@@ -137,27 +137,39 @@ __global__ __launch_bounds__(256, 2) void k_ffw_gemm(FfwGemm g) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{0};
 
+  // fragments in two register sets: the reads of step ks + 1 are issued before the MFMAs of
+  // step ks, and the last step of a chunk (its operands in registers) is multiplied after
+  // the next barrier, behind the first reads of the next chunk
+  u32x4 fa[2][2], fb[2][2];
+  auto rd = [&](const lds_char* s, int ks, int q) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) fa[q][mb] = lds_read16(s + rdA[ks] + 32 * kFRow * mb);
+    fb[q][0] = lds_read16(s + rdB[ks]);
+    fb[q][1] = lds_read16(s + rdB[ks] + dB1);
+  };
+  auto mm = [&](int q) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[q][mb], fb[q][nb], acc[mb][nb]);
+  };
   issue(0, sa[0]);
   for (int kc = 0; kc < nk; ++kc) {
     // chunk kc has landed (this wave's copies, then every wave's at the barrier), and every
-    // wave is done with chunk kc - 1, whose stage takes chunk kc + 1
+    // wave is done reading chunk kc - 1, whose stage takes chunk kc + 1
     vm_wait<0>();
     __syncthreads();
     if (kc + 1 < nk) issue(kc + 1, sa[(kc + 1) & 1]);
     const lds_char* s = (const lds_char*)stg[kc & 1];
+    rd(s, 0, 0);
+    if (kc > 0) mm(1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 fa[2], fb[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) fa[mb] = lds_read16(s + rdA[ks] + 32 * kFRow * mb);
-      fb[0] = lds_read16(s + rdB[ks]);
-      fb[1] = lds_read16(s + rdB[ks] + dB1);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[mb], fb[nb], acc[mb][nb]);
+    for (int ks = 0; ks < 3; ++ks) {
+      rd(s, ks + 1, (ks + 1) & 1);
+      mm(ks & 1);
     }
   }
+  mm(1);
 
   // epilogue: lane holds column n = fr of each 32-wide block and rows acc32_m(i, lane)
 #pragma unroll
