@@ -233,18 +233,26 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
   const int vb0 = vt0 + 4 * (lane >> 5);
   float amv = -INFINITY;
   int ami = 0x7FFFFFFF;
-  auto scan = [&](const f32x16& sb, int vb) {
+  // entries past V exist only in the last tile: a full half tile scans without the checks
+  const bool full = vt0 + kHalf <= V;
+  auto scan = [&](auto masked, const f32x16& sb, int vb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int v = vb + 8 * (i >> 2) + (i & 3);
-      const float x = v < V ? sb[i] : -INFINITY;
+      const float x = (!decltype(masked)::value || v < V) ? sb[i] : -INFINITY;
       argmax_next(amv, ami, x, v);  // v increases along the scan
     }
   };
-  scan(s0, vb0);
-  scan(s1, vb0 + 32);
-  scan(s2, vb0 + 64);
-  scan(s3, vb0 + 96);
+  auto scan_all = [&](auto masked) {
+    scan(masked, s0, vb0);
+    scan(masked, s1, vb0 + 32);
+    scan(masked, s2, vb0 + 64);
+    scan(masked, s3, vb0 + 96);
+  };
+  if (full)
+    scan_all(std::false_type{});
+  else
+    scan_all(std::true_type{});
   argmax_merge(amv, ami, xor_f(amv, 32), xor_i(ami, 32));
   // the half tile's largest z2: rounding is monotone and c2 > 0, so max_v (S_v c2) rounded
   // equals (max_v S_v) c2 rounded.  With the cap: the z2 of S's argmax, which the block loop
@@ -338,7 +346,6 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       }
     }
   };
-  const bool full = vt0 + kHalf <= V;
   // one 32-entry block at a time, in a run-time loop (one copy of the block's code: unrolled,
   // the blocks' Philox streams would compete for the registers that hold the logits)
   auto run = [&](auto masked) {
