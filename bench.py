@@ -21,7 +21,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "denoise_step_sampler_amd", "csrc", "vocab_gemm.hip")
+# the logits kernel's source and the headers it includes (the counters are void once any changes)
+KERNEL_SRCS = [os.path.join(ROOT, "denoise_step_sampler_amd", "csrc", f)
+               for f in ("vocab_gemm.hip", "dg_device.h", "dg_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm_logits.json")
 
 
@@ -29,10 +31,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(path: str) -> str:
+def source_hash(paths) -> str:
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -43,7 +48,7 @@ def measured_traffic(workload: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_hash(KERNEL_SRC):
+    if rec.get("source_sha256") != source_hash(KERNEL_SRCS):
         return None
     w = rec.get("workloads", {}).get(workload)
     return None if w is None else float(w["hbm_bytes_per_launch"])

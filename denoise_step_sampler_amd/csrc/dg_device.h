@@ -61,8 +61,10 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 // u near 1 included (measured on gfx950 against fp64), so the large Gumbel values that
 // decide the sample keep full relative precision.
 __device__ __forceinline__ float gumbel2s_from_word(uint32_t x) {
-  // (x >> 9) 2^-23 + 2^-24 in one fma: every term is exact, so the value is the same
-  const float u = __builtin_fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);
+  // (x >> 9) 2^-23 + 2^-24, exactly: alignbit(0x7F, x, 9) = 0x3F800000 | (x >> 9) is the float
+  // 1 + (x >> 9) 2^-23, and subtracting 1 - 2^-24 from a number in [1, 2) is exact (the two are
+  // within a factor of two of each other)
+  const float u = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, x, 9)) - (1.0f - 0x1p-24f);
   return -hw_log2(-hw_log2(u));
 }
 
