@@ -174,7 +174,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the vocabulary pass shards by canvas or by vocabulary; see DESIGN.md)",
+              "(the vocabulary pass would shard by canvas or by vocabulary range)",
               file=sys.stderr)
         return 2
 
