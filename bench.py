@@ -173,7 +173,7 @@ def main() -> int:
                     help="full_loop only: linear temperature schedule over the 32 steps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the vocabulary pass would shard by canvas or by vocabulary range)",
               file=sys.stderr)
         return 2
