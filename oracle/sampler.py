@@ -116,10 +116,21 @@ def accept_renoise(entropy, argmax_tok, gumbel_tok, commit, n_canvas: int, C: in
 #   adaptive stop: count = (mean H < threshold) ? count + 1 : 0, stopped when count >=
 #   stability_steps; stability_steps = 0 turns it off (never stopped: the fixed schedule).
 #
-# Readings: x0_draw is the row's Gumbel-max sample and conf the probability of its argmax
-# token, both under the step's tempered distribution; the uniform token comes from the
-# same renoise stream as accept_renoise; the state starts at prev_argmax = -1,
-# prev_conf = +inf, committed = 0 (no previous posterior: nothing commits at the first step).
+# Margins: the commit test compares two probabilities of the argmax token; conf >= prev_conf
+# is ln conf >= ln prev_conf, a comparison of log-probabilities, i.e. of logits minus their
+# log-partition, so its margin is taken on that scale (nats), like the argmax and Gumbel
+# margins: mu_commit = |ln conf - ln prev_conf| (infinite where the argmax is unchanged and
+# the rule commits regardless); the stop test's margin is |mean H - threshold| (nats).
+#
+# Readings: the posterior is p = softmax(logits), untempered (section 4.2 computes it so
+# before the rule), so conf = max_v p_v is the probability of the argmax token under p and
+# the stop test reads the mean entropy of p (section 4.4); only the x0-hat draw uses the
+# annealed temperature tau(k) (section 4.2, item 4): x0_draw is the row's Gumbel-max sample
+# of softmax(logits / tau(k)).  The vocabulary pass gives both at once when it runs its
+# statistics at T = 1 and its draw at tau(k) (vocab_pass_rows' draw_temperature_row).  The
+# uniform token comes from the same renoise stream as accept_renoise; the state starts at
+# prev_argmax = -1, prev_conf = +inf, committed = 0 (no previous posterior: nothing commits
+# at the first step).
 # ---------------------------------------------------------------------------------------
 @dataclass
 class LiteResult:
@@ -131,7 +142,7 @@ class LiteResult:
     stable_count: np.ndarray    # int64 [n]
     converged: np.ndarray       # uint8 [n]
     mean_entropy: np.ndarray    # fp64 [n]
-    mu_commit: np.ndarray       # fp64 [R]: |conf - prev_conf| where argmax changed, else inf
+    mu_commit: np.ndarray       # fp64 [R]: |ln conf - ln prev_conf| where argmax changed, else inf
     mu_stop: np.ndarray         # fp64 [n]: |mean H - threshold|
 
 
@@ -163,8 +174,8 @@ def lite_step(entropy, argmax_tok, gumbel_tok, conf, n_canvas: int, C: int, V: i
         x[rows] = np.where(new, gt[rows], np.where(cm[rows], x[rows], ren))
         cm[rows] |= new
         final[rows] = np.where(cm[rows], x[rows], gt[rows])
-        with np.errstate(invalid="ignore"):
-            mu_c[rows] = np.where(same, np.inf, np.abs(cf[rows] - pc[rows]))
+        with np.errstate(invalid="ignore", divide="ignore"):
+            mu_c[rows] = np.where(same, np.inf, np.abs(np.log(cf[rows]) - np.log(pc[rows])))
         pa[rows] = am[rows]
         pc[rows] = cf[rows]
         meanH[c] = math.fsum(H[rows]) / C

@@ -20,12 +20,17 @@ Definitions followed (cited by page and section):
 * argmax token: the smallest v attaining max S (deterministic prediction used by the
   stability test; Technical Report sec. 3.3 "Adaptive stopping heuristic"; vLLM blog,
   convergence: committed tokens are the clean argmax).
-* Gumbel-max sample: the smallest v attaining max (z_v + g_v), g_v standard Gumbel noise
+* Gumbel-max sample: the smallest v attaining max (z'_v + g_v), g_v standard Gumbel noise
   from the Philox layout in ``oracle.philox`` (vLLM blog, sampler section: the candidate
   token is argmax(logits / T + Gumbel noise); DiffusionGemma Explained, "Sampling": accepted
-  positions take a sample of their distribution).
-* confidence of a row: the probability of its argmax token under the tempered (and capped)
-  distribution, p_{argmax} (the "conf" of the DiffusionGemma-Lite commit rule, section 4.2).
+  positions take a sample of their distribution).  z' = cap(S) / T_draw with the draw
+  temperature T_draw, which is T unless the caller gives another one: the
+  DiffusionGemma-Lite commit rule (section 4.2) reads its posterior p = softmax(logits)
+  untempered and applies the annealed tau(k) to the x0-hat draw alone (item 4), so that
+  sampler runs the statistics at T = 1 and the draw at T_draw = tau(k).
+* confidence of a row: the probability of its argmax token under the distribution the
+  statistics describe, p_{argmax} (the "conf" of the DiffusionGemma-Lite commit rule,
+  section 4.2).
 * self-conditioning expectation sc = sum_v p_v E_v = p_hat_0 E (Technical Report sec. 3.2
   eq. (6), the argument of FFW; DiffusionGemma Explained, "Self-conditioning").
 
@@ -33,7 +38,10 @@ Rows of commit canvases produce only the argmax token (vLLM blog: a converged ca
 its clean argmax and gets no further sampling or self-conditioning).
 
 Decision margins (reported, used by the parity tests to exempt near-ties):
-  mu_A = S_(1) - S_(2) and mu_G = y_(1) - y_(2) over distinct vocab indices.
+  mu_A = S_(1) - S_(2) and mu_G = y_(1) - y_(2) over distinct vocab indices, with
+  y = z' + g the Gumbel keys: the distance from the decision to the nearest input that
+  would change it (lowering the winner's key by more than the margin hands the decision to
+  the runner-up).
 """
 from __future__ import annotations
 
@@ -63,6 +71,8 @@ class RowResult:
     mu_argmax: np.ndarray   # fp64 margins
     mu_gumbel: np.ndarray   # fp64 margins, inf for commit rows
     conf: Optional[np.ndarray] = None  # fp64 probability of the argmax token, NaN for commit rows
+    argmax2: Optional[np.ndarray] = None  # runner-up of the argmax (-1 when V = 1)
+    gumbel2: Optional[np.ndarray] = None  # runner-up of the Gumbel draw (-1: none)
 
 
 def _top2_margin(x: np.ndarray) -> float:
@@ -74,16 +84,30 @@ def _top2_margin(x: np.ndarray) -> float:
     return float(best - rest.max())
 
 
+def _runner_up(x: np.ndarray) -> int:
+    """The smallest index attaining the largest value among the indices other than the
+    winner (the decision the margin separates the winner from); -1 for a single entry."""
+    if x.shape[0] < 2:
+        return -1
+    i = int(np.argmax(x))
+    y = x.copy()
+    y[i] = -np.inf
+    return int(np.argmax(y))
+
+
 def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
                     temperature_row: np.ndarray, commit_row: np.ndarray,
                     seed: int, step_row: np.ndarray, want_sc: bool = True,
-                    row_block: int = 64, softcap: Optional[float] = None) -> RowResult:
+                    row_block: int = 64, softcap: Optional[float] = None,
+                    draw_temperature_row: Optional[np.ndarray] = None) -> RowResult:
     """Oracle results for the listed global rows.
 
     E64            fp64 [V, d] (the widened bf16 embedding)
     h_bits         bf16 bits [R, d] of the whole batch (only ``rows`` are read)
     temperature_row, commit_row, step_row: per global row (indexable by row id)
     softcap        None: z = S / T; c > 0: z = c tanh(S / c) / T
+    draw_temperature_row: per global row, the temperature of the Gumbel-max draw alone
+                   (None: the same as temperature_row)
     """
     if softcap is not None and not (softcap > 0 and math.isfinite(softcap)):
         raise ValueError("softcap must be finite and > 0")
@@ -97,6 +121,8 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
     mu_a = np.zeros(n)
     mu_g = np.full(n, np.inf)
     conf = np.full(n, np.nan)
+    am2 = np.full(n, -1, dtype=np.int64)
+    gt2 = np.full(n, -1, dtype=np.int64)
     sc = np.full((n, d), np.nan) if want_sc else None
     for b0 in range(0, n, row_block):
         b1 = min(n, b0 + row_block)
@@ -108,23 +134,27 @@ def vocab_pass_rows(E64: np.ndarray, h_bits: np.ndarray, rows: Sequence[int],
             s = S[j]
             amax[i] = int(np.argmax(s))                  # first index attaining the max
             mu_a[i] = _top2_margin(s)
+            am2[i] = _runner_up(s)
             if commit_row[r]:
                 continue
             T = float(temperature_row[r])
-            z = (s if softcap is None else softcap * np.tanh(s / softcap)) / T
+            cs = s if softcap is None else softcap * np.tanh(s / softcap)
+            z = cs / T
+            Td = T if draw_temperature_row is None else float(draw_temperature_row[r])
             m = z.max()
             lse[i] = m + np.log(np.sum(np.exp(z - m)))
             p = np.exp(z - lse[i])
             ent[i] = float(np.sum(p * (lse[i] - z)))
             conf[i] = p[amax[i]]
             g = philox.gumbel_noise(r, V, seed, int(step_row[r]))
-            y = z + g
+            y = cs / Td + g
             gtok[i] = int(np.argmax(y))
             mu_g[i] = _top2_margin(y)
+            gt2[i] = _runner_up(y)
             if want_sc:
                 sc[i] = p @ E64
     return RowResult(rows=rows, lse=lse, entropy=ent, argmax=amax, gumbel=gtok, sc=sc,
-                     mu_argmax=mu_a, mu_gumbel=mu_g, conf=conf)
+                     mu_argmax=mu_a, mu_gumbel=mu_g, conf=conf, argmax2=am2, gumbel2=gt2)
 
 
 def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:

@@ -106,3 +106,48 @@ def test_adaptive_off_is_the_fixed_schedule():
     assert np.array_equal(off.stable_count, [5, 7])
     for k in ("x", "committed", "final", "prev_argmax", "prev_conf"):
         assert np.array_equal(getattr(on, k), getattr(off, k)), k
+
+
+def test_posterior_is_untempered_and_only_the_draw_is_annealed():
+    """The commit rule reads p = softmax(logits) and only the x0 draw uses tau(k)
+    (DiffusionGemma-Lite, section 4.2, the posterior line and item 4).  Hand-worked, V = 21,
+    E = identity, so the logits are h itself, one position over two steps:
+      step 0: S = (3, 0 x 20), argmax 0: conf = e^3 / (e^3 + 20) = 0.50107 at T = 1;
+      step 1: S = (0, 1.5, -30 x 19), argmax 1 (changed): conf = e^1.5 / (e^1.5 + 1 + 19 e^-30)
+              = 0.81757 >= 0.50107 -> the position commits and takes its x0 draw.
+    With the posterior tempered at tau = 0.25 instead, the confidences would be
+    e^12 / (e^12 + 20) = 0.99988 and sigma(6) = 0.99753: weaker, no commit.  The draw is the
+    same in both readings (softmax(S / tau))."""
+    from oracle import vocab_pass as ovp
+    from denoise_step_sampler_amd import synth
+    V = 21
+    E64 = np.eye(V)
+    s0 = np.zeros(V, np.float32)
+    s0[0] = 3.0
+    s1 = np.full(V, -30.0, np.float32)
+    s1[0], s1[1] = 0.0, 1.5
+    h = synth.round_to_bf16(np.stack([s0, s1]))
+    ones, tau = np.ones(2), np.full(2, 0.25)
+    r = ovp.vocab_pass_rows(E64, h, [0, 1], ones, np.zeros(2, bool), 3, np.zeros(2),
+                            want_sc=False, draw_temperature_row=tau)
+    assert list(r.argmax) == [0, 1]
+    assert abs(r.conf[0] - np.exp(3) / (np.exp(3) + 20)) < 1e-12
+    assert abs(r.conf[1] - np.exp(1.5) / (np.exp(1.5) + 1 + 19 * np.exp(-30))) < 1e-12
+    # the draw follows softmax(S / tau): its Gumbel keys are S / 0.25 + g
+    g0 = philox.gumbel_noise(0, V, 3, 0)
+    assert r.gumbel[0] == int(np.argmax(ovp.widen_bf16(h[0]) / 0.25 + g0))
+    # step 0 then step 1 of one position each (C = 1 canvases, two of them side by side)
+    C = 1
+    x = np.zeros(2, np.int64)
+    st = osm.lite_step(r.entropy[:1], r.argmax[:1], r.gumbel[:1], r.conf[:1], 1, C, V, 0.1, 0,
+                       3, 0, x[:1], np.full(1, -1), np.full(1, np.inf), np.zeros(1, np.uint8),
+                       np.zeros(1))
+    st2 = osm.lite_step(r.entropy[1:], r.argmax[1:], r.gumbel[1:], r.conf[1:], 1, C, V, 0.1, 0,
+                        3, 1, st.x, st.prev_argmax, st.prev_conf, st.committed, st.stable_count)
+    assert st.committed[0] == 0 and st2.committed[0] == 1   # untempered: stronger -> commit
+    assert st2.x[0] == r.gumbel[1]                          # the x0 draw at tau
+    # the tempered reading of the same logits (statistics at tau) would not commit
+    rt = ovp.vocab_pass_rows(E64, h, [0, 1], tau, np.zeros(2, bool), 3, np.zeros(2),
+                             want_sc=False)
+    assert rt.conf[1] < rt.conf[0]
+    assert list(rt.gumbel) == list(r.gumbel)                # same draw either way
