@@ -20,7 +20,7 @@ DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = ra
 DG_CANVAS = 256
 
 EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass", "dg_vocab_pass_softcap",
-            "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
+            "dg_vocab_pass_ex", "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
             "dg_selfcond_input", "dg_lite_step", "dg_quantize_embedding_fp8",
             "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8", "dg_status_string",
             "dg_last_error")
@@ -52,6 +52,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_vocab_pass_softcap.argtypes = [P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P,
                                           F]
     lib.dg_vocab_pass_softcap.restype = I
+    lib.dg_vocab_pass_ex.argtypes = [P, P, I, I, I, I, P, P, F, P, U64, P, P, P, P, P, P, P, SZ, P]
+    lib.dg_vocab_pass_ex.restype = I
     lib.dg_accept_renoise.argtypes = [P, P, P, P, I, I, I, F, F, I, U64, P, P, P, P, P, P, P, P]
     lib.dg_accept_renoise.restype = I
     lib.dg_q_sample.argtypes = [P, I, I, I, P, U64, P, P]
@@ -132,6 +134,35 @@ def dg_vocab_pass_softcap(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: in
     """dg_vocab_pass on the soft-capped logits softcap * tanh(S / softcap)."""
     _vocab_pass(float(softcap), E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse,
                 entropy, argmax_tok, gumbel_tok, selfcond, workspace, stream)
+
+
+def dg_vocab_pass_ex(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: int, V: int, d: int,
+                     temperature: torch.Tensor, draw_temperature: Optional[torch.Tensor],
+                     softcap: float, commit: Optional[torch.Tensor], seed: int,
+                     step: torch.Tensor, lse: Optional[torch.Tensor], entropy: torch.Tensor,
+                     argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                     selfcond: Optional[torch.Tensor], workspace: torch.Tensor,
+                     stream=None) -> None:
+    """Statistics at `temperature`, the Gumbel-max draw at `draw_temperature` (None: the
+    same); softcap 0 for none."""
+    R = n_canvas * C
+    lib = load()
+    st = lib.dg_vocab_pass_ex(
+        _bf16_ptr(E, V * d, "E"), _bf16_ptr(h, R * d, "h"), n_canvas, C, V, d,
+        _ptr(temperature, torch.float32, n_canvas, "temperature"),
+        _ptr(draw_temperature, torch.float32, n_canvas, "draw_temperature"),
+        ctypes.c_float(softcap),
+        _ptr(commit, torch.uint8, n_canvas, "commit"),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(step, torch.int32, n_canvas, "step"),
+        _ptr(lse, torch.float32, R, "lse"),
+        _ptr(entropy, torch.float32, R, "entropy"),
+        _ptr(argmax_tok, torch.int32, R, "argmax_tok"),
+        _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
+        _ptr(selfcond, torch.float32, R * d, "selfcond"),
+        _ptr(workspace, torch.uint8, None, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check(st)
 
 
 def _vocab_pass(softcap, E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,

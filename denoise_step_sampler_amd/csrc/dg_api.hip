@@ -24,30 +24,11 @@ dg_status hip_fail(hipError_t e, const char* what) {
   return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Path of the vocabulary pass.  Default: the two-GEMM path (every d % 64 == 0).
-// DG_VOCAB_PATH=fused selects the cooperative single-kernel path (when its tiling covers d
-// and the device holds a 16-workgroup group per XCD), DG_VOCAB_PATH=split the four-kernel
-// path with fp32 tile weights.  The tests run all three.
-enum Path { kGemm, kFused, kSplit };
+// Path of the vocabulary pass, from the shape alone: the two-GEMM path for d % 128 == 0, the
+// split kernels (fp32 tile weights, four plain kernels) for the other multiples of 64.
+enum Path { kGemm, kSplit };
 
-int device_cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return n;
-}
-
-Path pick_path(int d, int* n_wg) {
-  const char* e = getenv("DG_VOCAB_PATH");
-  if (e != nullptr && strcmp(e, "split") == 0) return kSplit;
-  if (e != nullptr && strcmp(e, "fused") == 0 && dg::fused_supported(d)) {
-    int n = device_cu_count();
-    if (n <= 0) n = 256;  // sizing without a device: MI355X
-    *n_wg = n;
-    if ((n / 8) >= 16) return kFused;
-  }
-  return dg::gemm_supported(d) ? kGemm : kSplit;
-}
+Path pick_path(int d) { return dg::gemm_supported(d) ? kGemm : kSplit; }
 
 // Largest batch for which the FP8 pass streams the transposed codes through the expectation
 // pass (measured: one canvas 0.84 ms against 0.90 on bf16 rows and 1.27 on the dequantised
@@ -60,12 +41,8 @@ size_t fp8_offset(int n_canvas, int V, int d) {
 }
 
 size_t plan_bytes(int n_canvas, int V, int d) {
-  int n_wg = 0;
-  switch (pick_path(d, &n_wg)) {
-    case kGemm: return dg::gemm_plan(n_canvas, V, d).bytes;
-    case kFused: return dg::fused_plan(n_canvas, V, d, n_wg).bytes;
-    default: return dg::vocab_plan(n_canvas, V, d).bytes;
-  }
+  return pick_path(d) == kGemm ? dg::gemm_plan(n_canvas, V, d).bytes
+                               : dg::vocab_plan(n_canvas, V, d).bytes;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -124,13 +101,7 @@ size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d) {
   const dg_status s = check_vocab_shape(n_canvas, C, V, d);
   memcpy(g_err, keep, sizeof(g_err));
   if (s != DG_OK) return 0;
-  // The soft-capped pass always runs on the two-GEMM path: size for whichever is larger.
-  size_t n = plan_bytes(n_canvas, V, d);
-  if (dg::gemm_supported(d)) {
-    const size_t g = dg::gemm_plan(n_canvas, V, d).bytes;
-    if (g > n) n = g;
-  }
-  return n;
+  return plan_bytes(n_canvas, V, d);
 }
 
 }  // extern "C"
@@ -143,14 +114,17 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
                      size_t workspace_bytes, void* stream, float softcap,
                      bool force_gemm = false, const uint8_t* E8 = nullptr,
-                     const int32_t* E_exp = nullptr, const uint8_t* E8T = nullptr) {
+                     const int32_t* E_exp = nullptr, const uint8_t* E8T = nullptr,
+                     const float* draw_temperature = nullptr) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
     return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (softcap != 0.0f) force_gemm = true;
+  if (softcap != 0.0f || draw_temperature != nullptr) force_gemm = true;
   if (force_gemm && !dg::gemm_supported(d))
-    return fail(DG_ERR_UNSUPPORTED, "the soft cap and the FP8 embedding need d %% 128 == 0 (d=%d)",
+    return fail(DG_ERR_UNSUPPORTED,
+                "the soft cap, the draw temperature and the FP8 embedding need d %% 128 == 0 "
+                "(d=%d)",
                 d);
   if (!aligned16(E) || !aligned16(h))
     return fail(DG_ERR_INVALID_ARG, "E and h must be 16-byte aligned");
@@ -170,6 +144,7 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.V = V;
   a.d = d;
   a.temperature = temperature;
+  a.draw_temperature = draw_temperature;
   a.commit = commit;
   split_seed(seed, &a.k0, &a.k1);
   a.step = step;
@@ -183,21 +158,11 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.E_exp = E_exp;
   a.E8T = E8T;
   a.E8T_pitch = dg::fp8_transposed_pitch(V);
-  int n_wg = 0;
-  hipError_t e;
-  switch (force_gemm ? kGemm : pick_path(d, &n_wg)) {
-    case kGemm:
-      e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, (hipStream_t)stream);
-      break;
-    case kFused:
-      e = dg::fused_launch(a, dg::fused_plan(n_canvas, V, d, n_wg), workspace,
-                           (hipStream_t)stream);
-      break;
-    default:
-      e = dg::vocab_pass_launch(a, dg::vocab_plan(n_canvas, V, d), workspace,
-                                (hipStream_t)stream);
-      break;
-  }
+  const hipError_t e =
+      (force_gemm || pick_path(d) == kGemm)
+          ? dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, (hipStream_t)stream)
+          : dg::vocab_pass_launch(a, dg::vocab_plan(n_canvas, V, d), workspace,
+                                  (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
 }
@@ -227,6 +192,20 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
     return fail(DG_ERR_INVALID_ARG, "softcap must be finite and > 0");
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap);
+}
+
+dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
+                           int d, const float* temperature, const float* draw_temperature,
+                           float softcap, const uint8_t* commit, uint64_t seed,
+                           const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
+                           int32_t* gumbel_tok, float* selfcond, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
+    return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
+  return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
+                    false, nullptr, nullptr, nullptr, draw_temperature);
 }
 
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {

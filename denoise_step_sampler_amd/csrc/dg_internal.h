@@ -16,6 +16,8 @@ struct VocabArgs {
   int V;
   int d;
   const float* temperature;
+  const float* draw_temperature;  // temperature of the Gumbel-max draw alone, or null (the
+                                  // draw uses `temperature`; two-GEMM path only)
   const uint8_t* commit;
   uint32_t k0, k1;  // Philox key
   const int32_t* step;
@@ -89,22 +91,8 @@ GemmPlan gemm_plan(int n_canvas, int V, int d);
 hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
                        hipStream_t stream);
 
-// Fused cooperative path (vocab_fused.hip).
-struct FusedPlan {
-  int n_wg;       // workgroups launched (one per CU)
-  int per_xcd;    // workgroups per XCD
-  int n_groups;   // groups of 16 x halves workgroups (one or two per XCD)
-  int halves;     // halves per group: 2 when an XCD holds 32 workgroups
-  size_t R;
-  int n_tiles;
-  int s_v;        // vocabulary ranges per canvas
-  size_t off_sync, off_order, off_ring, off_ring_ref, off_st, off_accp, off_accM;
-  size_t bytes;
-};
-bool fused_supported(int d);
-FusedPlan fused_plan(int n_canvas, int V, int d, int n_wg);
-hipError_t fused_launch(const VocabArgs& a, const FusedPlan& p, void* workspace,
-                        hipStream_t stream);
+// Split path (vocab_pass.hip): the pass for widths the two-GEMM path does not tile
+// (d % 128 != 0).
 hipError_t vocab_pass_launch(const VocabArgs& a, const VocabPlan& p, void* workspace,
                              hipStream_t stream);
 

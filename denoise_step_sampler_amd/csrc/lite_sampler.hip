@@ -2,9 +2,12 @@
 // section 4.4 "Entropy-bounded adaptive stopping") on the vocabulary pass outputs:
 //
 //   k_lite_conf  conf_r = exp(z_am - lse_r), the probability of the row's argmax token under
-//                its tempered (and capped) distribution; z_am = S_am / T_c with S_am = h_r .
-//                E[am] recomputed as one 2d-byte dot product per row (one wave per row, 16-byte
-//                loads, fp32 accumulation), since the pass keeps only the argmax's index.
+//                the (capped) distribution the pass's statistics describe; z_am = S_am / T_c
+//                with T_c the statistics temperature (1 for the page's untempered posterior
+//                p = softmax(logits); the annealed tau(k) enters only the pass's x0-hat draw)
+//                and S_am = h_r . E[am] recomputed as one 2d-byte dot product per row (one
+//                wave per row, 16-byte loads, fp32 accumulation), since the pass keeps only the
+//                argmax's index.
 //   k_lite_step  one workgroup per canvas, one thread per position: the unchanged-or-stronger
 //                commit (argmax == prev or conf >= prev_conf), frozen commits, uniform
 //                redraw of the rest, the returned canvas, and the entropy-only stop counter

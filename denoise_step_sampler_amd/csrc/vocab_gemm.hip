@@ -219,12 +219,15 @@ __device__ __forceinline__ float soft_cap_z2(float s, const SoftCap& sc) {
 // kCap: z2 = soft_cap_z2(S) in place of S c2; the argmax stays on S.
 // kScaleP: the stored weights are 2^pexp[v] times the bf16 weights (exact; the expectation
 // pass then multiplies them by the FP8 codes), the normaliser sums the unscaled ones.
-template <bool kHeavy, bool kCap, bool kScaleP = false>
+// kSep: the Gumbel key takes its own temperature, c2g = log2(e) / T_draw (S c2g, or
+// tanh(S / c) c c2g with the cap) in place of z2; the statistics keep c2.
+template <bool kHeavy, bool kCap, bool kScaleP = false, bool kSep = false>
 __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, const f32x16& s2,
                                         const f32x16& s3, int vt0, int V, float c2,
                                         const SoftCap& cap, uint32_t row, uint32_t step,
                                         uint32_t k0, uint32_t k1, uint16_t* pt, int* ref_out,
-                                        LdsRowAcc* lds_st, const int32_t* pexp = nullptr) {
+                                        LdsRowAcc* lds_st, const int32_t* pexp = nullptr,
+                                        float c2g = 0.0f, float czg = 0.0f) {
   // HIP contracts a * b - c into one fma by default, which would round dz once instead of
   // twice and break the bit-for-bit recomputation in the combine (mul_rn / sub_rn keep the
   // two roundings)
@@ -306,7 +309,10 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
       float pv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float z2 = kCap ? sb[4 * q + j] : mul_rn(sb[4 * q + j], c2);
+        // with kSep and the cap, sb holds tanh(S / c): z2 = t (c c2), the key's t (c c2g)
+        const float z2 = kCap ? (kSep ? mul_rn(sb[4 * q + j], cap.cz) : sb[4 * q + j])
+                              : mul_rn(sb[4 * q + j], c2);
+        const float zk = !kSep ? z2 : kCap ? mul_rn(sb[4 * q + j], czg) : mul_rn(sb[4 * q + j], c2g);
         const float dz = sub_rn(z2, ref);
         const float g2 = gumbel2s_from_word(wd[j]);
         if (kMasked) {
@@ -314,13 +320,13 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
           const float pe = ok ? hw_exp2(dz) : 0.0f;
           ls += pe;
           as = __builtin_fmaf(pe, ok ? dz : 0.0f, as);
-          argmax_next(gv, gi, ok ? z2 + g2 : -INFINITY, vb + j);
+          argmax_next(gv, gi, ok ? zk + g2 : -INFINITY, vb + j);
           pv[j] = pe;
         } else {
           const float pe = hw_exp2(dz);
           ls += pe;
           as = __builtin_fmaf(pe, dz, as);
-          argmax_next(gv, gi, z2 + g2, vb + j);  // entries in increasing order
+          argmax_next(gv, gi, zk + g2, vb + j);  // entries in increasing order
           pv[j] = pe;
         }
       }
@@ -359,10 +365,12 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
         default: sb = s3; break;
       }
       // capped z2 of the whole block first, so that tanhf's temporaries are dead before
-      // the noise's are live
+      // the noise's are live (with kSep, tanh(S / c) alone: both products are formed below)
       if (kCap) {
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sb[i] = soft_cap_z2(sb[i], cap);
+        for (int i = 0; i < 16; ++i)
+          sb[i] = kSep ? tanhf(mul_rn(sb[i], cap.inv_c)) : soft_cap_z2(sb[i], cap);
       }
       block(masked, sb, vb0 + 32 * mb, pt + 512 * mb);
     }
@@ -441,7 +449,7 @@ __device__ __forceinline__ u32x4 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
 // steps, widened to bf16 in registers; the h fragments use the same permutation of K within
 // the chunk (step 2 j + t, lane half f: K = 32 j + 16 f + 8 t + 0..7), and the accumulator of
 // entry v is scaled by 2^E_exp[v] before the epilogue (exact).
-template <bool kCap, bool kF8>
+template <bool kCap, bool kF8, bool kSep = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   constexpr int kERow = kF8 ? kKC1 : kRow1;    // bytes of one staged E row
   constexpr int kHOff = kTile * kERow;         // 256 E rows, then 256 h rows
@@ -658,6 +666,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   const float c2 = kLog2e / g.a.temperature[c];
   SoftCap cap{};
   if (kCap) cap = SoftCap{1.0f / g.a.softcap, g.a.softcap * c2};
+  // kSep: the draw's constants (log2(e) / T_draw, and c log2(e) / T_draw with the cap)
+  const float c2g = kSep ? kLog2e / g.a.draw_temperature[c] : c2;
+  const float czg = kSep && kCap ? g.a.softcap * c2g : 0.0f;
   const uint32_t step = (uint32_t)g.a.step[c];
   const uint32_t k0 = g.a.k0, k1 = g.a.k1;
   const int rloc0 = 64 * rq + fr;  // row (in the canvas) of block 0; block 1 is 32 rows on
@@ -727,10 +738,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
       epi_row<true, kCap, true>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap,
                                 row1, step, k0, k1, prow1 + vblk, rout0 + 32, st1p, g.a.E_exp);
     } else if (heavy) {
-      epi_row<true, kCap>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
-                          step, k0, k1, prow0 + vblk, rout0, st0p);
-      epi_row<true, kCap>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap, row1,
-                          step, k0, k1, prow1 + vblk, rout0 + 32, st1p);
+      epi_row<true, kCap, false, kSep>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2,
+                                       cap, row0, step, k0, k1, prow0 + vblk, rout0, st0p,
+                                       nullptr, c2g, czg);
+      epi_row<true, kCap, false, kSep>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2,
+                                       cap, row1, step, k0, k1, prow1 + vblk, rout0 + 32, st1p,
+                                       nullptr, c2g, czg);
     } else {
       epi_row<false, false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
                             step, 0, 0, prow0, rout0, st0p);
@@ -1397,12 +1410,18 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid1((unsigned)(kWG * p.n_rounds));
+  const bool cap = a.softcap != 0.0f, sep = a.draw_temperature != nullptr;
   if (a.E8 != nullptr) {
-    if (a.softcap != 0.0f)
+    if (cap)
       hipLaunchKernelGGL((k_gemm_logits<true, true>), grid1, dim3(512), 0, stream, g);
     else
       hipLaunchKernelGGL((k_gemm_logits<false, true>), grid1, dim3(512), 0, stream, g);
-  } else if (a.softcap != 0.0f) {
+  } else if (sep) {
+    if (cap)
+      hipLaunchKernelGGL((k_gemm_logits<true, false, true>), grid1, dim3(512), 0, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm_logits<false, false, true>), grid1, dim3(512), 0, stream, g);
+  } else if (cap) {
     hipLaunchKernelGGL((k_gemm_logits<true, false>), grid1, dim3(512), 0, stream, g);
   } else {
     hipLaunchKernelGGL((k_gemm_logits<false, false>), grid1, dim3(512), 0, stream, g);

@@ -44,6 +44,9 @@ class VocabBuffers:
     mean_entropy: torch.Tensor
     C: int = B.DG_CANVAS
     extra: dict = field(default_factory=dict)
+    # temperature of the Gumbel-max draw alone ([n_canvas] fp32), or None: the draw uses
+    # `temperature` (the DiffusionGemma-Lite sampler: statistics at 1, the draw at tau(k))
+    draw_temperature: Optional[torch.Tensor] = None
 
     @property
     def R(self) -> int:
@@ -88,7 +91,14 @@ def from_workload(wl, want_selfcond: bool = True, device="cuda", E: Optional[tor
 
 
 def vocab_pass(b: VocabBuffers, seed: int, stream=None, softcap: Optional[float] = None) -> None:
-    """softcap: None for the plain logits, c > 0 for c tanh(S / c) before the temperature."""
+    """softcap: None for the plain logits, c > 0 for c tanh(S / c) before the temperature.
+    With b.draw_temperature the Gumbel-max draw takes that temperature (dg_vocab_pass_ex)."""
+    if b.draw_temperature is not None:
+        B.dg_vocab_pass_ex(b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.draw_temperature,
+                           0.0 if softcap is None else float(softcap), b.commit, seed, b.step,
+                           b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace,
+                           stream=stream)
+        return
     args = (b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed, b.step, b.lse,
             b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace)
     if softcap is None:

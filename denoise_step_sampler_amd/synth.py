@@ -191,15 +191,17 @@ def workload(name: str, seed: int = 0, V: Optional[int] = None, d: Optional[int]
     return wl
 
 
-def loop_scale(k: int) -> float:
-    """Signal strength of denoise step k in the full-loop workload: 0.5 + 0.25 k."""
-    return 0.5 + 0.25 * k
+def loop_scale(k: int, signal=(0.5, 0.25)) -> float:
+    """Signal strength of denoise step k in the full-loop workload: a + b k, (a, b) = (0.5,
+    0.25) for the workload as specified (a test may ask for a faster-growing signal)."""
+    return signal[0] + signal[1] * k
 
 
 def loop_hidden(wl: VocabWorkload, k: int, accepted_prev: Optional[np.ndarray]) -> np.ndarray:
     """Hidden state of step k of the full-loop workload.  ``accepted_prev`` (bool [R]) is the
-    previous step's accept mask (None at step 0: every position keeps its signal)."""
-    scale = np.full(wl.R, loop_scale(k), dtype=np.float32)
+    previous step's accept mask (None at step 0: every position keeps its signal).  The signal
+    schedule is wl.extra["signal"] if set, else (0.5, 0.25)."""
+    scale = np.full(wl.R, loop_scale(k, wl.extra.get("signal", (0.5, 0.25))), dtype=np.float32)
     return make_hidden(wl.E, wl.targets, scale, wl.seed, step=k, keep_signal=accepted_prev)
 
 

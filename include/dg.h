@@ -112,6 +112,28 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 float softcap);
 
+/* dg_vocab_pass_ex -- dg_vocab_pass_softcap (softcap > 0) or dg_vocab_pass (softcap = 0) whose
+ * Gumbel-max draw may use its own temperature.  The statistics (lse, entropy, selfcond) describe
+ * p = softmax(cap(S) / temperature[c]); the sample is
+ *   gumbel_tok[r] = smallest v attaining max_v (cap(S_v) / draw_temperature[c] + g_v)
+ * with the same noise g as dg_vocab_pass.  This is the DiffusionGemma-Lite sampler's split
+ * ([LITE] sec. 4.2 "The commit rule": the posterior p = softmax(logits) that the commit rule
+ * and the stop entropy of sec. 4.4 read is untempered, and only the x0-hat draw of step k
+ * uses the annealed temperature tau(k), item 4): call it with temperature = 1 and
+ * draw_temperature = tau(k).  draw_temperature = NULL draws at `temperature`, which is
+ * dg_vocab_pass_softcap / dg_vocab_pass exactly (same bits).
+ *  draw_temperature  [n_canvas] fp32, > 0, or NULL.
+ *  softcap           0 (no cap) or > 0 and finite ([host] scalar).
+ * Other arguments, layouts and outputs as dg_vocab_pass.  A draw temperature or a cap needs
+ * the default (two-GEMM) path: d % 128 == 0, else DG_ERR_UNSUPPORTED.
+ * Errors: as dg_vocab_pass_softcap. */
+dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
+                           int d, const float* temperature, const float* draw_temperature,
+                           float softcap, const uint8_t* commit, uint64_t seed,
+                           const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
+                           int32_t* gumbel_tok, float* selfcond, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* dg_quantize_embedding_fp8 -- the tied embedding as FP8 ([VLLM] ships an FP8 checkpoint with
  * quantised weights; the pages give no scale scheme): OCP E4M3 codes (bias 7, largest finite
  * 448, no infinities) with one power-of-two scale 2^k per row,
@@ -186,8 +208,11 @@ dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
 /* dg_lite_step -- the DiffusionGemma-Lite sampler step, a second sampler on the vocabulary
  * pass outputs ([LITE] sec. 4.2 "The commit rule", sec. 4.4 "Entropy-bounded adaptive
  * stopping").  Per row r of canvas c, with conf_r the probability of the argmax token under
- * the step's tempered distribution, exp(z_am - lse_r), z_am = cap(h_r . E[am]) / T_c
- * (cap(S) = softcap tanh(S / softcap), or S when softcap == 0):
+ * the distribution the pass's statistics describe, exp(z_am - lse_r), z_am =
+ * cap(h_r . E[am]) / T_c (cap(S) = softcap tanh(S / softcap), or S when softcap == 0).  The
+ * page's posterior is untempered (p = softmax(logits); only the x0-hat draw uses the annealed
+ * tau(k)), so the pass for this sampler is dg_vocab_pass_ex with temperature = 1 and
+ * draw_temperature = tau(k), and T_c here is that statistics temperature (1):
  *   commit = (argmax_tok == prev_argmax) || (conf >= prev_conf)   (unchanged-or-stronger)
  *   fresh  = commit && !committed                                 (frozen tokens stay)
  *   x      = fresh ? gumbel_tok : committed ? x : uniform token of the renoise counter
@@ -199,8 +224,9 @@ dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,
  * Initial state (no previous posterior, nothing commits at the first step): prev_argmax = -1,
  * prev_conf = +inf, committed = 0, stable_count = 0.
  *  h, E, temperature, lse, entropy, argmax_tok, gumbel_tok: the vocabulary pass's inputs and
- *            outputs of the step (lse, entropy, gumbel_tok of every row must be written: no
- *            commit canvases); softcap: the value given to dg_vocab_pass_softcap, else 0.
+ *            outputs of the step (temperature: the statistics temperature the pass was given;
+ *            lse, entropy, gumbel_tok of every row must be written: no commit canvases);
+ *            softcap: the value given to the pass, else 0.
  *  entropy_threshold finite; stability_steps >= 0.
  *  conf      [R] fp32 out.   x, prev_argmax [R] int32 in/out; prev_conf [R] fp32 in/out;
  *  committed [R] uint8 in/out; stable_count [n_canvas] in/out; final_tokens [R] out or NULL;

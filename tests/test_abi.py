@@ -29,7 +29,8 @@ def _lib():
 def test_header_symbols_exported():
     decl = _declared()
     assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass",
-                         "dg_vocab_pass_softcap", "dg_accept_renoise", "dg_q_sample",
+                         "dg_vocab_pass_softcap", "dg_vocab_pass_ex", "dg_accept_renoise",
+                         "dg_q_sample",
                          "dg_selfcond_input_workspace_size", "dg_selfcond_input",
                          "dg_lite_step", "dg_quantize_embedding_fp8",
                          "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8",
@@ -172,3 +173,22 @@ def test_selfcond_input_workspace_and_validation_on_host():
     # workspace too small
     assert f(None, dummy, dummy, None, None, None, None, None, 1, 256, 100, 64, 64, 1e-6,
              dummy, dummy, 16, None) == 3
+
+
+def test_vocab_pass_ex_refusals_on_host():
+    """dg_vocab_pass_ex refuses a bad soft cap, and a draw temperature on a width the two-GEMM
+    path does not tile, before any device work; the binding declares the symbol."""
+    from denoise_step_sampler_amd import binding
+    lib = _lib()
+    assert "dg_vocab_pass_ex" in binding.EXPORTED
+    f = lib.dg_vocab_pass_ex
+    P = 1 << 20
+    for c in (-1.0, float("inf"), float("nan")):
+        st = f(P, P, 1, 256, 4096, 256, P, P, c, None, 0, P, None, P, P, P, None, P, 1 << 40, None)
+        assert st == binding.DG_ERR_INVALID_ARG, c
+        assert b"softcap" in lib.dg_last_error()
+    st = f(P, P, 1, 256, 4096, 192, P, P, 0.0, None, 0, P, None, P, P, P, None, P, 1 << 40, None)
+    assert st == binding.DG_ERR_UNSUPPORTED
+    assert b"128" in lib.dg_last_error()
+    st = f(P, P, 1, 256, 4096, 256, None, P, 0.0, None, 0, P, None, P, P, P, None, P, 1 << 40, None)
+    assert st == binding.DG_ERR_INVALID_ARG       # temperature is required

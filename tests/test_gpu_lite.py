@@ -1,12 +1,15 @@
 """The DiffusionGemma-Lite sampler through the C ABI: several denoise steps of vocabulary pass +
 dg_lite_step on the GPU against the oracle's vocabulary pass + lite_step, each side carrying
-its own state from the same initial state.  Hidden states of step k keep the signal at the
-positions the oracle had committed (so both sides see the same inputs).  Every step's
-confidences (|delta| <= 2e-3 |ref| + 1e-6), commit masks, canvas tokens, returned canvas,
-stop counters and flags must agree bit for bit, except decisions whose oracle margin is below
-1e-4 (|conf - prev_conf| for the commit test, |mean H - threshold| for the stop test,
-argmax / Gumbel margins): the comparison stops at the first such decision that differs,
-after which the two trajectories may legitimately part."""
+its own state from the same initial state.  As the Lite page defines the step (section 4.2:
+the posterior p = softmax(logits) is untempered, only the x0-hat draw of step k uses tau(k),
+annealed linearly; section 4.4: the stop test reads the mean entropy of p), the pass runs its
+statistics at T = 1 and its Gumbel draw at tau(k) (dg_vocab_pass_ex).  Hidden states of step
+k keep the signal at the positions the oracle had committed (so both sides see the same
+inputs).  Every step's confidences (|delta| <= 2e-3 |ref| + 1e-6), commit masks, canvas
+tokens, returned canvas, stop counters and flags must agree bit for bit, except decisions
+whose oracle margin is below 1e-4 (|ln conf - ln prev_conf| for the commit test,
+|mean H - threshold| for the stop test, argmax / Gumbel margins): the comparison stops at the
+first such decision that differs, after which the two trajectories may legitimately part."""
 import sys
 
 import numpy as np
@@ -36,14 +39,15 @@ def _gpu():
     yield
 
 
-@pytest.mark.parametrize("softcap,stability,thr", [(None, 2, 7.5), (20.0, 0, 6.0)])
+@pytest.mark.parametrize("softcap,stability,thr", [(None, 2, 7.812), (20.0, 0, 6.0)])
 def test_lite_sampler_loop(softcap, stability, thr):
-    """Stop switched on with a threshold between the canvases' mean entropies (two canvases
-    stop), and switched off with a soft cap."""
+    """Stop switched on with a threshold among the canvases' mean entropies (in the oracle,
+    canvases 0 and 1 stop after step 5, 2 and 3 after step 7), and switched off with a soft
+    cap; tau(k) anneals from 1.0 toward 0.5 over the eight steps."""
     from denoise_step_sampler_amd import runner
     wl = synth.workload("full_loop", V=4096, d=256, n_canvas=4, seed=3)
     n, V, d = 4, wl.V, wl.d
-    wl.temperature = np.linspace(0.6, 1.0, n).astype(np.float32)
+    wl.temperature = np.ones(n, np.float32)     # the posterior is softmax(logits)
     E64 = ovp.widen_bf16(wl.E)
     E_t = runner.bf16_tensor(wl.E)
     seed, steps = 12, 8
@@ -52,20 +56,24 @@ def test_lite_sampler_loop(softcap, stability, thr):
              cm=np.zeros(n * C, np.uint8), cnt=np.zeros(n, np.int64))
     b = None
     compared = 0
+    stopped = np.zeros(n, bool)
     for k in range(steps):
+        tau = runner.temperature_schedule(k, steps, 1.0, 0.5)
         h = synth.loop_hidden(wl, k, o["cm"].astype(bool) if k else None)
         if b is None:
             b = runner.allocate(n, V, d, E_t, runner.bf16_tensor(h), wl.temperature, None,
                                 np.full(n, k, np.int32))
+            b.draw_temperature = torch.empty(n, dtype=torch.float32, device="cuda")
         else:
             b.h.copy_(runner.bf16_tensor(h))
             b.step.fill_(k)
+        b.draw_temperature.fill_(tau)
         runner.vocab_pass(b, seed, softcap=softcap)
         runner.lite_step(b, st, thr, stability, seed, softcap=softcap)
         torch.cuda.synchronize()
         ref = ovp.vocab_pass_rows(E64, h, np.arange(n * C), np.repeat(wl.temperature, C),
                                   np.zeros(n * C, bool), seed, np.full(n * C, k), want_sc=False,
-                                  softcap=softcap)
+                                  softcap=softcap, draw_temperature_row=np.full(n * C, tau))
         r = osm.lite_step(ref.entropy, ref.argmax, ref.gumbel, ref.conf, n, C, V, thr,
                           stability, seed, k, o["x"], o["pa"], o["pc"], o["cm"], o["cnt"])
         conf = st.conf.cpu().numpy()
@@ -88,4 +96,7 @@ def test_lite_sampler_loop(softcap, stability, thr):
         _say(f"   step {k}: committed {int(r.committed.sum())}, mean H "
              f"{np.round(r.mean_entropy, 3).tolist()}, stopped {r.converged.tolist()}")
         o = dict(x=r.x, pa=r.prev_argmax, pc=r.prev_conf, cm=r.committed, cnt=r.stable_count)
+        stopped |= r.converged.astype(bool)
     assert compared >= 4
+    if stability and compared == steps:
+        assert stopped.all()
