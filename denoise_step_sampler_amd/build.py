@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdg.so")
-SOURCES = ["dg_api.hip", "vocab_gemm.hip", "vocab_pass.hip", "accept_renoise.hip", "q_sample.hip",
+SOURCES = ["dg_api.hip", "vocab_gemm.hip", "embedding_f16.hip", "accept_renoise.hip", "q_sample.hip",
            "selfcond_ffw.hip", "lite_sampler.hip",
            "fp8.hip"]
 HEADERS = ["dg_device.h", "dg_internal.h"]

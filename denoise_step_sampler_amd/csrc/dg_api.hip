@@ -24,25 +24,13 @@ dg_status hip_fail(hipError_t e, const char* what) {
   return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Path of the vocabulary pass, from the shape alone: the two-GEMM path for d % 128 == 0, the
-// split kernels (fp32 tile weights, four plain kernels) for the other multiples of 64.
-enum Path { kGemm, kSplit };
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Path pick_path(int d) { return dg::gemm_supported(d) ? kGemm : kSplit; }
-
-// Largest batch for which the FP8 pass streams the transposed codes through the expectation
-// pass (measured: one canvas 0.84 ms against 0.90 on bf16 rows and 1.27 on the dequantised
-// copy; 32 canvases 19.6 ms against 19.3 on the copy).
-constexpr int kFp8StreamMaxCanvases = 4;
-
-// Bytes of the two-GEMM workspace before the FP8 pass's dequantised rows.
-size_t fp8_offset(int n_canvas, int V, int d) {
-  return (dg::gemm_plan(n_canvas, V, d).bytes + 255) & ~(size_t)255;
-}
-
-size_t plan_bytes(int n_canvas, int V, int d) {
-  return pick_path(d) == kGemm ? dg::gemm_plan(n_canvas, V, d).bytes
-                               : dg::vocab_plan(n_canvas, V, d).bytes;
+// Workspace of the vocabulary pass: the two-GEMM pieces, then (when the caller gives no fp16
+// transposed embedding and the expectation is asked for) room to build one.
+size_t gemm_bytes(int n_canvas, int V, int d) { return al256(dg::gemm_plan(n_canvas, V, d).bytes); }
+size_t pass_bytes(int n_canvas, int V, int d, bool build_e16t) {
+  return gemm_bytes(n_canvas, V, d) + (build_e16t ? al256(dg::e16t_bytes(V, d)) : 0);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -62,9 +50,9 @@ dg_status check_canvas(int n_canvas, int C) {
 dg_status check_vocab_shape(int n_canvas, int C, int V, int d) {
   dg_status s = check_canvas(n_canvas, C);
   if (s != DG_OK) return s;
-  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
+  if (V < 1 || V > DG_MAX_V) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, %d]", V, DG_MAX_V);
   if (d < 1 || d > DG_MAX_D) return fail(DG_ERR_INVALID_ARG, "d=%d outside [1, %d]", d, DG_MAX_D);
-  if (d % 64 != 0) return fail(DG_ERR_UNSUPPORTED, "d=%d: d must be a multiple of 64", d);
+  if (d % 128 != 0) return fail(DG_ERR_UNSUPPORTED, "d=%d: d must be a multiple of 128", d);
   return DG_OK;
 }
 
@@ -96,47 +84,75 @@ const char* dg_status_string(dg_status s) {
 const char* dg_last_error(void) { return g_err; }
 
 size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d) {
+  return dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, 0);
+}
+
+size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16t) {
   char keep[sizeof(g_err)];
   memcpy(keep, g_err, sizeof(g_err));
   const dg_status s = check_vocab_shape(n_canvas, C, V, d);
   memcpy(g_err, keep, sizeof(g_err));
   if (s != DG_OK) return 0;
-  return plan_bytes(n_canvas, V, d);
+  return pass_bytes(n_canvas, V, d, with_e16t == 0);
+}
+
+size_t dg_embedding_f16t_bytes(int V, int d) {
+  if (V < 1 || V > DG_MAX_V || d < 128 || d > DG_MAX_D || d % 128 != 0) return 0;
+  return dg::e16t_bytes(V, d);
+}
+
+dg_status dg_embedding_f16t(const uint16_t* E, int V, int d, uint16_t* E16T, void* stream) {
+  g_err[0] = 0;
+  if (V < 1 || V > DG_MAX_V) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, %d]", V, DG_MAX_V);
+  if (d < 128 || d > DG_MAX_D || d % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 128 in [128, %d]", d, DG_MAX_D);
+  if (!E || !E16T) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(E) || !aligned16(E16T))
+    return fail(DG_ERR_INVALID_ARG, "E and E16T must be 16-byte aligned");
+  const hipError_t e = dg::e16t_launch(E, V, d, E16T, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
+  return DG_OK;
 }
 
 }  // extern "C"
 
 namespace {
 
+// E: the bf16 embedding (read by the logits pass unless E8 is given, and by the combine's
+// exact corrections); E8 / E_exp: the FP8 form the logits pass streams instead; E16T: the fp16
+// transposed embedding for the expectation, or null: built in the workspace (from E8 when
+// given, else from E).
 dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
                      const float* temperature, const uint8_t* commit, uint64_t seed,
                      const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
-                     size_t workspace_bytes, void* stream, float softcap,
-                     bool force_gemm = false, const uint8_t* E8 = nullptr,
-                     const int32_t* E_exp = nullptr, const uint8_t* E8T = nullptr,
-                     const float* draw_temperature = nullptr) {
+                     size_t workspace_bytes, void* stream, float softcap, const uint8_t* E8,
+                     const int32_t* E_exp, const uint16_t* E16T,
+                     const float* draw_temperature) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
-  if (!E || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
+  if ((!E && !E8) || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
     return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (softcap != 0.0f || draw_temperature != nullptr) force_gemm = true;
-  if (force_gemm && !dg::gemm_supported(d))
-    return fail(DG_ERR_UNSUPPORTED,
-                "the soft cap, the draw temperature and the FP8 embedding need d %% 128 == 0 "
-                "(d=%d)",
-                d);
-  if (!aligned16(E) || !aligned16(h))
-    return fail(DG_ERR_INVALID_ARG, "E and h must be 16-byte aligned");
+  if ((E && !aligned16(E)) || !aligned16(h) || (E16T && !aligned16(E16T)))
+    return fail(DG_ERR_INVALID_ARG, "E, E16T and h must be 16-byte aligned");
   if (selfcond && !aligned16(selfcond))
     return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
-  const size_t need =
-      force_gemm ? dg::gemm_plan(n_canvas, V, d).bytes : plan_bytes(n_canvas, V, d);
+  const bool build = selfcond != nullptr && E16T == nullptr;
+  const size_t need = pass_bytes(n_canvas, V, d, build);
   if (!workspace || workspace_bytes < need)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (build) {
+    uint16_t* e16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                                gemm_bytes(n_canvas, V, d));
+    const hipError_t e = E8 ? dg::e16t_fp8_launch(E8, E_exp, V, d, e16, st)
+                            : dg::e16t_launch(E, V, d, e16, st);
+    if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
+    E16T = e16;
+  }
   dg::VocabArgs a{};
   a.E = E;
   a.h = h;
@@ -156,13 +172,8 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.softcap = softcap;
   a.E8 = E8;
   a.E_exp = E_exp;
-  a.E8T = E8T;
-  a.E8T_pitch = dg::fp8_transposed_pitch(V);
-  const hipError_t e =
-      (force_gemm || pick_path(d) == kGemm)
-          ? dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, (hipStream_t)stream)
-          : dg::vocab_pass_launch(a, dg::vocab_plan(n_canvas, V, d), workspace,
-                                  (hipStream_t)stream);
+  a.E16T = E16T;
+  const hipError_t e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, st);
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
 }
@@ -178,7 +189,8 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
                         size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
-                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, 0.0f);
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, 0.0f,
+                    nullptr, nullptr, nullptr, nullptr);
 }
 
 dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
@@ -191,51 +203,48 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
   if (!(softcap > 0.0f) || !isfinite(softcap))
     return fail(DG_ERR_INVALID_ARG, "softcap must be finite and > 0");
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
-                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap);
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
+                    nullptr, nullptr, nullptr, nullptr);
 }
 
-dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
-                           int d, const float* temperature, const float* draw_temperature,
-                           float softcap, const uint8_t* commit, uint64_t seed,
-                           const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
-                           int32_t* gumbel_tok, float* selfcond, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16T, const uint16_t* h,
+                           int n_canvas, int C, int V, int d, const float* temperature,
+                           const float* draw_temperature, float softcap, const uint8_t* commit,
+                           uint64_t seed, const int32_t* step, float* lse, float* entropy,
+                           int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
     return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
+  if (!E) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
-                    false, nullptr, nullptr, nullptr, draw_temperature);
+                    nullptr, nullptr, E16T, draw_temperature);
 }
 
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {
-  char keep[sizeof(g_err)];
-  memcpy(keep, g_err, sizeof(g_err));
-  const dg_status s = check_vocab_shape(n_canvas, C, V, d);
-  memcpy(g_err, keep, sizeof(g_err));
-  if (s != DG_OK || !dg::gemm_supported(d)) return 0;
-  return fp8_offset(n_canvas, V, d) + (((size_t)V * d * 2 + 255) & ~(size_t)255);
+  return dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, 0);
 }
 
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
-                                    uint8_t* codesT, int32_t* row_exp, void* stream) {
+                                    uint16_t* E16T, int32_t* row_exp, void* stream) {
   g_err[0] = 0;
-  if (V < 1 || V > (1 << 30)) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, 2^30]", V);
-  if (d < 64 || d > DG_MAX_D || d % 64 != 0)
-    return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 64 in [64, %d]", d, DG_MAX_D);
+  if (V < 1 || V > DG_MAX_V) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, %d]", V, DG_MAX_V);
+  if (d < 128 || d > DG_MAX_D || d % 128 != 0)
+    return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 128 in [128, %d]", d, DG_MAX_D);
   if (!E || !codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(E) || !aligned16(codes) || (codesT && !aligned16(codesT)))
-    return fail(DG_ERR_INVALID_ARG, "E, codes and codesT must be 16-byte aligned");
+  if (!aligned16(E) || !aligned16(codes) || (E16T && !aligned16(E16T)))
+    return fail(DG_ERR_INVALID_ARG, "E, codes and E16T must be 16-byte aligned");
   hipError_t e = dg::fp8_quantize_launch(E, V, d, codes, row_exp, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
-  if (codesT) {
-    e = dg::fp8_transpose_launch(codes, V, d, codesT, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "fp8 transpose launch");
+  if (E16T) {
+    e = dg::e16t_fp8_launch(codes, row_exp, V, d, E16T, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
   }
   return DG_OK;
 }
 
-dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint8_t* codesT, const int32_t* row_exp,
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16T, const int32_t* row_exp,
                             const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,
@@ -243,35 +252,14 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint8_t* codesT, const i
                             int32_t* gumbel_tok, float* selfcond, void* workspace,
                             size_t workspace_bytes, void* stream, float softcap) {
   g_err[0] = 0;
-  dg_status s = check_vocab_shape(n_canvas, C, V, d);
-  if (s != DG_OK) return s;
-  if (!dg::gemm_supported(d))
-    return fail(DG_ERR_UNSUPPORTED, "the FP8 embedding needs d %% 128 == 0 (d=%d)", d);
   if (!codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(codes) || !aligned16(row_exp) || (codesT && !aligned16(codesT)))
-    return fail(DG_ERR_INVALID_ARG, "codes, codesT and row_exp must be 16-byte aligned");
+  if (!aligned16(codes) || !aligned16(row_exp))
+    return fail(DG_ERR_INVALID_ARG, "codes and row_exp must be 16-byte aligned");
   if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
     return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
-  const size_t need = dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d);
-  if (!workspace || workspace_bytes < need)
-    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
-                need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-    return fail(DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  // the logits pass streams the codes.  The expectation pass streams the transposed codes for
-  // batches of up to four canvases (E comes from HBM for each: half the bytes, no copy);
-  // larger batches share E through L2 and run faster on the dequantised rows (exact bf16),
-  // written to the end of the workspace when the expectation is asked for
-  if (n_canvas > kFp8StreamMaxCanvases) codesT = nullptr;
-  const size_t off = fp8_offset(n_canvas, V, d);
-  uint16_t* Eq = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + off);
-  if (selfcond != nullptr && codesT == nullptr) {
-    const hipError_t e = dg::fp8_dequantize_launch(codes, row_exp, V, d, Eq, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "fp8 dequantize launch");
-  }
-  return vocab_pass(Eq, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
-                    argmax_tok, gumbel_tok, selfcond, workspace, off, stream, softcap, true, codes,
-                    row_exp, selfcond != nullptr ? codesT : nullptr);
+  return vocab_pass(nullptr, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
+                    codes, row_exp, E16T, nullptr);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

@@ -100,6 +100,20 @@ __device__ __forceinline__ float add_bf16x2(float acc, uint32_t w) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+
+// Two floats to packed fp16, round to nearest even (one v_cvt_pk_f16_f32); finite inputs
+// below 2^-24 in magnitude round to zero, below 2^-14 to subnormals.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+// acc + the two fp16 halves of w (one v_dot2c_f32_f16 against (1, 1)).
+__device__ __forceinline__ float add_f16x2(float acc, uint32_t w) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+}
+// x rounded to fp16 (nearest even) and back: the value an fp16 weight holds.
+__device__ __forceinline__ float round_f16(float x) { return (float)(_Float16)x; }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------------------
@@ -176,6 +190,15 @@ __device__ __forceinline__ void dma_asm(const void* base, uint32_t off, uint32_t
                : "m0");
 }
 #pragma clang diagnostic pop
+
+// A pointer the caller knows to be the same in every lane, read from the first lane (keeps an
+// address the compiler would otherwise hold per lane in scalar registers, as dma_asm needs).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {

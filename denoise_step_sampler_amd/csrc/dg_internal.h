@@ -27,49 +27,24 @@ struct VocabArgs {
   int32_t* gumbel_tok;
   float* selfcond;
   float softcap;  // > 0: z = softcap tanh(S / softcap) / T (two-GEMM path only); 0: z = S / T
-  // FP8 embedding for the logits pass (two-GEMM path): E4M3 codes [V, d] and row exponents
-  // [V], E = 2^E_exp[v] * value(codes); null: the logits pass reads E.  The expectation pass
-  // always reads E (bf16), which must then hold the same values.
+  // FP8 embedding for the logits pass: E4M3 codes [V, d] and row exponents [V],
+  // E = 2^E_exp[v] * value(codes); null: the logits pass reads E (then E is not read at all)
   const uint8_t* E8;
   const int32_t* E_exp;
-  // with E8: the transposed codes [d][pitch] for the expectation pass (then E is not read and
-  // the logits pass stores the weights scaled by 2^E_exp[v]), or null (the expectation pass
-  // reads E, the dequantised rows)
-  const uint8_t* E8T;
-  int E8T_pitch;
+  // the expectation pass's operand: the embedding as fp16, transposed, [d][e16t_pitch(V)]
+  // (required with selfcond)
+  const uint16_t* E16T;
 };
 
-// Workspace carve-up.
-struct VocabWs {
-  float* t_m;     // [n_tiles][R] tile max of z * log2(e)
-  float* t_l;     // [n_tiles][R] sum 2^(z2 - m)
-  float* t_a;     // [n_tiles][R] sum 2^(z2 - m) (z2 - m)
-  float* t_amv;   // [n_tiles][R] argmax logit
-  int* t_ami;     // [n_tiles][R] argmax index
-  float* t_gv;    // [n_tiles][R] Gumbel key (base-2 units)
-  int* t_gi;      // [n_tiles][R] Gumbel index
-  float* prob;    // [R][vpad] 2^(z2 - m_tile), or null when no expectation is asked for
-  float* row_m;   // [R] row max (base-2 units)
-  float* row_linv;  // [R] 1 / sum
-  float* accp;    // [n_split][R][d] expectation partials
-  int n_tiles;
-  size_t vpad;
-  int n_split;
-};
+// Row pitch (entries) of the transposed fp16 embedding: the vocabulary padded to whole
+// 256-entry tiles.
+inline int e16t_pitch(int V) { return (V + 255) / 256 * 256; }
+inline size_t e16t_bytes(int V, int d) { return (size_t)e16t_pitch(V) * (size_t)d * 2; }
+hipError_t e16t_launch(const uint16_t* E, int V, int d, uint16_t* E16T, hipStream_t stream);
+hipError_t e16t_fp8_launch(const uint8_t* codes, const int32_t* kexp, int V, int d,
+                           uint16_t* E16T, hipStream_t stream);
 
-struct VocabPlan {
-  size_t R;
-  int n_tiles;
-  size_t vpad;
-  int ds;
-  int n_split;
-  size_t off_tstat, off_prob, off_row, off_accp;
-  size_t bytes;
-};
-
-VocabPlan vocab_plan(int n_canvas, int V, int d);
-
-// Two-GEMM path (vocab_gemm.hip), the default.
+// The vocabulary pass (vocab_gemm.hip): two GEMMs over the same E, d % 128 == 0.
 struct GemmPlan {
   size_t R;
   int n_tiles;    // vocabulary tiles of 256
@@ -90,11 +65,6 @@ bool gemm_supported(int d);
 GemmPlan gemm_plan(int n_canvas, int V, int d);
 hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
                        hipStream_t stream);
-
-// Split path (vocab_pass.hip): the pass for widths the two-GEMM path does not tile
-// (d % 128 != 0).
-hipError_t vocab_pass_launch(const VocabArgs& a, const VocabPlan& p, void* workspace,
-                             hipStream_t stream);
 
 struct AcceptArgs {
   const float* entropy;
@@ -169,12 +139,6 @@ hipError_t lite_step_launch(const LiteArgs& a, hipStream_t stream);
 // FP8 embedding (fp8.hip): E4M3 codes with one power-of-two scale per row.
 hipError_t fp8_quantize_launch(const uint16_t* E, int V, int d, uint8_t* codes, int32_t* kexp,
                                hipStream_t stream);
-hipError_t fp8_dequantize_launch(const uint8_t* codes, const int32_t* kexp, int V, int d,
-                                 uint16_t* E, hipStream_t stream);
-// Transposed codes for the expectation pass: [d][fp8_transposed_pitch(V)], zero past V.
-inline int fp8_transposed_pitch(int V) { return (V + 255) / 256 * 256; }
-hipError_t fp8_transpose_launch(const uint8_t* codes, int V, int d, uint8_t* codesT,
-                                hipStream_t stream);
 
 hipError_t q_sample_launch(const int32_t* x0, int n_canvas, int V, const float* kappa,
                            uint32_t k0, uint32_t k1, int32_t* xt, hipStream_t stream);

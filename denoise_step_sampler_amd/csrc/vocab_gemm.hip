@@ -1,4 +1,4 @@
-// Vocabulary pass as two streamed GEMMs for gfx950 (the default path).
+// Vocabulary pass as two streamed GEMMs for gfx950.
 //
 // The pass computes, per row r of h and temperature T_c of its canvas c, the logits
 // S = h E^T (tied unembedding, "DiffusionGemma Technical Report" sec. 3.2 eq. (5)), the
@@ -14,27 +14,27 @@
 //                   and 128-entry half tile the integer reference ref = ceil(max z2)
 //                   (z2 = S log2(e) / T), the online-softmax partial (sum 2^(z2 - ref),
 //                   entropy moment), argmax and Philox Gumbel key; the weights 2^(z2 - ref)
-//                   in (0, 1] go to HBM as bf16 (one rounding), with the reference beside
+//                   in (0, 1] go to memory as fp16 (one rounding), with the reference beside
 //                   them.  The fp32 logits never leave the registers.
-//   k_gemm_selfcond acc[256 rows, BN columns] += P~ E over one vocabulary range (bf16 MFMA
-//                   16x16x32).  Each weight fragment is brought to the range's reference
-//                   M = max ref by subtracting (M - ref) from its bf16 exponent field with
-//                   unsigned saturation (v_pk_sub_u16 clamp): an exact power-of-two scaling
-//                   (flush to zero below 2^-126), so every weight is rounded to bf16 once.
+//   k_gemm_selfcond acc[256 rows, BN columns] += P~ E over one vocabulary range (fp16 MFMA
+//                   16x16x32 on the weights and the fp16 transposed embedding), each row's
+//                   accumulator rescaled by powers of two to the reference of the half tile
+//                   being added.
 //   k_gemm_rows     per row: merges the statistic partials (max/sum/moment merge of the
 //                   chunked logsumexp in "DiffusionGemma-Lite", (value, -index) max for the
-//                   tokens), corrects the four largest weights' bf16 rounding exactly and
-//                   forms the range weights 2^(M_s - m) / lb of the expectation partials;
+//                   tokens), corrects the four largest weights' fp16 rounding exactly and
+//                   forms the range weights 2^(U_s - m) / lb of the expectation partials;
 //   k_gemm_sc       per row and column: the weighted sum of the expectation partials.
 //
 // Both GEMMs run 512-thread workgroups (one per CU) on 256 x 256 tiles and stage their
 // operands through LDS by LDS DMA (global_load_lds_dwordx4, 1 KB per instruction, issued as
-// inline assembly with explicit vmcnt waits) in a ring of four stages of 32-element K
-// chunks, so each chunk's copies are issued three chunks before it is multiplied.  Work is
-// mapped to the eight XCDs so that the CUs of one XCD share operands through their L2: the
-// logits pass runs four canvases per XCD over the same vocabulary tiles (each E line is
-// read by all four), the expectation pass runs the column blocks of one (range, canvas)
-// pair on one XCD (the weights are read once from HBM, E of the range by every canvas of
+// inline assembly with explicit vmcnt waits): the logits pass in two stages of 64-element K
+// chunks (each chunk's copies issued one chunk ahead), the expectation pass in four stages of
+// 32-entry chunks (three ahead).  Work is mapped to the eight XCDs so that the CUs of one XCD
+// share operands through their L2: the logits pass runs up to eight canvases per XCD over the
+// same vocabulary tiles (each E line is read by all of them) while the XCDs of a canvas group
+// split the vocabulary; the expectation pass runs the column blocks of one (range, canvas)
+// pair on one XCD (the weights are read once from memory, E of the range by every canvas of
 // the XCD).
 #include <stdlib.h>
 #include <string.h>
@@ -104,7 +104,7 @@ __device__ __forceinline__ int lanes_at(int pos, int n_canvas, int gmax) {
 
 // Running statistics of one row over the tiles of a lane (base-2 units): reference m, sum
 // l = sum 2^(z2 - m), moment a = sum 2^(z2 - m) (z2 - m), and lb = the same sum over the
-// bf16-rounded weights the expectation pass multiplies (its normaliser).
+// fp16-rounded weights the expectation pass multiplies (its normaliser).
 struct RowAcc {
   float m, l, a, lb, amv, gv;
   int ami, gi;
@@ -164,7 +164,8 @@ struct GemmK {
   const int* order;   // [n_canvas] canvases, non-commit first
   const int* pos;     // [n_canvas] position of each canvas in order
   const int* n_nc_p;  // number of non-commit canvases
-  uint16_t* P;        // bf16 weights 2^(z2 - ref) in MFMA-fragment order: 1 KB blocks
+  uint16_t* P;        // fp16 weights 2^(z2 - ref) in MFMA-fragment order (null: no
+                      // expectation, nothing stored): 1 KB blocks
                       // [row / 16][v / 32], entry (row, v) at 8 (row % 16 + 16 ((v % 32) / 8))
                       // + v % 8 of its block; row = 256 pos + i
   int* ref;           // [n_half][R] integer references (base-2 units), row = 256 pos + i
@@ -217,17 +218,15 @@ __device__ __forceinline__ float soft_cap_z2(float s, const SoftCap& sc) {
 }
 
 // kCap: z2 = soft_cap_z2(S) in place of S c2; the argmax stays on S.
-// kScaleP: the stored weights are 2^pexp[v] times the bf16 weights (exact; the expectation
-// pass then multiplies them by the FP8 codes), the normaliser sums the unscaled ones.
 // kSep: the Gumbel key takes its own temperature, c2g = log2(e) / T_draw (S c2g, or
 // tanh(S / c) c c2g with the cap) in place of z2; the statistics keep c2.
-template <bool kHeavy, bool kCap, bool kScaleP = false, bool kSep = false>
+// kStore: the weights are stored at pt (the expectation is asked for).
+template <bool kHeavy, bool kCap, bool kSep = false, bool kStore = true>
 __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, const f32x16& s2,
                                         const f32x16& s3, int vt0, int V, float c2,
                                         const SoftCap& cap, uint32_t row, uint32_t step,
                                         uint32_t k0, uint32_t k1, uint16_t* pt, int* ref_out,
-                                        LdsRowAcc* lds_st, const int32_t* pexp = nullptr,
-                                        float c2g = 0.0f, float czg = 0.0f) {
+                                        LdsRowAcc* lds_st, float c2g = 0.0f, float czg = 0.0f) {
   // HIP contracts a * b - c into one fma by default, which would round dz once instead of
   // twice and break the bit-for-bit recomputation in the combine (mul_rn / sub_rn keep the
   // two roundings)
@@ -330,26 +329,9 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
           pv[j] = pe;
         }
       }
-      const uint32_t w01 = pack_bf16x2(pv[0], pv[1]), w23 = pack_bf16x2(pv[2], pv[3]);
-      lsb = add_bf16x2(add_bf16x2(lsb, w01), w23);
-      if constexpr (kScaleP) {
-        int ke[4];
-        if constexpr (kMasked) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ke[j] = pexp[min(vb + j, V - 1)];
-        } else {
-          const i32x4v k4 = *reinterpret_cast<const i32x4v*>(pexp + vb);  // vb % 4 == 0
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ke[j] = k4[j];
-        }
-        const uint32_t x01 = pack_bf16x2(__builtin_amdgcn_ldexpf(pv[0], ke[0]),
-                                         __builtin_amdgcn_ldexpf(pv[1], ke[1]));
-        const uint32_t x23 = pack_bf16x2(__builtin_amdgcn_ldexpf(pv[2], ke[2]),
-                                         __builtin_amdgcn_ldexpf(pv[3], ke[3]));
-        *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{x01, x23};
-      } else {
-        *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
-      }
+      const uint32_t w01 = pack_f16x2(pv[0], pv[1]), w23 = pack_f16x2(pv[2], pv[3]);
+      lsb = add_f16x2(add_f16x2(lsb, w01), w23);
+      if (kStore) *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
     }
   };
   // one 32-entry block at a time, in a run-time loop (one copy of the block's code: unrolled,
@@ -732,18 +714,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     }
     int* rout0 = g.ref + (size_t)(2 * tt + vh) * R + (size_t)p * kTile + rloc0;
     const size_t vblk = (size_t)(vt0 >> 5) * 512;  // first 32-entry block of the half tile
-    if (kF8 && heavy && g.a.E8T != nullptr) {
-      epi_row<true, kCap, true>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap,
-                                row0, step, k0, k1, prow0 + vblk, rout0, st0p, g.a.E_exp);
-      epi_row<true, kCap, true>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap,
-                                row1, step, k0, k1, prow1 + vblk, rout0 + 32, st1p, g.a.E_exp);
-    } else if (heavy) {
-      epi_row<true, kCap, false, kSep>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2,
-                                       cap, row0, step, k0, k1, prow0 + vblk, rout0, st0p,
-                                       nullptr, c2g, czg);
-      epi_row<true, kCap, false, kSep>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2,
-                                       cap, row1, step, k0, k1, prow1 + vblk, rout0 + 32, st1p,
-                                       nullptr, c2g, czg);
+    if (heavy && g.P != nullptr) {
+      epi_row<true, kCap, kSep>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
+                                step, k0, k1, prow0 + vblk, rout0, st0p, c2g, czg);
+      epi_row<true, kCap, kSep>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2, cap, row1,
+                                step, k0, k1, prow1 + vblk, rout0 + 32, st1p, c2g, czg);
+    } else if (heavy) {  // no expectation: the weights are not stored
+      epi_row<true, kCap, kSep, false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2,
+                                       cap, row0, step, k0, k1, prow0, rout0, st0p, c2g, czg);
+      epi_row<true, kCap, kSep, false>(acc[0][1], acc[1][1], acc[2][1], acc[3][1], vt0, V, c2,
+                                       cap, row1, step, k0, k1, prow1, rout0 + 32, st1p, c2g, czg);
     } else {
       epi_row<false, false>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], vt0, V, c2, cap, row0,
                             step, 0, 0, prow0, rout0, st0p);
@@ -782,54 +762,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 
 // ---------------------------------------------------------------------------------------
 // Expectation pass.  Units (non-commit position pc, column block j, range s); the pairs
-// (s, pc) are numbered range-major, pair q runs on XCD q % 8, and the XCD's units
-// (its pairs in order, each with its column blocks) go round-robin to its 32 slots.
+// (s, pc) are numbered range-major, pair q runs on XCD q % 8, and the XCD's units (its pairs
+// in order, each with its column blocks) go round-robin to its 32 slots.
 // Wave w: rows [64 (w >> 1), +64) x columns [16 NCB (w & 1), +16 NCB) of the unit's BN.
+//
+// Operands, both fp16 on v_mfma_f32_16x16x32_f16: the weights 2^(z2 - ref) the logits pass
+// stored, each relative to the integer reference ref of its row and 128-entry half tile, and
+// E16T [d][vp] (the embedding transposed: a B fragment, eight consecutive vocabulary entries of
+// one column, is one 16-byte read).  The weights are multiplied as stored.  The fp32
+// accumulator of a row is kept in units of 2^U, U the reference of the half tile being added:
+// at each half tile boundary it is rescaled by 2^(U_old - U_new), a power of two (exact, or a
+// harmless underflow of contributions that small).  Relative to its own half tile every stored
+// weight keeps fp16's full precision down to 2^-14 and its subnormals below, so no cross-tile
+// shift pushes a tail out of range.  A half tile whose reference lies more than kDropMax below
+// the row's current unit would add less than 128 2^-kDropMax of it and is skipped (its weights
+// zeroed for that row), which bounds the rescaled accumulator far inside fp32's range.  The
+// partial's reference is the row's final U.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// Bank swizzle of the staged E rows of the expectation pass: the 32-byte column pair p of
-// staged row `row` sits at pair p ^ e_swz(row).  A transpose read touches, per lane group,
-// rows k0 + 8 g + (0..3) (and + 4): with 16 pairs a row (NCB >= 4, 512- or 256-byte rows, so
-// every row starts on the same bank) the low two row bits and bit 3 spread those rows over
-// the eight 32-byte bank windows; with 4 pairs a row (NCB = 2, two rows per 256 bytes) row
-// bit 0 already alternates the half, so bits 1 and 3 pick the pair.
-template <int NCB>
-__device__ __forceinline__ int e_swz(int row) {
-  return NCB >= 4 ? ((row & 3) | (((row >> 3) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
-}
-
-// B operand of v_mfma_f32_16x16x32_bf16 for 16 columns of the staged E rows [k0, k0 + 32)
-// (k0 a multiple of 32; row pitch `pitch` bytes): lane (g = lane / 16, i = lane % 16) needs
-// E[k0 + 8 g + 0..7][col i].  Two transpose reads: lane j of a 16-lane group addresses row
-// k0 + 8 g + 4 half + j / 4, bytes 8 (j % 4) .. + 7 of the columns' 32-byte pair; lane i then
-// holds rows + 0..3 of column i.  `a` is the lane's byte address of row 8 g + j / 4 and of the
-// columns' swizzled pair (row * pitch + 32 (pair ^ e_swz(row)) + 8 (j % 4)).
-__device__ __forceinline__ u32x4 e_frag(const lds_char* e, int pitch, int k0, int a) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const lds_char* q = e + a + k0 * pitch;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q));
-  const i16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q + 4 * pitch));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
-// Scales 8 bf16 weights by 2^-sh (sh in [0, 255]) by lowering their exponent fields with
-// unsigned saturation: exact while the result stays normal, zero below.
-// (Written component by component: the same operation as a loop over v[q] was compiled to a
-// single 32-bit load whose result was copied to all four words.)
-__device__ __forceinline__ uint32_t sub_sat_u16x2(uint32_t x, u16x2 k) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, x), k));
-}
-__device__ __forceinline__ u32x4 shift_down(u32x4 v, uint32_t sh7) {
-  const u16x2 k = {(unsigned short)sh7, (unsigned short)sh7};
-  return u32x4{sub_sat_u16x2(v.x, k), sub_sat_u16x2(v.y, k), sub_sat_u16x2(v.z, k),
-               sub_sat_u16x2(v.w, k)};
+__device__ __forceinline__ f32x4 mfma16x16x32h(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 struct Unit {
@@ -854,41 +808,30 @@ __device__ __forceinline__ Unit unit_at(int x, int lu, int n_nc, int n_range, in
   return u;
 }
 
-
 __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
 }
 
-// One workgroup per unit: workgroup b runs unit b / 8 of XCD b % 8.  A unit spans at most
-// kMaxUnitTiles vocabulary tiles (its exponent shifts fit in LDS).
+// A unit spans at most kMaxUnitTiles vocabulary tiles (its rescale table fits in LDS).
 constexpr int kMaxUnitTiles = 64;
+constexpr int kDropMax = 90;  // base-2 units below the row's current unit: skipped
+constexpr int kSkip = -128;   // rescale-table entry of a skipped (row, half tile)
 
-// kF8: E arrives as the transposed FP8 codes (g.a.E8T, [d][pitch]) and the weights were
-// stored scaled by 2^E_exp[v]: the stage holds BN column rows of 32 codes (32 bytes each, the
-// two 16-byte halves swapped on rows with bit 3 set), a B fragment is one 8-byte read (the 8
-// codes of one column) widened to bf16 in registers.
-template <int NCB, bool kF8 = false>
+template <int NCB>
 __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int BN = 32 * NCB;            // columns of a unit
-  constexpr int kPitchE = 2 * BN;         // bytes of one staged E row (bf16)
   constexpr int kKC2 = 32;                // K chunk (vocabulary entries) per stage
   constexpr int kNst2 = 4;                // stages: copies run three chunks ahead
   constexpr int kPB = kTile * 2 * kKC2;   // weights: 16 fragment blocks of 1 KB (16 KB)
-  constexpr int kEB = kF8 ? BN * kKC2 : kKC2 * kPitchE;  // E: 32 rows x BN columns
+  constexpr int kEB = BN * kKC2 * 2;      // E16T: BN column rows of 64 bytes
   constexpr int kStage = kPB + kEB;
   constexpr int kNE = kEB / 1024;         // E copies per stage (2 NCB)
   constexpr int kNEw = kNE >= 8 ? kNE / 8 : 1;  // E copies per wave (waves >= kNE repeat one)
   static_assert(kNE % 8 == 0 || kNE < 8, "E copies must divide among the eight waves");
   constexpr int kCpw = 2 + kNEw;          // copies per wave and chunk
-  constexpr int kC16 = BN / 8;            // 16-byte chunks per staged E row
-  constexpr int kRowsPerCopy = 1024 / kPitchE;  // E rows per 1 KB copy
   __shared__ __attribute__((aligned(1024))) char stg[kNst2][kStage];
-  // exponent shifts: byte (ht, row) at 256 ht + 64 rw + 4 (row % 16) + rb for
-  // row = 64 rw + 16 rb + row % 16, so one 32-bit read gives a lane its four A rows
-  __shared__ __attribute__((aligned(16))) uint8_t shb[2 * kMaxUnitTiles * kTile];
-  // the prologue's two partial maxima per row live in stage 1 (no copy has been issued yet)
-  int (*sM)[kTile] = reinterpret_cast<int (*)[kTile]>(stg[1]);
-  const int V = g.a.V, d = g.a.d;
+  // rescale exponent of (half tile ht, row) at kTile ht + row; kSkip: skipped
+  __shared__ __attribute__((aligned(16))) int8_t dl[2 * kMaxUnitTiles * kTile];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int rw = w >> 1, cw = w & 1;
@@ -900,145 +843,123 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   if (!u.valid || u.t1 <= u.t0) return;
   const int nh = 2 * (u.t1 - u.t0);  // half tiles of the unit (<= 2 kMaxUnitTiles)
 
-  // ---- prologue: reference M of every row over the unit's half tiles, then the shifts
-  {
-    const int row = t & (kTile - 1), hh = t >> 8;
-    const int* rp = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + row;
-    int mx = INT32_MIN;
+  // ---- prologue: per row, the unit of each half tile and the rescale exponents
+  if (t < kTile) {
+    const int* rp = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + t;
+    int U = INT32_MIN;
 #pragma unroll 8
-    for (int ht = hh; ht < nh; ht += 2) mx = max(mx, rp[(size_t)ht * R]);
-    sM[hh][row] = mx;
-    __syncthreads();
-    const int M = max(sM[0][row], sM[1][row]);
-    const int pos = 64 * (row >> 6) + 4 * (row & 15) + ((row >> 4) & 3);
-#pragma unroll 8
-    for (int ht = hh; ht < nh; ht += 2) {
+    for (int ht = 0; ht < nh; ++ht) {
       const int rf = rp[(size_t)ht * R];
-      shb[ht * kTile + pos] = (uint8_t)((rf == INT32_MIN) ? 0 : min(M - rf, 255));
+      int dv = 0;
+      if (rf != INT32_MIN) {  // INT32_MIN: a half tile past V (zero weights)
+        if (U == INT32_MIN) {
+          U = rf;             // the first: the accumulator is still zero
+        } else if (U - rf > kDropMax) {
+          dv = kSkip;
+        } else {
+          dv = max(U - rf, -127);
+          U = rf;
+        }
+      }
+      dl[ht * kTile + t] = (int8_t)dv;
     }
-    if (hh == 0) sM[0][row] = M;
-    __syncthreads();
+    if (u.j == 0)
+      g.accM[(size_t)u.s * R + (size_t)u.pc * kTile + t] = U == INT32_MIN ? -INFINITY : (float)U;
   }
-  const int ar = lane & 15;
-  int M[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) M[rb] = sM[0][64 * rw + 16 * rb + ar];
-  __syncthreads();  // sM (stage 1) is overwritten by the first copies
+  __syncthreads();
 
-  // ---- copies.  Weights: copy j of wave w moves the fragment block of row16 2 w + j for
-  // the chunk (LDS 1 KB number 2 w + j); E: copy m moves the stage's 1 KB number
-  // (w + 8 m) % kNE, i.e. rows kRowsPerCopy ((w + 8 m) % kNE) + lane / kC16.
+  // ---- copies.  Weights: copy j of wave w moves the fragment block of row16 2 w + j for the
+  // chunk (LDS 1 KB number 2 w + j).  E: copy e moves the stage's column rows 16 e + lane / 4
+  // (64 bytes each: the chunk's 32 vocabulary entries of one column); lane % 4 is the 16-byte
+  // segment it fills, holding the logical segment (lane % 4) ^ ((row / 4) % 4), so that the
+  // sixteen rows one B-fragment read pass serves fall on distinct banks.
   const size_t nvb = g.vpad / 32;
   const char* pbase = reinterpret_cast<const char*>(g.P) +
                       (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024;
   const uint32_t offP = 16u * (uint32_t)lane;
-  const uint32_t epitch = 2u * (uint32_t)d;
-  const char* ebase = reinterpret_cast<const char*>(g.a.E) + (size_t)u.j * BN * 2;
-  const int v00 = u.t0 * kTile;
+  const size_t pitchT = g.vpad * 2;  // bytes of one E16T row
+  const char* ebase = reinterpret_cast<const char*>(g.a.E16T) + (size_t)(u.j * BN) * pitchT +
+                      (size_t)u.t0 * kTile * 2;
+  const int ew = kNE >= 8 ? w : w % kNE;  // this wave's first E copy
+  const uint32_t offE = (uint32_t)(lane >> 2) * (uint32_t)pitchT +
+                        16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   const int nkc = (u.t1 - u.t0) * (kTile / kKC2);  // a multiple of 8
-  const int erow0 = lane / kC16;                     // row within the copy
-  const int ew = kNE >= 8 ? w : w % kNE;             // this wave's first E copy
-  // swizzled 16-byte column chunk this lane fetches into its (linear) LDS slot; the rows a
-  // lane fills, kRowsPerCopy (ew + 8 m) + erow0, agree in their low four bits for every m, so
-  // one value serves all of the lane's copies
-  static_assert((8 * kRowsPerCopy) % 16 == 0, "copies of one lane share the swizzle");
-  static_assert(kC16 >= 8 && (NCB >= 4 ? kC16 >= 16 : true), "swizzle stays within a row");
-  const uint32_t ecol =
-      16u * (uint32_t)((lane % kC16) ^ (2 * e_swz<NCB>(kRowsPerCopy * ew + erow0)));
-  // this lane's transpose-read address of column block 0 (block cb: ea0 ^ 32 cb; the
-  // swizzle is an XOR on the pair index and the blocks of a wave are pairs 8 cw .. 8 cw + 7,
-  // or 4 cw .. + 3, or 2 cw .. + 1: XOR with 32 cb stays among them)
-  const int erl = 8 * (lane >> 4) + ((lane & 15) >> 2);
-  const int ea0 = erl * kPitchE + ((32 * NCB * cw) ^ (32 * e_swz<NCB>(erl))) + 8 * (lane & 3);
   uint32_t sa[kNst2];  // LDS addresses of the stages
 #pragma unroll
   for (int q = 0; q < kNst2; ++q) sa[q] = (uint32_t)(uintptr_t)(lds_char*)stg[q];
 
   // copies of chunk kc (clamped to the unit's last chunk: the copies issued past the end go
-  // to a stage nobody reads again): the weights, and the E rows
+  // to a stage nobody reads again)
+  // (the copy sources are wave-uniform; uniform_ptr states it, so that they stay in SGPRs)
   auto issue_p = [&](int kc, uint32_t dst) {
     kc = min(kc, nkc - 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      dma_asm(pbase + ((size_t)j * nvb + kc) * 1024, offP, dst + 1024u * (uint32_t)(2 * w + j));
+      dma_asm(uniform_ptr(pbase + ((size_t)j * nvb + kc) * 1024), offP,
+              dst + 1024u * (uint32_t)(2 * w + j));
   };
-  // kF8: copy e moves the 32 column rows 32 e + lane / 2 of the stage, 16 bytes each; the
-  // transposed codes are zero up to the padded width, so no row needs clamping
-  const uint32_t off8 = (uint32_t)(lane >> 1) * (uint32_t)(kF8 ? g.a.E8T_pitch : 0) +
-                        16u * (uint32_t)((lane & 1) ^ ((lane >> 4) & 1));
   auto issue_e = [&](int kc, uint32_t dst) {
     kc = min(kc, nkc - 1);
-    if constexpr (kF8) {
-      const int v0 = v00 + kc * kKC2;
-#pragma unroll
-      for (int m = 0; m < kNEw; ++m) {
-        const int e = ew + 8 * m;
-        const uint8_t* eb8 =
-            g.a.E8T + (size_t)(u.j * BN + 32 * e) * (size_t)g.a.E8T_pitch + (size_t)v0;
-        dma_asm(eb8, off8, dst + (uint32_t)kPB + 1024u * (uint32_t)e);
-      }
-      return;
-    }
-    // E rows past V - 1 (tail of the last tile, zero weights) read row V - 1
-    const int vb = min(v00 + kc * kKC2, V - 1);
-    const int lim = V - 1 - vb;
-    const char* eb = ebase + (size_t)vb * epitch;
-    // the lane's first row, opaque here so that each copy's clamped row is formed next to
-    // its copy (three VALU operations) instead of being kept per copy for the whole loop
-    int row0 = kRowsPerCopy * ew + erow0;
-    asm volatile("" : "+v"(row0));
 #pragma unroll
     for (int m = 0; m < kNEw; ++m) {
-      const int row = row0 + 8 * kRowsPerCopy * m;
-      dma_asm(eb, (uint32_t)min(row, lim) * epitch + ecol,
-              dst + (uint32_t)kPB + 1024u * (uint32_t)(ew + 8 * m));
+      const int e = ew + 8 * m;
+      dma_asm(uniform_ptr(ebase + (size_t)(16 * e) * pitchT + (size_t)kc * (kKC2 * 2)), offE,
+              dst + (uint32_t)kPB + 1024u * (uint32_t)e);
     }
   };
 
+  // B-fragment read of column block cb: lane (i = lane % 16, g = lane / 16) reads column row
+  // 16 NCB cw + 16 cb + i, logical segment g
+  const int ar = lane & 15;
+  const uint32_t eoff = (uint32_t)kPB + (uint32_t)(16 * NCB * cw + ar) * 64u +
+                        16u * (uint32_t)((lane >> 4) ^ ((ar >> 2) & 3));
   f32x4 acc[4][NCB];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
+  uint32_t amask[4];  // per A row of the lane (64 rw + 16 rb + ar): 0 if its half tile is skipped
+
+  // half tile ht begins: rescale the lane's accumulator rows (64 rw + 16 rb + 4 (lane / 16) + i)
+  // to the half tile's unit, and mask the skipped A rows
+  auto half_tile = [&](int ht) {
+    const lds_char* dh = (const lds_char*)dl + ht * kTile + 64 * rw;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const uint32_t dw = lds_u32(dh + 16 * rb + 4 * (lane >> 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int e = (int)(int8_t)(uint8_t)(dw >> (8 * i));
+        e = e == kSkip ? 0 : e;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[rb][cb][i] = __builtin_amdgcn_ldexpf(acc[rb][cb][i], e);
+      }
+      const int8_t da = *reinterpret_cast<const __attribute__((address_space(3))) int8_t*>(
+          dh + 16 * rb + ar);
+      amask[rb] = da == kSkip ? 0u : 0xFFFFFFFFu;
+    }
+  };
 
   // one chunk from stage sc once its copies have landed (the two chunks issued after it may
-  // still be in flight), with the shifts of its half tile; copies chunk kn into stage sn,
-  // which every wave finished reading before the barrier
-  auto chunk = [&](const char* sc, uint32_t sn, int kn, uint32_t shw) {
+  // still be in flight); copies chunk kn into stage sn, which every wave finished reading
+  // before the barrier
+  auto chunk = [&](const char* sc, uint32_t sn, int kn) {
     vm_wait<2 * kCpw>();
     __syncthreads();
     // the E copies at once (E may miss in L2), the weight copies halfway through the chunk
     issue_e(kn, sn);
-    uint32_t sh7[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) sh7[rb] = ((shw >> (8 * rb)) & 0xFFu) << 7;
     const lds_char* sp = (const lds_char*)sc;
-    const lds_char* se = (const lds_char*)(sc + kPB);
-    // the swizzle term, opaque to the compiler per chunk: the swizzled read addresses are
-    // formed next to their reads instead of being hoisted out of the loop (which holds one
-    // register per column block for the whole loop and spills)
-    int ea = ea0;
-    asm volatile("" : "+v"(ea));
     u32x4 fa[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
-      fa[rb] = shift_down(lds_read16(sp + (4 * rw + rb) * 1024 + 16 * lane), sh7[rb]);
+      fa[rb] = lds_read16(sp + (4 * rw + rb) * 1024 + 16 * lane) & amask[rb];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       if (cb == NCB / 2) issue_p(kn, sn);
-      u32x4 fb;
-      if constexpr (kF8) {
-        // column row 16 NCB cw + 16 cb + i, codes 8 g .. 8 g + 7 (g = lane / 16)
-        const int r8 = 16 * NCB * cw + 16 * cb + (lane & 15);
-        const int gq = lane >> 4;
-        const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
-            se + r8 * 32 + 16 * ((gq >> 1) ^ (((lane & 15) >> 3) & 1)) + 8 * (gq & 1));
-        fb = e4m3x8_bf16(x[0], x[1]);
-      } else {
-        fb = e_frag(se, kPitchE, 0, ea ^ (32 * cb));
-      }
+      const u32x4 fb = lds_read16(sp + eoff + 1024 * cb);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32(fa[rb], fb, acc[rb][cb]);
+      for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32h(fa[rb], fb, acc[rb][cb]);
     }
   };
 
@@ -1047,17 +968,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     issue_e(q, sa[q]);
     issue_p(q, sa[q]);
   }
-  const lds_char* shp = (const lds_char*)shb + 64 * rw + 4 * ar;
-  for (int kc = 0; kc < nkc; kc += kNst2) {
-    const uint32_t shw = lds_u32(shp + (kc >> 2) * kTile);  // half tile kc / 4
-    chunk(stg[0], sa[3], kc + 3, shw);
-    chunk(stg[1], sa[0], kc + 4, shw);
-    chunk(stg[2], sa[1], kc + 5, shw);
-    chunk(stg[3], sa[2], kc + 6, shw);
+  for (int kc = 0; kc < nkc; kc += kNst2) {  // one half tile (four chunks) per iteration
+    half_tile(kc >> 2);
+    chunk(stg[0], sa[3], kc + 3);
+    chunk(stg[1], sa[0], kc + 4);
+    chunk(stg[2], sa[1], kc + 5);
+    chunk(stg[3], sa[2], kc + 6);
   }
   vm_wait<0>();
-  // expectation partial of this unit; the column-block-0 unit also records the references
-  float* out = g.accp + ((size_t)u.s * R + (size_t)u.pc * kTile) * d + (size_t)u.j * BN +
+  // expectation partial of this unit, in units of 2^U of its rows
+  float* out = g.accp + ((size_t)u.s * R + (size_t)u.pc * kTile) * g.a.d + (size_t)u.j * BN +
                16 * NCB * cw + (lane & 15);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
@@ -1065,14 +985,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     for (int i = 0; i < 4; ++i) {
       const int row = 64 * rw + 16 * rb + 4 * (lane >> 4) + i;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) out[(size_t)row * d + 16 * cb] = acc[rb][cb][i];
+      for (int cb = 0; cb < NCB; ++cb) out[(size_t)row * g.a.d + 16 * cb] = acc[rb][cb][i];
     }
-  if (u.j == 0 && cw == 0 && lane < 16) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      g.accM[(size_t)u.s * R + (size_t)u.pc * kTile + 64 * rw + 16 * rb + ar] =
-          M[rb] == INT32_MIN ? -INFINITY : (float)M[rb];
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1113,15 +1027,16 @@ __global__ __launch_bounds__(256) void k_gemm_init(const uint8_t* commit, int n,
 // ---------------------------------------------------------------------------------------
 // Combine, in two kernels.  k_gemm_rows: one wave per row merges the statistic partials of
 // the row's lanes (and their top-4 half-tile maxima), writes lse / entropy / argmax / Gumbel
-// token, and the weights of the expectation sum: fac[s] = 2^(M_s - m) / lb' for the range
-// partials and coef[k] / lb' for the four exact corrections.  k_gemm_sc: one thread per
-// (row, column) forms sum_s fac[s] acc_s + sum_k coef[k] E[v_k].
+// token, and the weights of the expectation sum: fac[s] = 2^(U_s - m) / lb' for the range
+// partials (U_s: the partial's reference) and coef[k] / lb' for the four exact corrections.
+// k_gemm_sc: one thread per (row, column) forms sum_s fac[s] acc_s + sum_k coef[k] E[v_k].
 //
-// Expectation normaliser and top-4 correction.  The expectation pass multiplies bf16 weights
-// w~ = bf16(2^(z2 - ref)); dividing by the sum of the same rounded weights (lb) cancels a
+// Expectation normaliser and top-4 correction.  The expectation pass multiplies fp16 weights
+// w~ = fp16(2^(z2 - ref)); dividing by the sum of the same rounded weights (lb) cancels a
 // common rounding, and the four largest half-tile maxima of the row, whose rounding would
-// otherwise dominate the error, are restored exactly: their residual w - w~ (w recomputed
-// here bit for bit as the logits pass computed it) is added, scaled, to numerator and lb.
+// otherwise dominate the error of a peaked row, are restored exactly: their residual w - w~
+// (w recomputed here bit for bit as the logits pass computed it) is added, scaled, to
+// numerator and lb.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
   const int n_canvas = g.a.n_canvas;
@@ -1205,7 +1120,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmK g) {
     if (tm[k] != -INFINITY) {
       const float ref = fminf(fmaxf(ceilf(tm[k]), -16777216.0f), 16777216.0f);
       const float w = hw_exp2(sub_rn(tm[k], ref));
-      const float wr = __uint_as_float(f32_to_bf16_bits(w) << 16);
+      const float wr = round_f16(w);
       cf[k] = (w - wr) * hw_exp2(ref - m);
     }
     lbc += cf[k];
@@ -1258,7 +1173,7 @@ __global__ __launch_bounds__(256) void k_gemm_sc(GemmK g) {
   }
   for (; s < nr; ++s) acc += fr[s] * src[(size_t)s * stride];
   const int* vi = reinterpret_cast<const int*>(fr) + 68;
-  if (g.a.E8 != nullptr && g.a.E8T != nullptr) {
+  if (g.a.E8 != nullptr) {
     // E from the FP8 codes: 2^E_exp[v] value(code), exact
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1381,7 +1296,8 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   g.order = order;
   g.pos = pos;
   g.n_nc_p = n_nc;
-  g.P = reinterpret_cast<uint16_t*>(b + p.off_P);
+  // the weights are stored only when the expectation is asked for
+  g.P = a.selfcond != nullptr ? reinterpret_cast<uint16_t*>(b + p.off_P) : nullptr;
   g.ref = reinterpret_cast<int*>(b + p.off_ref);
   const size_t st = al256g((size_t)p.st_stride * p.R * 4);
   g.st_m = reinterpret_cast<float*>(b + p.off_st + 0 * st);
@@ -1430,26 +1346,10 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   if (e != hipSuccess) return e;
   if (a.selfcond != nullptr) {
     const dim3 grid((unsigned)(p.flat ? p.n_units : 8 * p.n_units_xcd));
-    const bool f8 = a.E8 != nullptr && a.E8T != nullptr;
     switch (p.ncb) {
-      case 8:
-        if (f8)
-          hipLaunchKernelGGL((k_gemm_selfcond<8, true>), grid, dim3(512), 0, stream, g);
-        else
-          hipLaunchKernelGGL((k_gemm_selfcond<8, false>), grid, dim3(512), 0, stream, g);
-        break;
-      case 4:
-        if (f8)
-          hipLaunchKernelGGL((k_gemm_selfcond<4, true>), grid, dim3(512), 0, stream, g);
-        else
-          hipLaunchKernelGGL((k_gemm_selfcond<4, false>), grid, dim3(512), 0, stream, g);
-        break;
-      default:
-        if (f8)
-          hipLaunchKernelGGL((k_gemm_selfcond<2, true>), grid, dim3(512), 0, stream, g);
-        else
-          hipLaunchKernelGGL((k_gemm_selfcond<2, false>), grid, dim3(512), 0, stream, g);
-        break;
+      case 8: hipLaunchKernelGGL((k_gemm_selfcond<8>), grid, dim3(512), 0, stream, g); break;
+      case 4: hipLaunchKernelGGL((k_gemm_selfcond<4>), grid, dim3(512), 0, stream, g); break;
+      default: hipLaunchKernelGGL((k_gemm_selfcond<2>), grid, dim3(512), 0, stream, g); break;
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

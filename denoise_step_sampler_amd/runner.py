@@ -47,20 +47,32 @@ class VocabBuffers:
     # temperature of the Gumbel-max draw alone ([n_canvas] fp32), or None: the draw uses
     # `temperature` (the DiffusionGemma-Lite sampler: statistics at 1, the draw at tau(k))
     draw_temperature: Optional[torch.Tensor] = None
+    # the prepared fp16 transposed embedding (embedding_f16t), or None: each pass builds it in
+    # its workspace
+    E16T: Optional[torch.Tensor] = None
 
     @property
     def R(self) -> int:
         return self.n_canvas * self.C
 
 
+def embedding_f16t(E: torch.Tensor, V: int, d: int, stream=None) -> torch.Tensor:
+    """The fp16 transposed embedding the expectation multiplies (once per embedding)."""
+    t = torch.empty(d * B.e16t_pitch(V), dtype=torch.int16, device=E.device)
+    B.dg_embedding_f16t(E, V, d, t, stream=stream)
+    return t
+
+
 def allocate(n_canvas: int, V: int, d: int, E: torch.Tensor, h: torch.Tensor,
              temperature, commit, step, want_selfcond: bool = True,
-             sentinel: float = float("nan"), device="cuda") -> VocabBuffers:
+             sentinel: float = float("nan"), device="cuda",
+             E16T: Optional[torch.Tensor] = None) -> VocabBuffers:
+    """E16T: the prepared fp16 transposed embedding, or None (each pass builds one)."""
     R = n_canvas * B.DG_CANVAS
     f32 = dict(dtype=torch.float32, device=device)
     i32 = dict(dtype=torch.int32, device=device)
     u8 = dict(dtype=torch.uint8, device=device)
-    ws_bytes = B.dg_vocab_pass_workspace_size(n_canvas, B.DG_CANVAS, V, d)
+    ws_bytes = B.dg_vocab_pass_ex_workspace_size(n_canvas, B.DG_CANVAS, V, d, E16T is not None)
     if ws_bytes == 0:
         raise ValueError(f"unsupported shape n={n_canvas} V={V} d={d}")
     return VocabBuffers(
@@ -79,22 +91,25 @@ def allocate(n_canvas: int, V: int, d: int, E: torch.Tensor, h: torch.Tensor,
         next_tokens=torch.full((R,), -7, **i32),
         accept_mask=torch.full((R,), 7, **u8),
         converged=torch.full((n_canvas,), 7, **u8),
-        mean_entropy=torch.full((n_canvas,), sentinel, **f32))
+        mean_entropy=torch.full((n_canvas,), sentinel, **f32), E16T=E16T)
 
 
 def from_workload(wl, want_selfcond: bool = True, device="cuda", E: Optional[torch.Tensor] = None,
-                  commit_any: Optional[bool] = None) -> VocabBuffers:
+                  commit_any: Optional[bool] = None,
+                  E16T: Optional[torch.Tensor] = None) -> VocabBuffers:
     E_t = bf16_tensor(wl.E, device) if E is None else E
     commit = wl.commit if (commit_any if commit_any is not None else bool(wl.commit.any())) else None
     return allocate(wl.n_canvas, wl.V, wl.d, E_t, bf16_tensor(wl.h, device), wl.temperature,
-                    commit, wl.step, want_selfcond=want_selfcond, device=device)
+                    commit, wl.step, want_selfcond=want_selfcond, device=device, E16T=E16T)
 
 
 def vocab_pass(b: VocabBuffers, seed: int, stream=None, softcap: Optional[float] = None) -> None:
     """softcap: None for the plain logits, c > 0 for c tanh(S / c) before the temperature.
-    With b.draw_temperature the Gumbel-max draw takes that temperature (dg_vocab_pass_ex)."""
-    if b.draw_temperature is not None:
-        B.dg_vocab_pass_ex(b.E, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.draw_temperature,
+    With b.draw_temperature the Gumbel-max draw takes that temperature, with b.E16T the
+    expectation multiplies the prepared embedding (both through dg_vocab_pass_ex)."""
+    if b.draw_temperature is not None or b.E16T is not None:
+        B.dg_vocab_pass_ex(b.E, b.E16T, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+                           b.draw_temperature,
                            0.0 if softcap is None else float(softcap), b.commit, seed, b.step,
                            b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace,
                            stream=stream)
@@ -182,20 +197,20 @@ def lite_step(b: VocabBuffers, s: LiteState, threshold: float, stability_steps: 
 
 @dataclass
 class Fp8Embedding:
-    """The FP8 form of an embedding on the device: E4M3 codes, their transpose (or None) and
-    per-row exponents."""
+    """The FP8 form of an embedding on the device: E4M3 codes, per-row exponents, and the fp16
+    transposed dequantised rows the expectation multiplies (or None: built per pass)."""
     codes: torch.Tensor
-    codesT: Optional[torch.Tensor]
+    E16T: Optional[torch.Tensor]
     row_exp: torch.Tensor
 
 
 def quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, stream=None,
-                           transposed: bool = True) -> Fp8Embedding:
+                           with_e16t: bool = True) -> Fp8Embedding:
     f = Fp8Embedding(codes=torch.empty(V * d, dtype=torch.uint8, device=E.device),
-                     codesT=(torch.empty(d * B.fp8_pitch(V), dtype=torch.uint8, device=E.device)
-                             if transposed else None),
+                     E16T=(torch.empty(d * B.e16t_pitch(V), dtype=torch.int16, device=E.device)
+                           if with_e16t else None),
                      row_exp=torch.empty(V, dtype=torch.int32, device=E.device))
-    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.codesT, f.row_exp, stream=stream)
+    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.E16T, f.row_exp, stream=stream)
     return f
 
 
@@ -209,7 +224,7 @@ def fp8_workspace(n_canvas: int, V: int, d: int, device="cuda") -> torch.Tensor:
 def vocab_pass_fp8(b: VocabBuffers, f: Fp8Embedding, workspace: torch.Tensor, seed: int,
                    stream=None, softcap: Optional[float] = None) -> None:
     """The vocabulary pass on the FP8 embedding f (b.E is not read)."""
-    B.dg_vocab_pass_fp8(f.codes, f.codesT, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+    B.dg_vocab_pass_fp8(f.codes, f.E16T, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
                         b.commit, seed, b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok,
                         b.selfcond, workspace, stream=stream,
                         softcap=0.0 if softcap is None else softcap)

@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   DG_OK = 0,
   DG_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, non-finite scalar */
-  DG_ERR_UNSUPPORTED = 2, /* valid but not implemented (C != 256, d % 64 != 0, ...) */
+  DG_ERR_UNSUPPORTED = 2, /* valid but not implemented (C != 256, d % 128 != 0, ...) */
   DG_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than dg_vocab_pass_workspace_size */
   DG_ERR_HIP = 4          /* a HIP runtime call failed; see dg_last_error() */
 } dg_status;
@@ -55,10 +55,33 @@ typedef enum {
 #define DG_CANVAS 256        /* positions per canvas (the only supported C) */
 #define DG_MAX_D 8192        /* largest hidden width */
 #define DG_MAX_CANVASES 4096 /* largest number of canvases per call */
+#define DG_MAX_V (1 << 26)   /* largest vocabulary */
 
-/* Bytes of device workspace dg_vocab_pass needs for this shape ([host], pure function;
- * returns 0 for a shape dg_vocab_pass would reject). */
+/* Bytes of device workspace dg_vocab_pass, dg_vocab_pass_softcap and dg_vocab_pass_fp8 need
+ * for this shape ([host], pure function; 0 for a shape they would reject).  It includes room
+ * for the fp16 transposed embedding the expectation multiplies (see dg_embedding_f16t), which
+ * these entry points build in the workspace when the expectation is asked for. */
 size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d);
+
+/* As dg_vocab_pass_workspace_size, for dg_vocab_pass_ex: with_e16t != 0 when the caller
+ * passes its own E16T (then no room for one is needed), 0 otherwise. */
+size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16t);
+
+/* dg_embedding_f16t -- the embedding in the form the self-conditioning expectation multiplies:
+ * fp16, transposed, E16T[k * DG_E16T_PITCH(V) + v] = fp16(E[v, k]) for v < V (round to nearest
+ * even), 0 for V <= v < DG_E16T_PITCH(V).  The expectation sum_v p_v E_v ([TR] eq. (6)) runs on
+ * fp16 MFMA because probability weights in bf16 (8 significant bits) leave a relative error of
+ * about 1e-3 in the expectation of a flat distribution, at the 2e-3 bar; fp16 has 11 bits.
+ * The embedding is constant across denoising steps: a caller builds this once (like the FP8
+ * codes) and hands it to dg_vocab_pass_ex; the other entry points build it per call.
+ *  E      [V, d] bf16, |E| < 65504 (larger values give unspecified expectation rows).
+ *  V      1 .. DG_MAX_V;  d: multiple of 128, 128 .. DG_MAX_D.
+ *  E16T   [d, DG_E16T_PITCH(V)] uint16 (fp16 bits) out, dg_embedding_f16t_bytes(V, d) bytes.
+ *  E and E16T 16-byte aligned.
+ * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
+#define DG_E16T_PITCH(V) ((((V) + 255) / 256) * 256)
+size_t dg_embedding_f16t_bytes(int V, int d);
+dg_status dg_embedding_f16t(const uint16_t* E, int V, int d, uint16_t* E16T, void* stream);
 
 /* dg_vocab_pass -- the fused vocabulary pass of one denoising step.
  *
@@ -77,13 +100,15 @@ size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d);
  *  E            [V, d] bf16, read only.
  *  h            [n_canvas * C, d] bf16 final hidden states, read only.
  *  n_canvas     1 .. DG_MAX_CANVASES.   C: must be DG_CANVAS.
- *  V            1 .. 2^30.   d: 64 .. DG_MAX_D, multiple of 64.
+ *  V            1 .. DG_MAX_V.   d: 128 .. DG_MAX_D, multiple of 128.
  *  temperature  [n_canvas] fp32, > 0.
  *  commit       [n_canvas] uint8 or NULL (no canvas commits).
  *  seed         Philox key.   step: [n_canvas] int32 step ids (third Gumbel counter word).
  *  lse          [R] fp32 or NULL.    entropy: [R] fp32 (nats).
  *  argmax_tok   [R] int32.           gumbel_tok: [R] int32.
- *  selfcond     [R, d] fp32 or NULL (then the expectation is not computed).
+ *  selfcond     [R, d] fp32 or NULL (then the expectation is not computed).  The expectation
+ *               multiplies fp16 probability weights by the fp16 embedding (dg_embedding_f16t,
+ *               built here in the workspace when selfcond is given).
  *  workspace    device scratch of at least dg_vocab_pass_workspace_size(n_canvas, C, V, d)
  *               bytes; its contents on entry do not matter and are clobbered.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP. */
@@ -103,7 +128,6 @@ dg_status dg_vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int 
  * increasing, so it is also the argmax of the capped logits).  All other arguments, layouts
  * and outputs as dg_vocab_pass.
  *  softcap      > 0 and finite ([host] scalar; the pages do not print its value).
- * Runs on the default (two-GEMM) path: needs d % 128 == 0, else DG_ERR_UNSUPPORTED.
  * Errors: as dg_vocab_pass; DG_ERR_INVALID_ARG for a softcap that is not finite and > 0. */
 dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
                                 int d, const float* temperature, const uint8_t* commit,
@@ -113,7 +137,8 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
                                 float softcap);
 
 /* dg_vocab_pass_ex -- dg_vocab_pass_softcap (softcap > 0) or dg_vocab_pass (softcap = 0) whose
- * Gumbel-max draw may use its own temperature.  The statistics (lse, entropy, selfcond) describe
+ * Gumbel-max draw may use its own temperature and whose expectation may take a prepared
+ * fp16 embedding.  The statistics (lse, entropy, selfcond) describe
  * p = softmax(cap(S) / temperature[c]); the sample is
  *   gumbel_tok[r] = smallest v attaining max_v (cap(S_v) / draw_temperature[c] + g_v)
  * with the same noise g as dg_vocab_pass.  This is the DiffusionGemma-Lite sampler's split
@@ -122,17 +147,19 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
  * uses the annealed temperature tau(k), item 4): call it with temperature = 1 and
  * draw_temperature = tau(k).  draw_temperature = NULL draws at `temperature`, which is
  * dg_vocab_pass_softcap / dg_vocab_pass exactly (same bits).
+ *  E16T              dg_embedding_f16t(E) or NULL (then built in the workspace when selfcond
+ *                    is given); the same values either way.
  *  draw_temperature  [n_canvas] fp32, > 0, or NULL.
  *  softcap           0 (no cap) or > 0 and finite ([host] scalar).
- * Other arguments, layouts and outputs as dg_vocab_pass.  A draw temperature or a cap needs
- * the default (two-GEMM) path: d % 128 == 0, else DG_ERR_UNSUPPORTED.
+ *  workspace         dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, E16T != NULL) bytes.
+ * Other arguments, layouts and outputs as dg_vocab_pass.
  * Errors: as dg_vocab_pass_softcap. */
-dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V,
-                           int d, const float* temperature, const float* draw_temperature,
-                           float softcap, const uint8_t* commit, uint64_t seed,
-                           const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
-                           int32_t* gumbel_tok, float* selfcond, void* workspace,
-                           size_t workspace_bytes, void* stream);
+dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16T, const uint16_t* h,
+                           int n_canvas, int C, int V, int d, const float* temperature,
+                           const float* draw_temperature, float softcap, const uint8_t* commit,
+                           uint64_t seed, const int32_t* step, float* lse, float* entropy,
+                           int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* dg_quantize_embedding_fp8 -- the tied embedding as FP8 ([VLLM] ships an FP8 checkpoint with
  * quantised weights; the pages give no scale scheme): OCP E4M3 codes (bias 7, largest finite
@@ -140,33 +167,28 @@ dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* h, int n_canvas, i
  *   k_v = the smallest integer >= -117 with max_j |E_vj| <= 448 * 2^k_v (-117 for a zero row)
  *   codes_vj = the E4M3 value nearest to E_vj / 2^k_v, ties to the even code (zero -> 0x00).
  * A power-of-two scale makes every dequantised value 2^k * value(code) an exact bf16 number.
- *  E        [V, d] bf16, finite, |E| < 2^127.   d % 64 == 0, 64 <= d <= DG_MAX_D.
+ *  E        [V, d] bf16, finite, |E| < 2^127.   d % 128 == 0, 128 <= d <= DG_MAX_D.
  *  codes    [V, d] uint8 out;  row_exp [V] int32 out.
- *  codesT   [d, DG_FP8_PITCH(V)] uint8 out, or NULL: the transposed codes the expectation pass
- *           reads (codesT[k][v] = codes[v][k], zero for v >= V).
- *  E, codes and codesT 16-byte aligned.
+ *  E16T     [d, DG_E16T_PITCH(V)] fp16 out, or NULL: the expectation pass's operand built from
+ *           the dequantised rows (dg_embedding_f16t of E~ below).
+ *  E, codes and E16T 16-byte aligned.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
-#define DG_FP8_PITCH(V) ((((V) + 255) / 256) * 256)
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
-                                    uint8_t* codesT, int32_t* row_exp, void* stream);
+                                    uint16_t* E16T, int32_t* row_exp, void* stream);
 
 /* dg_vocab_pass_fp8_workspace_size -- bytes of workspace dg_vocab_pass_fp8 needs ([host],
- * pure): the two-GEMM workspace plus V * d bf16 for the dequantised rows.  0 if unsupported. */
+ * pure; 0 if unsupported): as dg_vocab_pass_workspace_size. */
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d);
 
 /* dg_vocab_pass_fp8 -- dg_vocab_pass (dg_vocab_pass_softcap when softcap > 0) on the FP8
- * embedding (codes, codesT, row_exp) of dg_quantize_embedding_fp8: the embedding is
+ * embedding (codes, row_exp, and E16T) of dg_quantize_embedding_fp8: the embedding is
  * E~_vj = 2^row_exp[v] * value(codes_vj), and the logits, statistics, samples and
  * self-conditioning expectation are those of E~.  The logits pass streams the codes and
- * scales each entry's sum by 2^row_exp[v] (exact).  With codesT and n_canvas <= 4 the
- * expectation pass streams the transposed codes against weights stored scaled by
- * 2^row_exp[v] (exact); otherwise (codesT == NULL, or larger batches, which share E through
- * L2) and with selfcond given it reads E~ dequantised exactly to bf16 into the workspace.
- * Results equal those of dg_vocab_pass on E~ up to the order of fp32 accumulation.
- * Runs on the two-GEMM path (d % 128 == 0, else DG_ERR_UNSUPPORTED).  softcap: 0 (none) or
- * finite > 0.  Other arguments, outputs and errors as dg_vocab_pass; codes and row_exp
- * 16-byte aligned. */
-dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint8_t* codesT, const int32_t* row_exp,
+ * scales each entry's sum by 2^row_exp[v] (exact); the expectation multiplies E16T (built from
+ * the codes in the workspace when NULL and selfcond is given).  Results equal those of
+ * dg_vocab_pass on E~ up to the order of fp32 accumulation.  softcap: 0 (none) or finite > 0.
+ * Other arguments, outputs and errors as dg_vocab_pass; codes and row_exp 16-byte aligned. */
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16T, const int32_t* row_exp,
                             const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,

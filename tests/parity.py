@@ -15,7 +15,9 @@ warrant fails the test.
 """
 from __future__ import annotations
 
+import json
 import math
+import os
 from dataclasses import dataclass
 from typing import Optional
 
@@ -28,6 +30,17 @@ EXEMPT_FRAC = 0.01
 # slack of the independent recomputation of a margin (both sides are fp64 sums of the same
 # exact products, in different orders)
 RECOMPUTE_SLACK = 1e-9
+
+
+def record(rep: dict) -> dict:
+    """Appends a comparison report, named by the running test, to the JSON-lines file that
+    DG_PARITY_LOG names (the per-case parity counts of a test run); returns the report."""
+    path = os.environ.get("DG_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
+                                **rep}) + "\n")
+    return rep
 
 
 def exempt_budget(n_rows: int, max_exempt: Optional[int]) -> int:
@@ -140,7 +153,7 @@ def compare_vocab(out: dict, ref, commit_row: np.ndarray, inputs: Optional[Vocab
         assert np.all(np.asarray(out["gumbel"])[cm] == -7)
         if out.get("sc") is not None:
             assert np.all(np.isnan(np.asarray(out["sc"])[cm]))
-    return rep
+    return record(rep)
 
 
 def accept_margins(H: np.ndarray, budget: float) -> np.ndarray:
@@ -200,4 +213,4 @@ def compare_sampler(got: dict, ref, commit: np.ndarray, C: int, H: Optional[np.n
     if ncv.any() and got.get("mean_entropy") is not None:
         me = np.asarray(got["mean_entropy"], np.float64)[ncv]
         assert np.allclose(me, ref.mean_entropy[ncv], rtol=1e-6, atol=1e-7)
-    return rep
+    return record(rep)

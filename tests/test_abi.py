@@ -28,7 +28,8 @@ def _lib():
 
 def test_header_symbols_exported():
     decl = _declared()
-    assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass",
+    assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass_ex_workspace_size",
+                         "dg_embedding_f16t_bytes", "dg_embedding_f16t", "dg_vocab_pass",
                          "dg_vocab_pass_softcap", "dg_vocab_pass_ex", "dg_accept_renoise",
                          "dg_q_sample",
                          "dg_selfcond_input_workspace_size", "dg_selfcond_input",
@@ -51,7 +52,16 @@ def test_workspace_size_pure_host():
     assert f(1, 256, 4096, 256) > 0
     assert f(32, 256, 262144, 2816) > f(1, 256, 262144, 2816) > 0
     assert f(1, 128, 4096, 256) == 0      # C != 256
-    assert f(1, 256, 4096, 96) == 0       # d % 64
+    assert f(1, 256, 4096, 96) == 0       # d % 128
+    assert f(1, 256, 4096, 192) == 0      # d % 128
+    assert f(1, 256, (1 << 26) + 1, 256) == 0
+    g = lib.dg_vocab_pass_ex_workspace_size
+    # a caller-prepared fp16 embedding needs no room in the workspace
+    assert f(2, 256, 4096, 256) - g(2, 256, 4096, 256, 1) == lib.dg_embedding_f16t_bytes(4096, 256)
+    assert g(2, 256, 4096, 256, 0) == f(2, 256, 4096, 256)
+    assert lib.dg_embedding_f16t_bytes(4096, 256) == 256 * 4096 * 2
+    assert lib.dg_embedding_f16t_bytes(4000, 256) == 256 * 4096 * 2   # padded to whole tiles
+    assert lib.dg_embedding_f16t_bytes(4096, 192) == 0
     assert f(0, 256, 4096, 256) == 0
     assert f(1, 256, 0, 256) == 0
     assert f(1, 256, 4096, 8192 + 64) == 0
@@ -78,6 +88,7 @@ def test_vocab_pass_validation_errors():
     assert _vp(lib, C=128) == DG_ERR_UNSUPPORTED
     assert b"C=128" in lib.dg_last_error()
     assert _vp(lib, d=96) == DG_ERR_UNSUPPORTED
+    assert _vp(lib, d=192) == DG_ERR_UNSUPPORTED
     assert _vp(lib, n=0) == DG_ERR_INVALID_ARG
     assert _vp(lib, V=0) == DG_ERR_INVALID_ARG
     assert _vp(lib, E=(1 << 20) + 2) == DG_ERR_INVALID_ARG          # misaligned
@@ -184,11 +195,21 @@ def test_vocab_pass_ex_refusals_on_host():
     f = lib.dg_vocab_pass_ex
     P = 1 << 20
     for c in (-1.0, float("inf"), float("nan")):
-        st = f(P, P, 1, 256, 4096, 256, P, P, c, None, 0, P, None, P, P, P, None, P, 1 << 40, None)
+        st = f(P, P, P, 1, 256, 4096, 256, P, P, c, None, 0, P, None, P, P, P, None, P, 1 << 40,
+               None)
         assert st == binding.DG_ERR_INVALID_ARG, c
         assert b"softcap" in lib.dg_last_error()
-    st = f(P, P, 1, 256, 4096, 192, P, P, 0.0, None, 0, P, None, P, P, P, None, P, 1 << 40, None)
+    st = f(P, P, P, 1, 256, 4096, 192, P, P, 0.0, None, 0, P, None, P, P, P, None, P, 1 << 40,
+           None)
     assert st == binding.DG_ERR_UNSUPPORTED
     assert b"128" in lib.dg_last_error()
-    st = f(P, P, 1, 256, 4096, 256, None, P, 0.0, None, 0, P, None, P, P, P, None, P, 1 << 40, None)
+    st = f(P, P, P, 1, 256, 4096, 256, None, P, 0.0, None, 0, P, None, P, P, P, None, P, 1 << 40,
+           None)
     assert st == binding.DG_ERR_INVALID_ARG       # temperature is required
+    st = f(P, P + 8, P, 1, 256, 4096, 256, P, None, 0.0, None, 0, P, None, P, P, P, P, P,
+           1 << 40, None)
+    assert st == binding.DG_ERR_INVALID_ARG       # E16T misaligned
+    e = lib.dg_embedding_f16t
+    assert e(P, 4096, 192, P, None) == binding.DG_ERR_UNSUPPORTED
+    assert e(None, 4096, 256, P, None) == binding.DG_ERR_INVALID_ARG
+    assert e(P, 0, 256, P, None) == binding.DG_ERR_INVALID_ARG

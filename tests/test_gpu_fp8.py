@@ -66,10 +66,10 @@ def _special_embedding(V, d, seed):
     return synth.round_to_bf16(E.astype(np.float32))
 
 
-def _quantize_gpu(E_bits, V, d, transposed=True):
+def _quantize_gpu(E_bits, V, d, with_e16t=True):
     from denoise_step_sampler_amd import runner
     E_t = runner.bf16_tensor(E_bits)
-    f = runner.quantize_embedding_fp8(E_t, V, d, transposed=transposed)
+    f = runner.quantize_embedding_fp8(E_t, V, d, with_e16t=with_e16t)
     torch.cuda.synchronize()
     return f, f.codes.cpu().numpy().reshape(V, d), f.row_exp.cpu().numpy()
 
@@ -77,35 +77,38 @@ def _quantize_gpu(E_bits, V, d, transposed=True):
 def test_quantizer_bit_exact():
     V, d = 3000, 256
     E = _special_embedding(V, d, 4)
-    _, codes, k = _quantize_gpu(E, V, d)
+    f, codes, k = _quantize_gpu(E, V, d)
     q_ref, k_ref = of8.quantize_rows(ovp.widen_bf16(E))
     assert np.array_equal(k, k_ref), np.nonzero(k != k_ref)[0][:8]
     bad = np.argwhere(codes != q_ref)
     assert bad.size == 0, [(int(r), int(c), int(codes[r, c]), int(q_ref[r, c])) for r, c in bad[:8]]
-    # the transposed codes: [d][pitch], zero past V
-    f, _, _ = _quantize_gpu(E, V, d)
+    # the expectation's operand: the dequantised rows as fp16, transposed, zero past V (the
+    # row scaled by 2^40 lies beyond fp16's range and becomes infinities on both sides)
     pitch = (V + 255) // 256 * 256
-    qT = f.codesT.cpu().numpy().reshape(d, pitch)
-    assert np.array_equal(qT[:, :V], q_ref.T) and np.all(qT[:, V:] == 0)
+    qT = f.E16T.cpu().numpy().view(np.uint16).reshape(d, pitch)
+    with np.errstate(over="ignore"):
+        want = of8.dequantize_rows(q_ref, k_ref).astype(np.float16).view(np.uint16).T
+    assert np.array_equal(qT[:, :V], want) and np.all(qT[:, V:] == 0)
 
 
-@pytest.mark.parametrize("softcap,transposed", [(None, True), (15.0, True), (None, False)])
-def test_fp8_vocab_pass_parity_and_bf16_identity(softcap, transposed):
-    """The pass on the codes (transposed codes for the expectation, or its dequantised copy)
-    against the oracle on the dequantised rows and against the bf16 pass on them."""
+@pytest.mark.parametrize("softcap,prepared", [(None, True), (15.0, True), (None, False)])
+def test_fp8_vocab_pass_parity_and_bf16_identity(softcap, prepared):
+    """The pass on the codes (with the quantiser's fp16 rows for the expectation, or rows the
+    pass builds itself) against the oracle on the dequantised rows, and the bf16 pass on those
+    rows against the same oracle."""
     from denoise_step_sampler_amd import runner
     V, d, n = 5000, 256, 3
     wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=9)
     wl.commit = np.array([0, 1, 0], np.uint8)
     wl.temperature = np.array([0.5, 0.8, 1.1], np.float32)
-    f, codes, k = _quantize_gpu(wl.E, V, d, transposed)
+    f, codes, k = _quantize_gpu(wl.E, V, d, prepared)
     q_ref, k_ref = of8.quantize_rows(ovp.widen_bf16(wl.E))
     assert np.array_equal(codes, q_ref) and np.array_equal(k, k_ref)
     Eq = of8.dequantize_rows(q_ref, k_ref)              # the oracle's dequantised rows
     Eq_bits = synth.round_to_bf16(Eq.astype(np.float32))
     assert np.array_equal(ovp.widen_bf16(Eq_bits), Eq)  # exact in bf16
     seed = 0xF8
-    _say(f"[vocab_pass_fp8] softcap={softcap} transposed={transposed} n={n} V={V} d={d}")
+    _say(f"[vocab_pass_fp8] softcap={softcap} prepared={prepared} n={n} V={V} d={d}")
     b = runner.from_workload(wl)
     ws = runner.fp8_workspace(n, V, d)
     runner.vocab_pass_fp8(b, f, ws, seed, softcap=softcap)
@@ -134,8 +137,8 @@ def test_fp8_vocab_pass_parity_and_bf16_identity(softcap, transposed):
 
 def test_fp8_full_size_batched():
     """V = 262144, d = 2816: quantiser rows against the oracle on a sample, and the FP8 pass on
-    sampled rows against the oracle on the dequantised embedding, for 32 canvases (expectation
-    on the dequantised copy) and for one canvas (expectation on the transposed codes)."""
+    sampled rows against the oracle on the dequantised embedding, for 32 canvases and for one
+    canvas."""
     from denoise_step_sampler_amd import runner
     _say("[vocab_pass_fp8] generating V=262144 d=2816 embedding")
     E = synth.make_embedding(262144, 2816, seed=0)
@@ -162,7 +165,6 @@ def test_fp8_full_size_batched():
     rows = np.sort(np.concatenate([c * C + rng.choice(C, 3, replace=False) for c in canv]))
     _against_oracle(b, wl, Eq64, rows, 5, label="32 canvases:")
     del b, ws
-    # one canvas: the expectation pass streams the transposed codes
     wl1 = synth.workload("large_v", E=E)
     c1 = runner.from_workload(wl1)
     runner.vocab_pass_fp8(c1, f, runner.fp8_workspace(1, V, d), 7)
