@@ -20,7 +20,7 @@ DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = ra
 DG_CANVAS = 256
 
 EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass_ex_workspace_size",
-            "dg_embedding_f16t_bytes", "dg_embedding_f16t", "dg_vocab_pass", "dg_vocab_pass_softcap",
+            "dg_embedding_f16_bytes", "dg_embedding_f16", "dg_vocab_pass", "dg_vocab_pass_softcap",
             "dg_vocab_pass_ex", "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
             "dg_selfcond_input", "dg_lite_step", "dg_quantize_embedding_fp8",
             "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8", "dg_status_string",
@@ -50,10 +50,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_vocab_pass_workspace_size.restype = SZ
     lib.dg_vocab_pass_ex_workspace_size.argtypes = [I, I, I, I, I]
     lib.dg_vocab_pass_ex_workspace_size.restype = SZ
-    lib.dg_embedding_f16t_bytes.argtypes = [I, I]
-    lib.dg_embedding_f16t_bytes.restype = SZ
-    lib.dg_embedding_f16t.argtypes = [P, I, I, P, P]
-    lib.dg_embedding_f16t.restype = I
+    lib.dg_embedding_f16_bytes.argtypes = [I, I]
+    lib.dg_embedding_f16_bytes.restype = SZ
+    lib.dg_embedding_f16.argtypes = [P, I, I, P, P]
+    lib.dg_embedding_f16.restype = I
     lib.dg_vocab_pass.argtypes = [P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P]
     lib.dg_vocab_pass.restype = I
     lib.dg_vocab_pass_softcap.argtypes = [P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ, P,
@@ -144,19 +144,19 @@ def dg_vocab_pass_softcap(E: torch.Tensor, h: torch.Tensor, n_canvas: int, C: in
                 entropy, argmax_tok, gumbel_tok, selfcond, workspace, stream)
 
 
-def e16t_pitch(V: int) -> int:
-    """Row pitch (entries) of the fp16 transposed embedding (DG_E16T_PITCH)."""
+def e16_rows(V: int) -> int:
+    """Rows of the fp16 embedding: V padded to whole 256-entry tiles (DG_E16_ROWS)."""
     return (V + 255) // 256 * 256
 
 
-def dg_vocab_pass_ex_workspace_size(n_canvas: int, C: int, V: int, d: int, with_e16t: bool) -> int:
-    return int(load().dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, int(bool(with_e16t))))
+def dg_vocab_pass_ex_workspace_size(n_canvas: int, C: int, V: int, d: int, with_e16: bool) -> int:
+    return int(load().dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, int(bool(with_e16))))
 
 
-def dg_embedding_f16t(E: torch.Tensor, V: int, d: int, E16T: torch.Tensor, stream=None) -> None:
-    """E16T: [d * e16t_pitch(V)] fp16 bits (torch.int16/uint16 or torch.float16)."""
-    _check(load().dg_embedding_f16t(_bf16_ptr(E, V * d, "E"), V, d,
-                                    _f16_ptr(E16T, d * e16t_pitch(V), "E16T"), _stream(stream)))
+def dg_embedding_f16(E: torch.Tensor, V: int, d: int, E16: torch.Tensor, stream=None) -> None:
+    """E16: [e16_rows(V) * d] fp16 bits (torch.int16/uint16 or torch.float16)."""
+    _check(load().dg_embedding_f16(_bf16_ptr(E, V * d, "E"), V, d,
+                                    _f16_ptr(E16, d * e16_rows(V), "E16"), _stream(stream)))
 
 
 def _f16_ptr(t: Optional[torch.Tensor], numel: int, name: str):
@@ -167,7 +167,7 @@ def _f16_ptr(t: Optional[torch.Tensor], numel: int, name: str):
     return _ptr(t, t.dtype, numel, name)
 
 
-def dg_vocab_pass_ex(E: torch.Tensor, E16T: Optional[torch.Tensor], h: torch.Tensor,
+def dg_vocab_pass_ex(E: torch.Tensor, E16: Optional[torch.Tensor], h: torch.Tensor,
                      n_canvas: int, C: int, V: int, d: int,
                      temperature: torch.Tensor, draw_temperature: Optional[torch.Tensor],
                      softcap: float, commit: Optional[torch.Tensor], seed: int,
@@ -176,11 +176,11 @@ def dg_vocab_pass_ex(E: torch.Tensor, E16T: Optional[torch.Tensor], h: torch.Ten
                      selfcond: Optional[torch.Tensor], workspace: torch.Tensor,
                      stream=None) -> None:
     """Statistics at `temperature`, the Gumbel-max draw at `draw_temperature` (None: the
-    same); softcap 0 for none; E16T the prepared fp16 transposed embedding or None."""
+    same); softcap 0 for none; E16 the prepared fp16 embedding or None."""
     R = n_canvas * C
     lib = load()
     st = lib.dg_vocab_pass_ex(
-        _bf16_ptr(E, V * d, "E"), _f16_ptr(E16T, d * e16t_pitch(V), "E16T"),
+        _bf16_ptr(E, V * d, "E"), _f16_ptr(E16, d * e16_rows(V), "E16"),
         _bf16_ptr(h, R * d, "h"), n_canvas, C, V, d,
         _ptr(temperature, torch.float32, n_canvas, "temperature"),
         _ptr(draw_temperature, torch.float32, n_canvas, "draw_temperature"),
@@ -323,12 +323,12 @@ def dg_lite_step(h: torch.Tensor, E: torch.Tensor, temperature: torch.Tensor, ls
 
 
 def dg_quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, codes: torch.Tensor,
-                              E16T: Optional[torch.Tensor], row_exp: torch.Tensor,
+                              E16: Optional[torch.Tensor], row_exp: torch.Tensor,
                               stream=None) -> None:
     lib = load()
     _check(lib.dg_quantize_embedding_fp8(_bf16_ptr(E, V * d, "E"), V, d,
                                          _ptr(codes, torch.uint8, V * d, "codes"),
-                                         _f16_ptr(E16T, d * e16t_pitch(V), "E16T"),
+                                         _f16_ptr(E16, d * e16_rows(V), "E16"),
                                          _ptr(row_exp, torch.int32, V, "row_exp"),
                                          _stream(stream)))
 
@@ -337,7 +337,7 @@ def dg_vocab_pass_fp8_workspace_size(n_canvas: int, C: int, V: int, d: int) -> i
     return int(load().dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d))
 
 
-def dg_vocab_pass_fp8(codes: torch.Tensor, E16T: Optional[torch.Tensor], row_exp: torch.Tensor,
+def dg_vocab_pass_fp8(codes: torch.Tensor, E16: Optional[torch.Tensor], row_exp: torch.Tensor,
                       h: torch.Tensor, n_canvas: int,
                       C: int, V: int, d: int, temperature: torch.Tensor,
                       commit: Optional[torch.Tensor], seed: int, step: torch.Tensor,
@@ -349,7 +349,7 @@ def dg_vocab_pass_fp8(codes: torch.Tensor, E16T: Optional[torch.Tensor], row_exp
     lib = load()
     st = lib.dg_vocab_pass_fp8(
         _ptr(codes, torch.uint8, V * d, "codes"),
-        _f16_ptr(E16T, d * e16t_pitch(V), "E16T"),
+        _f16_ptr(E16, d * e16_rows(V), "E16"),
         _ptr(row_exp, torch.int32, V, "row_exp"),
         _bf16_ptr(h, R * d, "h"), n_canvas, C, V, d,
         _ptr(temperature, torch.float32, n_canvas, "temperature"),

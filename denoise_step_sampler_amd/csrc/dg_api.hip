@@ -27,10 +27,10 @@ dg_status hip_fail(hipError_t e, const char* what) {
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of the vocabulary pass: the two-GEMM pieces, then (when the caller gives no fp16
-// transposed embedding and the expectation is asked for) room to build one.
+// embedding and the expectation is asked for) room to build one.
 size_t gemm_bytes(int n_canvas, int V, int d) { return al256(dg::gemm_plan(n_canvas, V, d).bytes); }
-size_t pass_bytes(int n_canvas, int V, int d, bool build_e16t) {
-  return gemm_bytes(n_canvas, V, d) + (build_e16t ? al256(dg::e16t_bytes(V, d)) : 0);
+size_t pass_bytes(int n_canvas, int V, int d, bool build_e16) {
+  return gemm_bytes(n_canvas, V, d) + (build_e16 ? al256(dg::e16_bytes(V, d)) : 0);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -87,29 +87,29 @@ size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d) {
   return dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, 0);
 }
 
-size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16t) {
+size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16) {
   char keep[sizeof(g_err)];
   memcpy(keep, g_err, sizeof(g_err));
   const dg_status s = check_vocab_shape(n_canvas, C, V, d);
   memcpy(g_err, keep, sizeof(g_err));
   if (s != DG_OK) return 0;
-  return pass_bytes(n_canvas, V, d, with_e16t == 0);
+  return pass_bytes(n_canvas, V, d, with_e16 == 0);
 }
 
-size_t dg_embedding_f16t_bytes(int V, int d) {
+size_t dg_embedding_f16_bytes(int V, int d) {
   if (V < 1 || V > DG_MAX_V || d < 128 || d > DG_MAX_D || d % 128 != 0) return 0;
-  return dg::e16t_bytes(V, d);
+  return dg::e16_bytes(V, d);
 }
 
-dg_status dg_embedding_f16t(const uint16_t* E, int V, int d, uint16_t* E16T, void* stream) {
+dg_status dg_embedding_f16(const uint16_t* E, int V, int d, uint16_t* E16, void* stream) {
   g_err[0] = 0;
   if (V < 1 || V > DG_MAX_V) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, %d]", V, DG_MAX_V);
   if (d < 128 || d > DG_MAX_D || d % 128 != 0)
     return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 128 in [128, %d]", d, DG_MAX_D);
-  if (!E || !E16T) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(E) || !aligned16(E16T))
-    return fail(DG_ERR_INVALID_ARG, "E and E16T must be 16-byte aligned");
-  const hipError_t e = dg::e16t_launch(E, V, d, E16T, (hipStream_t)stream);
+  if (!E || !E16) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(E) || !aligned16(E16))
+    return fail(DG_ERR_INVALID_ARG, "E and E16 must be 16-byte aligned");
+  const hipError_t e = dg::e16_launch(E, V, d, E16, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
   return DG_OK;
 }
@@ -119,25 +119,25 @@ dg_status dg_embedding_f16t(const uint16_t* E, int V, int d, uint16_t* E16T, voi
 namespace {
 
 // E: the bf16 embedding (read by the logits pass unless E8 is given, and by the combine's
-// exact corrections); E8 / E_exp: the FP8 form the logits pass streams instead; E16T: the fp16
-// transposed embedding for the expectation, or null: built in the workspace (from E8 when
+// exact corrections); E8 / E_exp: the FP8 form the logits pass streams instead; E16: the fp16
+// embedding for the expectation, or null: built in the workspace (from E8 when
 // given, else from E).
 dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, int V, int d,
                      const float* temperature, const uint8_t* commit, uint64_t seed,
                      const int32_t* step, float* lse, float* entropy, int32_t* argmax_tok,
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
                      size_t workspace_bytes, void* stream, float softcap, const uint8_t* E8,
-                     const int32_t* E_exp, const uint16_t* E16T,
+                     const int32_t* E_exp, const uint16_t* E16,
                      const float* draw_temperature) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if ((!E && !E8) || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
     return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if ((E && !aligned16(E)) || !aligned16(h) || (E16T && !aligned16(E16T)))
-    return fail(DG_ERR_INVALID_ARG, "E, E16T and h must be 16-byte aligned");
+  if ((E && !aligned16(E)) || !aligned16(h) || (E16 && !aligned16(E16)))
+    return fail(DG_ERR_INVALID_ARG, "E, E16 and h must be 16-byte aligned");
   if (selfcond && !aligned16(selfcond))
     return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
-  const bool build = selfcond != nullptr && E16T == nullptr;
+  const bool build = selfcond != nullptr && E16 == nullptr;
   const size_t need = pass_bytes(n_canvas, V, d, build);
   if (!workspace || workspace_bytes < need)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
@@ -148,10 +148,10 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   if (build) {
     uint16_t* e16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
                                                 gemm_bytes(n_canvas, V, d));
-    const hipError_t e = E8 ? dg::e16t_fp8_launch(E8, E_exp, V, d, e16, st)
-                            : dg::e16t_launch(E, V, d, e16, st);
+    const hipError_t e = E8 ? dg::e16_fp8_launch(E8, E_exp, V, d, e16, st)
+                            : dg::e16_launch(E, V, d, e16, st);
     if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
-    E16T = e16;
+    E16 = e16;
   }
   dg::VocabArgs a{};
   a.E = E;
@@ -172,7 +172,7 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.softcap = softcap;
   a.E8 = E8;
   a.E_exp = E_exp;
-  a.E16T = E16T;
+  a.E16 = E16;
   const hipError_t e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, st);
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
@@ -207,7 +207,7 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
                     nullptr, nullptr, nullptr, nullptr);
 }
 
-dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16T, const uint16_t* h,
+dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16, const uint16_t* h,
                            int n_canvas, int C, int V, int d, const float* temperature,
                            const float* draw_temperature, float softcap, const uint8_t* commit,
                            uint64_t seed, const int32_t* step, float* lse, float* entropy,
@@ -219,7 +219,7 @@ dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16T, const uint16
   if (!E) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
-                    nullptr, nullptr, E16T, draw_temperature);
+                    nullptr, nullptr, E16, draw_temperature);
 }
 
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {
@@ -227,24 +227,24 @@ size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {
 }
 
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
-                                    uint16_t* E16T, int32_t* row_exp, void* stream) {
+                                    uint16_t* E16, int32_t* row_exp, void* stream) {
   g_err[0] = 0;
   if (V < 1 || V > DG_MAX_V) return fail(DG_ERR_INVALID_ARG, "V=%d outside [1, %d]", V, DG_MAX_V);
   if (d < 128 || d > DG_MAX_D || d % 128 != 0)
     return fail(DG_ERR_UNSUPPORTED, "d=%d: need a multiple of 128 in [128, %d]", d, DG_MAX_D);
   if (!E || !codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (!aligned16(E) || !aligned16(codes) || (E16T && !aligned16(E16T)))
-    return fail(DG_ERR_INVALID_ARG, "E, codes and E16T must be 16-byte aligned");
+  if (!aligned16(E) || !aligned16(codes) || (E16 && !aligned16(E16)))
+    return fail(DG_ERR_INVALID_ARG, "E, codes and E16 must be 16-byte aligned");
   hipError_t e = dg::fp8_quantize_launch(E, V, d, codes, row_exp, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
-  if (E16T) {
-    e = dg::e16t_fp8_launch(codes, row_exp, V, d, E16T, (hipStream_t)stream);
+  if (E16) {
+    e = dg::e16_fp8_launch(codes, row_exp, V, d, E16, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
   }
   return DG_OK;
 }
 
-dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16T, const int32_t* row_exp,
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16, const int32_t* row_exp,
                             const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,
@@ -259,7 +259,7 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16T, const in
     return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
   return vocab_pass(nullptr, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
-                    codes, row_exp, E16T, nullptr);
+                    codes, row_exp, E16, nullptr);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

@@ -31,18 +31,17 @@ struct VocabArgs {
   // E = 2^E_exp[v] * value(codes); null: the logits pass reads E (then E is not read at all)
   const uint8_t* E8;
   const int32_t* E_exp;
-  // the expectation pass's operand: the embedding as fp16, transposed, [d][e16t_pitch(V)]
+  // the expectation pass's operand: the embedding as fp16, [e16_rows(V)][d], rows past V zero
   // (required with selfcond)
-  const uint16_t* E16T;
+  const uint16_t* E16;
 };
 
-// Row pitch (entries) of the transposed fp16 embedding: the vocabulary padded to whole
-// 256-entry tiles.
-inline int e16t_pitch(int V) { return (V + 255) / 256 * 256; }
-inline size_t e16t_bytes(int V, int d) { return (size_t)e16t_pitch(V) * (size_t)d * 2; }
-hipError_t e16t_launch(const uint16_t* E, int V, int d, uint16_t* E16T, hipStream_t stream);
-hipError_t e16t_fp8_launch(const uint8_t* codes, const int32_t* kexp, int V, int d,
-                           uint16_t* E16T, hipStream_t stream);
+// Rows of the fp16 embedding: the vocabulary padded to whole 256-entry tiles.
+inline int e16_rows(int V) { return (V + 255) / 256 * 256; }
+inline size_t e16_bytes(int V, int d) { return (size_t)e16_rows(V) * (size_t)d * 2; }
+hipError_t e16_launch(const uint16_t* E, int V, int d, uint16_t* E16, hipStream_t stream);
+hipError_t e16_fp8_launch(const uint8_t* codes, const int32_t* kexp, int V, int d,
+                          uint16_t* E16, hipStream_t stream);
 
 // The vocabulary pass (vocab_gemm.hip): two GEMMs over the same E, d % 128 == 0.
 struct GemmPlan {

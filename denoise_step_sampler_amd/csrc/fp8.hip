@@ -5,7 +5,7 @@
 // so the vocabulary pass on the FP8 embedding is the bf16 pass on its dequantised rows.
 //
 //   k_fp8_quantize    one wave per row: the row's |max|, k from its exponent field, codes
-// (The expectation pass's fp16 transposed operand is built from the codes by e16t_fp8_launch.)
+// (The expectation pass's fp16 operand is built from the codes by e16_fp8_launch.)
 #include "dg_device.h"
 #include "dg_internal.h"
 

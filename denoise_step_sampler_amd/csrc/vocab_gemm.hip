@@ -17,9 +17,8 @@
 //                   in (0, 1] go to memory as fp16 (one rounding), with the reference beside
 //                   them.  The fp32 logits never leave the registers.
 //   k_gemm_selfcond acc[256 rows, BN columns] += P~ E over one vocabulary range (fp16 MFMA
-//                   16x16x32 on the weights and the fp16 transposed embedding), each row's
-//                   accumulator rescaled by powers of two to the reference of the half tile
-//                   being added.
+//                   16x16x32 on the weights and the fp16 embedding), each half tile's weights
+//                   scaled by a power of two to a common unit of the row.
 //   k_gemm_rows     per row: merges the statistic partials (max/sum/moment merge of the
 //                   chunked logsumexp in "DiffusionGemma-Lite", (value, -index) max for the
 //                   tokens), corrects the four largest weights' fp16 rounding exactly and
@@ -768,16 +767,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 //
 // Operands, both fp16 on v_mfma_f32_16x16x32_f16: the weights 2^(z2 - ref) the logits pass
 // stored, each relative to the integer reference ref of its row and 128-entry half tile, and
-// E16T [d][vp] (the embedding transposed: a B fragment, eight consecutive vocabulary entries of
-// one column, is one 16-byte read).  The weights are multiplied as stored.  The fp32
-// accumulator of a row is kept in units of 2^U, U the reference of the half tile being added:
-// at each half tile boundary it is rescaled by 2^(U_old - U_new), a power of two (exact, or a
-// harmless underflow of contributions that small).  Relative to its own half tile every stored
-// weight keeps fp16's full precision down to 2^-14 and its subnormals below, so no cross-tile
-// shift pushes a tail out of range.  A half tile whose reference lies more than kDropMax below
-// the row's current unit would add less than 128 2^-kDropMax of it and is skipped (its weights
-// zeroed for that row), which bounds the rescaled accumulator far inside fp32's range.  The
-// partial's reference is the row's final U.
+// E16 [vp][d] (the embedding as fp16, rows padded with zeros to whole tiles), staged row-major
+// and read as B fragments with transpose reads.  Every row's partial is kept in units of 2^U,
+// U = M - 15 with M the row's largest half-tile reference over the unit's vocabulary range
+// (the prologue reads them all first): a half tile with reference rf enters with its weights
+// multiplied by 2^(rf - U) in fp16 (one packed multiply per A register).  For rf >= U that is
+// a scale by 2^0 .. 2^15, exact (the weights are at most 1, so at most 2^15 < 65504), and the
+// products are those of the stored weights; for rf < U the scaled weights round to fp16's
+// subnormal grid (2^-24 in units of 2^U, i.e. 2^-39 of the row's largest weight) and below
+// 2^-25 of the unit vanish, which changes the partial by less than 2^14 2^-40 of that largest
+// weight.  Each stored weight keeps fp16's precision relative to its own half tile, so a flat
+// distribution's expectation loses nothing to the cross-tile scaling; the fp32 accumulator
+// holds at most 2^14 terms of at most 2^15 |E|.
 // ---------------------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -812,10 +813,48 @@ __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
 }
 
-// A unit spans at most kMaxUnitTiles vocabulary tiles (its rescale table fits in LDS).
+// Bank swizzle of the staged E rows of the expectation pass: the 32-byte column pair p of
+// staged row `row` sits at pair p ^ e_swz(row).  A transpose read touches, per lane group,
+// rows k0 + 8 g + (0..3) (and + 4): with 16 pairs a row (NCB >= 4, 512- or 256-byte rows, so
+// every row starts on the same bank) the low two row bits and bit 3 spread those rows over
+// the eight 32-byte bank windows; with 4 pairs a row (NCB = 2, two rows per 256 bytes) row
+// bit 0 already alternates the half, so bits 1 and 3 pick the pair.
+template <int NCB>
+__device__ __forceinline__ int e_swz(int row) {
+  return NCB >= 4 ? ((row & 3) | (((row >> 3) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+}
+
+// B operand of v_mfma_f32_16x16x32_f16 for 16 columns of the staged E rows [0, 32) (row pitch
+// `pitch` bytes): lane (g = lane / 16, i = lane % 16) needs E[8 g + 0..7][col i].  Two transpose
+// reads: lane j of a 16-lane group addresses row 8 g + 4 half + j / 4, bytes 8 (j % 4) .. + 7 of
+// the columns' 32-byte pair; lane i then holds rows + 0..3 of column i.  `a` is the lane's byte
+// address of row 8 g + j / 4 and of the columns' swizzled pair
+// (row * pitch + 32 (pair ^ e_swz(row)) + 8 (j % 4)).
+__device__ __forceinline__ u32x4 e_frag(const lds_char* e, int pitch, int a) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const lds_char* q = e + a;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q + 4 * pitch));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// A unit spans at most kMaxUnitTiles vocabulary tiles (its scale table fits in LDS).
 constexpr int kMaxUnitTiles = 64;
-constexpr int kDropMax = 90;  // base-2 units below the row's current unit: skipped
-constexpr int kSkip = -128;   // rescale-table entry of a skipped (row, half tile)
+constexpr int kUp = 15;     // U = M - kUp: the largest half tile's weights enter times 2^15
+constexpr int kZero = -25;  // scale-table entry of a half tile whose weights vanish (or past V)
+
+// fp16 bits of 2^k for kZero <= k <= kUp (0 for kZero), twice
+__device__ __forceinline__ uint32_t f16_pow2x2(int k) {
+  const uint32_t h = k >= -14 ? (uint32_t)(k + 15) << 10 : (k > kZero ? 1u << (k + 24) : 0u);
+  return h | (h << 16);
+}
+
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b));
+}
 
 template <int NCB>
 __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
@@ -823,15 +862,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int kKC2 = 32;                // K chunk (vocabulary entries) per stage
   constexpr int kNst2 = 4;                // stages: copies run three chunks ahead
   constexpr int kPB = kTile * 2 * kKC2;   // weights: 16 fragment blocks of 1 KB (16 KB)
-  constexpr int kEB = BN * kKC2 * 2;      // E16T: BN column rows of 64 bytes
+  constexpr int kPitchE = 2 * BN;         // bytes of one staged E row
+  constexpr int kEB = kKC2 * kPitchE;     // E: 32 rows x BN columns
   constexpr int kStage = kPB + kEB;
   constexpr int kNE = kEB / 1024;         // E copies per stage (2 NCB)
   constexpr int kNEw = kNE >= 8 ? kNE / 8 : 1;  // E copies per wave (waves >= kNE repeat one)
   static_assert(kNE % 8 == 0 || kNE < 8, "E copies must divide among the eight waves");
   constexpr int kCpw = 2 + kNEw;          // copies per wave and chunk
+  constexpr int kC16 = BN / 8;            // 16-byte chunks per staged E row
+  constexpr int kRowsPerCopy = 1024 / kPitchE;  // E rows per 1 KB copy
   __shared__ __attribute__((aligned(1024))) char stg[kNst2][kStage];
-  // rescale exponent of (half tile ht, row) at kTile ht + row; kSkip: skipped
-  __shared__ __attribute__((aligned(16))) int8_t dl[2 * kMaxUnitTiles * kTile];
+  // scale exponent rf - U of (half tile ht, row): byte 256 ht + 64 rw + 4 (row % 16) + rb for
+  // row = 64 rw + 16 rb + row % 16, so that one 32-bit read gives a lane its four A rows
+  __shared__ __attribute__((aligned(16))) int8_t shb[2 * kMaxUnitTiles * kTile];
+  // the prologue's two partial maxima per row live in stage 1 (no copy has been issued yet)
+  int (*sM)[kTile] = reinterpret_cast<int (*)[kTile]>(stg[1]);
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int rw = w >> 1, cw = w & 1;
@@ -843,46 +888,55 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   if (!u.valid || u.t1 <= u.t0) return;
   const int nh = 2 * (u.t1 - u.t0);  // half tiles of the unit (<= 2 kMaxUnitTiles)
 
-  // ---- prologue: per row, the unit of each half tile and the rescale exponents
-  if (t < kTile) {
-    const int* rp = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + t;
-    int U = INT32_MIN;
+  // ---- prologue: per row (two threads, alternate half tiles) the largest reference M, then
+  // the scale exponents; the partial's unit U = M - kUp (-inf for a range past V)
+  {
+    const int row = t & (kTile - 1), hh = t >> 8;
+    const int* rp = g.ref + (size_t)2 * u.t0 * R + (size_t)u.pc * kTile + row;
+    int mx = INT32_MIN;  // INT32_MIN: a half tile past V (zero weights)
 #pragma unroll 8
-    for (int ht = 0; ht < nh; ++ht) {
+    for (int ht = hh; ht < nh; ht += 2) mx = max(mx, rp[(size_t)ht * R]);
+    sM[hh][row] = mx;
+    __syncthreads();
+    const int M = max(sM[0][row], sM[1][row]);
+    const int pos = 64 * (row >> 6) + 4 * (row & 15) + ((row >> 4) & 3);
+#pragma unroll 8
+    for (int ht = hh; ht < nh; ht += 2) {
       const int rf = rp[(size_t)ht * R];
-      int dv = 0;
-      if (rf != INT32_MIN) {  // INT32_MIN: a half tile past V (zero weights)
-        if (U == INT32_MIN) {
-          U = rf;             // the first: the accumulator is still zero
-        } else if (U - rf > kDropMax) {
-          dv = kSkip;
-        } else {
-          dv = max(U - rf, -127);
-          U = rf;
-        }
-      }
-      dl[ht * kTile + t] = (int8_t)dv;
+      // rf <= M; references lie within +-2^24, so the difference does not overflow
+      shb[ht * kTile + pos] = (int8_t)(rf == INT32_MIN ? kZero : max(rf - M + kUp, kZero));
     }
-    if (u.j == 0)
-      g.accM[(size_t)u.s * R + (size_t)u.pc * kTile + t] = U == INT32_MIN ? -INFINITY : (float)U;
+    if (hh == 0 && u.j == 0)
+      g.accM[(size_t)u.s * R + (size_t)u.pc * kTile + row] =
+          M == INT32_MIN ? -INFINITY : (float)(M - kUp);
+    __syncthreads();  // sM (stage 1) is overwritten by the first copies
   }
-  __syncthreads();
 
   // ---- copies.  Weights: copy j of wave w moves the fragment block of row16 2 w + j for the
-  // chunk (LDS 1 KB number 2 w + j).  E: copy e moves the stage's column rows 16 e + lane / 4
-  // (64 bytes each: the chunk's 32 vocabulary entries of one column); lane % 4 is the 16-byte
-  // segment it fills, holding the logical segment (lane % 4) ^ ((row / 4) % 4), so that the
-  // sixteen rows one B-fragment read pass serves fall on distinct banks.
+  // chunk (LDS 1 KB number 2 w + j).  E: copy m moves the stage's 1 KB number (w + 8 m) % kNE,
+  // i.e. rows kRowsPerCopy ((w + 8 m) % kNE) + lane / kC16, each lane 16 bytes of a row
+  // holding the swizzled 16-byte column chunk.
   const size_t nvb = g.vpad / 32;
   const char* pbase = reinterpret_cast<const char*>(g.P) +
                       (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024;
   const uint32_t offP = 16u * (uint32_t)lane;
-  const size_t pitchT = g.vpad * 2;  // bytes of one E16T row
-  const char* ebase = reinterpret_cast<const char*>(g.a.E16T) + (size_t)(u.j * BN) * pitchT +
-                      (size_t)u.t0 * kTile * 2;
-  const int ew = kNE >= 8 ? w : w % kNE;  // this wave's first E copy
-  const uint32_t offE = (uint32_t)(lane >> 2) * (uint32_t)pitchT +
-                        16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t epitch = 2u * (uint32_t)g.a.d;
+  const char* ebase = reinterpret_cast<const char*>(g.a.E16) +
+                      ((size_t)u.t0 * kTile) * epitch + (size_t)u.j * BN * 2;
+  const int erow0 = lane / kC16;                     // row within the copy
+  const int ew = kNE >= 8 ? w : w % kNE;             // this wave's first E copy
+  // swizzled 16-byte column chunk this lane fetches into its (linear) LDS slot; the rows a
+  // lane fills, kRowsPerCopy (ew + 8 m) + erow0, agree in their low four bits for every m, so
+  // one value serves all of the lane's copies
+  static_assert((8 * kRowsPerCopy) % 16 == 0, "copies of one lane share the swizzle");
+  static_assert(kC16 >= 8 && (NCB >= 4 ? kC16 >= 16 : true), "swizzle stays within a row");
+  const uint32_t ecol =
+      16u * (uint32_t)((lane % kC16) ^ (2 * e_swz<NCB>(kRowsPerCopy * ew + erow0)));
+  // this lane's transpose-read address of column block 0 (block cb: ea0 ^ 32 cb; the swizzle is
+  // an XOR on the pair index and the blocks of a wave are pairs 8 cw .. 8 cw + 7, or 4 cw ..
+  // + 3, or 2 cw .. + 1: XOR with 32 cb stays among them)
+  const int erl = 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int ea0 = erl * kPitchE + ((32 * NCB * cw) ^ (32 * e_swz<NCB>(erl))) + 8 * (lane & 3);
   const int nkc = (u.t1 - u.t0) * (kTile / kKC2);  // a multiple of 8
   uint32_t sa[kNst2];  // LDS addresses of the stages
 #pragma unroll
@@ -900,64 +954,50 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   };
   auto issue_e = [&](int kc, uint32_t dst) {
     kc = min(kc, nkc - 1);
+    const char* eb = uniform_ptr(ebase + (size_t)kc * kKC2 * epitch);
+    // the lane's first row, opaque here so that each copy's row offset is formed next to its
+    // copy instead of being kept per copy for the whole loop
+    int row0 = kRowsPerCopy * ew + erow0;
+    asm volatile("" : "+v"(row0));
 #pragma unroll
     for (int m = 0; m < kNEw; ++m) {
-      const int e = ew + 8 * m;
-      dma_asm(uniform_ptr(ebase + (size_t)(16 * e) * pitchT + (size_t)kc * (kKC2 * 2)), offE,
-              dst + (uint32_t)kPB + 1024u * (uint32_t)e);
+      const int row = row0 + 8 * kRowsPerCopy * m;
+      dma_asm(eb, (uint32_t)row * epitch + ecol, dst + (uint32_t)kPB + 1024u * (uint32_t)(ew + 8 * m));
     }
   };
 
-  // B-fragment read of column block cb: lane (i = lane % 16, g = lane / 16) reads column row
-  // 16 NCB cw + 16 cb + i, logical segment g
   const int ar = lane & 15;
-  const uint32_t eoff = (uint32_t)kPB + (uint32_t)(16 * NCB * cw + ar) * 64u +
-                        16u * (uint32_t)((lane >> 4) ^ ((ar >> 2) & 3));
   f32x4 acc[4][NCB];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
-  uint32_t amask[4];  // per A row of the lane (64 rw + 16 rb + ar): 0 if its half tile is skipped
-
-  // half tile ht begins: rescale the lane's accumulator rows (64 rw + 16 rb + 4 (lane / 16) + i)
-  // to the half tile's unit, and mask the skipped A rows
-  auto half_tile = [&](int ht) {
-    const lds_char* dh = (const lds_char*)dl + ht * kTile + 64 * rw;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const uint32_t dw = lds_u32(dh + 16 * rb + 4 * (lane >> 4));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int e = (int)(int8_t)(uint8_t)(dw >> (8 * i));
-        e = e == kSkip ? 0 : e;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          acc[rb][cb][i] = __builtin_amdgcn_ldexpf(acc[rb][cb][i], e);
-      }
-      const int8_t da = *reinterpret_cast<const __attribute__((address_space(3))) int8_t*>(
-          dh + 16 * rb + ar);
-      amask[rb] = da == kSkip ? 0u : 0xFFFFFFFFu;
-    }
-  };
-
   // one chunk from stage sc once its copies have landed (the two chunks issued after it may
-  // still be in flight); copies chunk kn into stage sn, which every wave finished reading
-  // before the barrier
-  auto chunk = [&](const char* sc, uint32_t sn, int kn) {
+  // still be in flight), its weights scaled by sc2 (per A row of the lane: 64 rw + 16 rb + ar);
+  // copies chunk kn into stage sn, which every wave finished reading before the barrier
+  auto chunk = [&](const char* sc, uint32_t sn, int kn, const uint32_t (&sc2)[4]) {
     vm_wait<2 * kCpw>();
     __syncthreads();
     // the E copies at once (E may miss in L2), the weight copies halfway through the chunk
     issue_e(kn, sn);
     const lds_char* sp = (const lds_char*)sc;
+    const lds_char* se = (const lds_char*)(sc + kPB);
+    // the swizzle term, opaque to the compiler per chunk: the swizzled read addresses are
+    // formed next to their reads instead of being hoisted out of the loop (which holds one
+    // register per column block for the whole loop and spills)
+    int ea = ea0;
+    asm volatile("" : "+v"(ea));
     u32x4 fa[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      fa[rb] = lds_read16(sp + (4 * rw + rb) * 1024 + 16 * lane) & amask[rb];
+    for (int rb = 0; rb < 4; ++rb) {
+      const u32x4 x = lds_read16(sp + (4 * rw + rb) * 1024 + 16 * lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fa[rb][q] = mul_f16x2(x[q], sc2[rb]);
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       if (cb == NCB / 2) issue_p(kn, sn);
-      const u32x4 fb = lds_read16(sp + eoff + 1024 * cb);
+      const u32x4 fb = e_frag(se, kPitchE, ea ^ (32 * cb));
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32h(fa[rb], fb, acc[rb][cb]);
     }
@@ -968,15 +1008,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     issue_e(q, sa[q]);
     issue_p(q, sa[q]);
   }
+  const lds_char* shp = (const lds_char*)shb + 64 * rw + 4 * ar;
   for (int kc = 0; kc < nkc; kc += kNst2) {  // one half tile (four chunks) per iteration
-    half_tile(kc >> 2);
-    chunk(stg[0], sa[3], kc + 3);
-    chunk(stg[1], sa[0], kc + 4);
-    chunk(stg[2], sa[1], kc + 5);
-    chunk(stg[3], sa[2], kc + 6);
+    const uint32_t shw = lds_u32(shp + (kc >> 2) * kTile);
+    uint32_t sc2[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) sc2[rb] = f16_pow2x2((int)(int8_t)(uint8_t)(shw >> (8 * rb)));
+    chunk(stg[0], sa[3], kc + 3, sc2);
+    chunk(stg[1], sa[0], kc + 4, sc2);
+    chunk(stg[2], sa[1], kc + 5, sc2);
+    chunk(stg[3], sa[2], kc + 6, sc2);
   }
   vm_wait<0>();
-  // expectation partial of this unit, in units of 2^U of its rows
+  // expectation partial of this unit, in units of 2^U of its rows (U = M - kUp)
   float* out = g.accp + ((size_t)u.s * R + (size_t)u.pc * kTile) * g.a.d + (size_t)u.j * BN +
                16 * NCB * cw + (lane & 15);
 #pragma unroll

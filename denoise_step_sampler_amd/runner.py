@@ -47,32 +47,32 @@ class VocabBuffers:
     # temperature of the Gumbel-max draw alone ([n_canvas] fp32), or None: the draw uses
     # `temperature` (the DiffusionGemma-Lite sampler: statistics at 1, the draw at tau(k))
     draw_temperature: Optional[torch.Tensor] = None
-    # the prepared fp16 transposed embedding (embedding_f16t), or None: each pass builds it in
+    # the prepared fp16 embedding (embedding_f16), or None: each pass builds it in
     # its workspace
-    E16T: Optional[torch.Tensor] = None
+    E16: Optional[torch.Tensor] = None
 
     @property
     def R(self) -> int:
         return self.n_canvas * self.C
 
 
-def embedding_f16t(E: torch.Tensor, V: int, d: int, stream=None) -> torch.Tensor:
-    """The fp16 transposed embedding the expectation multiplies (once per embedding)."""
-    t = torch.empty(d * B.e16t_pitch(V), dtype=torch.int16, device=E.device)
-    B.dg_embedding_f16t(E, V, d, t, stream=stream)
+def embedding_f16(E: torch.Tensor, V: int, d: int, stream=None) -> torch.Tensor:
+    """The fp16 embedding the expectation multiplies (once per embedding)."""
+    t = torch.empty(d * B.e16_rows(V), dtype=torch.int16, device=E.device)
+    B.dg_embedding_f16(E, V, d, t, stream=stream)
     return t
 
 
 def allocate(n_canvas: int, V: int, d: int, E: torch.Tensor, h: torch.Tensor,
              temperature, commit, step, want_selfcond: bool = True,
              sentinel: float = float("nan"), device="cuda",
-             E16T: Optional[torch.Tensor] = None) -> VocabBuffers:
-    """E16T: the prepared fp16 transposed embedding, or None (each pass builds one)."""
+             E16: Optional[torch.Tensor] = None) -> VocabBuffers:
+    """E16: the prepared fp16 embedding, or None (each pass builds one)."""
     R = n_canvas * B.DG_CANVAS
     f32 = dict(dtype=torch.float32, device=device)
     i32 = dict(dtype=torch.int32, device=device)
     u8 = dict(dtype=torch.uint8, device=device)
-    ws_bytes = B.dg_vocab_pass_ex_workspace_size(n_canvas, B.DG_CANVAS, V, d, E16T is not None)
+    ws_bytes = B.dg_vocab_pass_ex_workspace_size(n_canvas, B.DG_CANVAS, V, d, E16 is not None)
     if ws_bytes == 0:
         raise ValueError(f"unsupported shape n={n_canvas} V={V} d={d}")
     return VocabBuffers(
@@ -91,24 +91,24 @@ def allocate(n_canvas: int, V: int, d: int, E: torch.Tensor, h: torch.Tensor,
         next_tokens=torch.full((R,), -7, **i32),
         accept_mask=torch.full((R,), 7, **u8),
         converged=torch.full((n_canvas,), 7, **u8),
-        mean_entropy=torch.full((n_canvas,), sentinel, **f32), E16T=E16T)
+        mean_entropy=torch.full((n_canvas,), sentinel, **f32), E16=E16)
 
 
 def from_workload(wl, want_selfcond: bool = True, device="cuda", E: Optional[torch.Tensor] = None,
                   commit_any: Optional[bool] = None,
-                  E16T: Optional[torch.Tensor] = None) -> VocabBuffers:
+                  E16: Optional[torch.Tensor] = None) -> VocabBuffers:
     E_t = bf16_tensor(wl.E, device) if E is None else E
     commit = wl.commit if (commit_any if commit_any is not None else bool(wl.commit.any())) else None
     return allocate(wl.n_canvas, wl.V, wl.d, E_t, bf16_tensor(wl.h, device), wl.temperature,
-                    commit, wl.step, want_selfcond=want_selfcond, device=device, E16T=E16T)
+                    commit, wl.step, want_selfcond=want_selfcond, device=device, E16=E16)
 
 
 def vocab_pass(b: VocabBuffers, seed: int, stream=None, softcap: Optional[float] = None) -> None:
     """softcap: None for the plain logits, c > 0 for c tanh(S / c) before the temperature.
-    With b.draw_temperature the Gumbel-max draw takes that temperature, with b.E16T the
+    With b.draw_temperature the Gumbel-max draw takes that temperature, with b.E16 the
     expectation multiplies the prepared embedding (both through dg_vocab_pass_ex)."""
-    if b.draw_temperature is not None or b.E16T is not None:
-        B.dg_vocab_pass_ex(b.E, b.E16T, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+    if b.draw_temperature is not None or b.E16 is not None:
+        B.dg_vocab_pass_ex(b.E, b.E16, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
                            b.draw_temperature,
                            0.0 if softcap is None else float(softcap), b.commit, seed, b.step,
                            b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, b.workspace,
@@ -197,20 +197,20 @@ def lite_step(b: VocabBuffers, s: LiteState, threshold: float, stability_steps: 
 
 @dataclass
 class Fp8Embedding:
-    """The FP8 form of an embedding on the device: E4M3 codes, per-row exponents, and the fp16
-    transposed dequantised rows the expectation multiplies (or None: built per pass)."""
+    """The FP8 form of an embedding on the device: E4M3 codes, per-row exponents, and the
+    dequantised rows as fp16, which the expectation multiplies (or None: built per pass)."""
     codes: torch.Tensor
-    E16T: Optional[torch.Tensor]
+    E16: Optional[torch.Tensor]
     row_exp: torch.Tensor
 
 
 def quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, stream=None,
-                           with_e16t: bool = True) -> Fp8Embedding:
+                           with_e16: bool = True) -> Fp8Embedding:
     f = Fp8Embedding(codes=torch.empty(V * d, dtype=torch.uint8, device=E.device),
-                     E16T=(torch.empty(d * B.e16t_pitch(V), dtype=torch.int16, device=E.device)
-                           if with_e16t else None),
+                     E16=(torch.empty(d * B.e16_rows(V), dtype=torch.int16, device=E.device)
+                           if with_e16 else None),
                      row_exp=torch.empty(V, dtype=torch.int32, device=E.device))
-    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.E16T, f.row_exp, stream=stream)
+    B.dg_quantize_embedding_fp8(E, V, d, f.codes, f.E16, f.row_exp, stream=stream)
     return f
 
 
@@ -224,7 +224,7 @@ def fp8_workspace(n_canvas: int, V: int, d: int, device="cuda") -> torch.Tensor:
 def vocab_pass_fp8(b: VocabBuffers, f: Fp8Embedding, workspace: torch.Tensor, seed: int,
                    stream=None, softcap: Optional[float] = None) -> None:
     """The vocabulary pass on the FP8 embedding f (b.E is not read)."""
-    B.dg_vocab_pass_fp8(f.codes, f.E16T, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+    B.dg_vocab_pass_fp8(f.codes, f.E16, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
                         b.commit, seed, b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok,
                         b.selfcond, workspace, stream=stream,
                         softcap=0.0 if softcap is None else softcap)
@@ -327,3 +327,57 @@ def run_loop(wl, seed: int, max_steps: int = 32, stream=None, on_step=None,
         active = active[~conv]
     return LoopResult(steps_run=len(step_ms), steps_to_converge=steps_to_converge,
                       positions=positions, step_ms=step_ms)
+
+
+def run_loop_device(wl, seed: int, max_steps: int = 32, stream=None,
+                    E: Optional[torch.Tensor] = None, E16: Optional[torch.Tensor] = None,
+                    schedule: Optional[tuple] = None, softcap: Optional[float] = None,
+                    noise_seed: int = 0) -> LoopResult:
+    """The full-loop workload with no host round trip inside the loop: the hidden states of
+    step k, s_k E[target] kept where step k - 1 accepted plus N(0, 1) noise, are synthesised on
+    the device (torch's generator, seeded per step; the same recipe as synth.loop_hidden with
+    another random stream), and a canvas that has converged stays in the batch as a commit
+    canvas (its argmax only, as a converged canvas is committed) instead of leaving it.  Each
+    step's GPU time is taken with events around the step alone (synthesis excluded)."""
+    from . import synth
+    stream = stream if stream is not None else torch.cuda.current_stream()
+    n, C = wl.n_canvas, B.DG_CANVAS
+    R, dev = n * C, "cuda"
+    E_t = bf16_tensor(wl.E) if E is None else E
+    tgt = torch.from_numpy(wl.targets.astype(np.int64)).to(dev)
+    E_tgt = E_t.view(torch.bfloat16).reshape(wl.V, wl.d)[tgt].float()
+    b = allocate(n, wl.V, wl.d, E_t, bf16_tensor(wl.h), wl.temperature, np.zeros(n, np.uint8),
+                 np.zeros(n, np.int32), E16=E16)
+    keep = torch.ones(R, dtype=torch.float32, device=dev)
+    done = torch.zeros(n, dtype=torch.bool, device=dev)
+    stc = torch.full((n,), -1, dtype=torch.int64, device=dev)
+    active = torch.zeros(max_steps, dtype=torch.int64, device=dev)
+    gen = torch.Generator(device=dev)
+    events = []
+    with torch.cuda.stream(stream):
+        for k in range(max_steps):
+            gen.manual_seed(noise_seed * 1000003 + k)
+            noise = torch.randn((R, wl.d), generator=gen, device=dev, dtype=torch.float32)
+            s_k = synth.loop_scale(k, wl.extra.get("signal", (0.5, 0.25)))
+            h = E_tgt * (s_k * keep)[:, None] + noise
+            b.h.copy_(h.to(torch.bfloat16).view(torch.int16))
+            b.step.fill_(k)
+            if schedule is not None:
+                b.temperature.fill_(temperature_schedule(k, max_steps, *schedule))
+            b.commit.copy_(done.to(torch.uint8))
+            active[k] = (~done).sum()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            denoise_step(b, wl.budget, wl.confidence, wl.stability, seed, stream, softcap)
+            t1.record(stream)
+            events.append((t0, t1))
+            keep = b.accept_mask.float()
+            new = b.converged.bool() & ~done
+            stc = torch.where(new, torch.full_like(stc, k), stc)
+            done = done | new
+    torch.cuda.synchronize()
+    act = active.cpu().numpy()
+    return LoopResult(steps_run=max_steps, steps_to_converge=stc.cpu().numpy(),
+                      positions=int(act.sum()) * C,
+                      step_ms=[a.elapsed_time(z) for a, z in events])

@@ -59,29 +59,29 @@ typedef enum {
 
 /* Bytes of device workspace dg_vocab_pass, dg_vocab_pass_softcap and dg_vocab_pass_fp8 need
  * for this shape ([host], pure function; 0 for a shape they would reject).  It includes room
- * for the fp16 transposed embedding the expectation multiplies (see dg_embedding_f16t), which
+ * for the fp16 embedding the expectation multiplies (see dg_embedding_f16), which
  * these entry points build in the workspace when the expectation is asked for. */
 size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d);
 
-/* As dg_vocab_pass_workspace_size, for dg_vocab_pass_ex: with_e16t != 0 when the caller
- * passes its own E16T (then no room for one is needed), 0 otherwise. */
-size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16t);
+/* As dg_vocab_pass_workspace_size, for dg_vocab_pass_ex: with_e16 != 0 when the caller
+ * passes its own E16 (then no room for one is needed), 0 otherwise. */
+size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16);
 
-/* dg_embedding_f16t -- the embedding in the form the self-conditioning expectation multiplies:
- * fp16, transposed, E16T[k * DG_E16T_PITCH(V) + v] = fp16(E[v, k]) for v < V (round to nearest
- * even), 0 for V <= v < DG_E16T_PITCH(V).  The expectation sum_v p_v E_v ([TR] eq. (6)) runs on
+/* dg_embedding_f16 -- the embedding in the form the self-conditioning expectation multiplies:
+ * fp16, row-major, rows padded with zeros to whole 256-entry tiles: E16[v * d + k] =
+ * fp16(E[v, k]) for v < V (round to nearest even), 0 for V <= v < DG_E16_ROWS(V).  The expectation sum_v p_v E_v ([TR] eq. (6)) runs on
  * fp16 MFMA because probability weights in bf16 (8 significant bits) leave a relative error of
  * about 1e-3 in the expectation of a flat distribution, at the 2e-3 bar; fp16 has 11 bits.
  * The embedding is constant across denoising steps: a caller builds this once (like the FP8
  * codes) and hands it to dg_vocab_pass_ex; the other entry points build it per call.
  *  E      [V, d] bf16, |E| < 65504 (larger values give unspecified expectation rows).
  *  V      1 .. DG_MAX_V;  d: multiple of 128, 128 .. DG_MAX_D.
- *  E16T   [d, DG_E16T_PITCH(V)] uint16 (fp16 bits) out, dg_embedding_f16t_bytes(V, d) bytes.
- *  E and E16T 16-byte aligned.
+ *  E16    [DG_E16_ROWS(V), d] uint16 (fp16 bits) out, dg_embedding_f16_bytes(V, d) bytes.
+ *  E and E16 16-byte aligned.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
-#define DG_E16T_PITCH(V) ((((V) + 255) / 256) * 256)
-size_t dg_embedding_f16t_bytes(int V, int d);
-dg_status dg_embedding_f16t(const uint16_t* E, int V, int d, uint16_t* E16T, void* stream);
+#define DG_E16_ROWS(V) ((((V) + 255) / 256) * 256)
+size_t dg_embedding_f16_bytes(int V, int d);
+dg_status dg_embedding_f16(const uint16_t* E, int V, int d, uint16_t* E16, void* stream);
 
 /* dg_vocab_pass -- the fused vocabulary pass of one denoising step.
  *
@@ -107,7 +107,7 @@ dg_status dg_embedding_f16t(const uint16_t* E, int V, int d, uint16_t* E16T, voi
  *  lse          [R] fp32 or NULL.    entropy: [R] fp32 (nats).
  *  argmax_tok   [R] int32.           gumbel_tok: [R] int32.
  *  selfcond     [R, d] fp32 or NULL (then the expectation is not computed).  The expectation
- *               multiplies fp16 probability weights by the fp16 embedding (dg_embedding_f16t,
+ *               multiplies fp16 probability weights by the fp16 embedding (dg_embedding_f16,
  *               built here in the workspace when selfcond is given).
  *  workspace    device scratch of at least dg_vocab_pass_workspace_size(n_canvas, C, V, d)
  *               bytes; its contents on entry do not matter and are clobbered.
@@ -147,14 +147,14 @@ dg_status dg_vocab_pass_softcap(const uint16_t* E, const uint16_t* h, int n_canv
  * uses the annealed temperature tau(k), item 4): call it with temperature = 1 and
  * draw_temperature = tau(k).  draw_temperature = NULL draws at `temperature`, which is
  * dg_vocab_pass_softcap / dg_vocab_pass exactly (same bits).
- *  E16T              dg_embedding_f16t(E) or NULL (then built in the workspace when selfcond
+ *  E16               dg_embedding_f16(E) or NULL (then built in the workspace when selfcond
  *                    is given); the same values either way.
  *  draw_temperature  [n_canvas] fp32, > 0, or NULL.
  *  softcap           0 (no cap) or > 0 and finite ([host] scalar).
- *  workspace         dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, E16T != NULL) bytes.
+ *  workspace         dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, E16 != NULL) bytes.
  * Other arguments, layouts and outputs as dg_vocab_pass.
  * Errors: as dg_vocab_pass_softcap. */
-dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16T, const uint16_t* h,
+dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16, const uint16_t* h,
                            int n_canvas, int C, int V, int d, const float* temperature,
                            const float* draw_temperature, float softcap, const uint8_t* commit,
                            uint64_t seed, const int32_t* step, float* lse, float* entropy,
@@ -169,26 +169,26 @@ dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16T, const uint16
  * A power-of-two scale makes every dequantised value 2^k * value(code) an exact bf16 number.
  *  E        [V, d] bf16, finite, |E| < 2^127.   d % 128 == 0, 128 <= d <= DG_MAX_D.
  *  codes    [V, d] uint8 out;  row_exp [V] int32 out.
- *  E16T     [d, DG_E16T_PITCH(V)] fp16 out, or NULL: the expectation pass's operand built from
- *           the dequantised rows (dg_embedding_f16t of E~ below).
- *  E, codes and E16T 16-byte aligned.
+ *  E16      [DG_E16_ROWS(V), d] fp16 out, or NULL: the expectation pass's operand built from
+ *           the dequantised rows (dg_embedding_f16 of E~ below).
+ *  E, codes and E16 16-byte aligned.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,
-                                    uint16_t* E16T, int32_t* row_exp, void* stream);
+                                    uint16_t* E16, int32_t* row_exp, void* stream);
 
 /* dg_vocab_pass_fp8_workspace_size -- bytes of workspace dg_vocab_pass_fp8 needs ([host],
  * pure; 0 if unsupported): as dg_vocab_pass_workspace_size. */
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d);
 
 /* dg_vocab_pass_fp8 -- dg_vocab_pass (dg_vocab_pass_softcap when softcap > 0) on the FP8
- * embedding (codes, row_exp, and E16T) of dg_quantize_embedding_fp8: the embedding is
+ * embedding (codes, row_exp, and E16) of dg_quantize_embedding_fp8: the embedding is
  * E~_vj = 2^row_exp[v] * value(codes_vj), and the logits, statistics, samples and
  * self-conditioning expectation are those of E~.  The logits pass streams the codes and
- * scales each entry's sum by 2^row_exp[v] (exact); the expectation multiplies E16T (built from
+ * scales each entry's sum by 2^row_exp[v] (exact); the expectation multiplies E16 (built from
  * the codes in the workspace when NULL and selfcond is given).  Results equal those of
  * dg_vocab_pass on E~ up to the order of fp32 accumulation.  softcap: 0 (none) or finite > 0.
  * Other arguments, outputs and errors as dg_vocab_pass; codes and row_exp 16-byte aligned. */
-dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16T, const int32_t* row_exp,
+dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16, const int32_t* row_exp,
                             const uint16_t* h,
                             int n_canvas, int C, int V, int d, const float* temperature,
                             const uint8_t* commit, uint64_t seed, const int32_t* step,

@@ -29,7 +29,7 @@ def _lib():
 def test_header_symbols_exported():
     decl = _declared()
     assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass_ex_workspace_size",
-                         "dg_embedding_f16t_bytes", "dg_embedding_f16t", "dg_vocab_pass",
+                         "dg_embedding_f16_bytes", "dg_embedding_f16", "dg_vocab_pass",
                          "dg_vocab_pass_softcap", "dg_vocab_pass_ex", "dg_accept_renoise",
                          "dg_q_sample",
                          "dg_selfcond_input_workspace_size", "dg_selfcond_input",
@@ -57,11 +57,11 @@ def test_workspace_size_pure_host():
     assert f(1, 256, (1 << 26) + 1, 256) == 0
     g = lib.dg_vocab_pass_ex_workspace_size
     # a caller-prepared fp16 embedding needs no room in the workspace
-    assert f(2, 256, 4096, 256) - g(2, 256, 4096, 256, 1) == lib.dg_embedding_f16t_bytes(4096, 256)
+    assert f(2, 256, 4096, 256) - g(2, 256, 4096, 256, 1) == lib.dg_embedding_f16_bytes(4096, 256)
     assert g(2, 256, 4096, 256, 0) == f(2, 256, 4096, 256)
-    assert lib.dg_embedding_f16t_bytes(4096, 256) == 256 * 4096 * 2
-    assert lib.dg_embedding_f16t_bytes(4000, 256) == 256 * 4096 * 2   # padded to whole tiles
-    assert lib.dg_embedding_f16t_bytes(4096, 192) == 0
+    assert lib.dg_embedding_f16_bytes(4096, 256) == 256 * 4096 * 2
+    assert lib.dg_embedding_f16_bytes(4000, 256) == 256 * 4096 * 2   # padded to whole tiles
+    assert lib.dg_embedding_f16_bytes(4096, 192) == 0
     assert f(0, 256, 4096, 256) == 0
     assert f(1, 256, 0, 256) == 0
     assert f(1, 256, 4096, 8192 + 64) == 0
@@ -208,8 +208,8 @@ def test_vocab_pass_ex_refusals_on_host():
     assert st == binding.DG_ERR_INVALID_ARG       # temperature is required
     st = f(P, P + 8, P, 1, 256, 4096, 256, P, None, 0.0, None, 0, P, None, P, P, P, P, P,
            1 << 40, None)
-    assert st == binding.DG_ERR_INVALID_ARG       # E16T misaligned
-    e = lib.dg_embedding_f16t
+    assert st == binding.DG_ERR_INVALID_ARG       # E16 misaligned
+    e = lib.dg_embedding_f16
     assert e(P, 4096, 192, P, None) == binding.DG_ERR_UNSUPPORTED
     assert e(None, 4096, 256, P, None) == binding.DG_ERR_INVALID_ARG
     assert e(P, 0, 256, P, None) == binding.DG_ERR_INVALID_ARG

@@ -66,10 +66,10 @@ def _special_embedding(V, d, seed):
     return synth.round_to_bf16(E.astype(np.float32))
 
 
-def _quantize_gpu(E_bits, V, d, with_e16t=True):
+def _quantize_gpu(E_bits, V, d, with_e16=True):
     from denoise_step_sampler_amd import runner
     E_t = runner.bf16_tensor(E_bits)
-    f = runner.quantize_embedding_fp8(E_t, V, d, with_e16t=with_e16t)
+    f = runner.quantize_embedding_fp8(E_t, V, d, with_e16=with_e16)
     torch.cuda.synchronize()
     return f, f.codes.cpu().numpy().reshape(V, d), f.row_exp.cpu().numpy()
 
@@ -82,13 +82,13 @@ def test_quantizer_bit_exact():
     assert np.array_equal(k, k_ref), np.nonzero(k != k_ref)[0][:8]
     bad = np.argwhere(codes != q_ref)
     assert bad.size == 0, [(int(r), int(c), int(codes[r, c]), int(q_ref[r, c])) for r, c in bad[:8]]
-    # the expectation's operand: the dequantised rows as fp16, transposed, zero past V (the
-    # row scaled by 2^40 lies beyond fp16's range and becomes infinities on both sides)
-    pitch = (V + 255) // 256 * 256
-    qT = f.E16T.cpu().numpy().view(np.uint16).reshape(d, pitch)
+    # the expectation's operand: the dequantised rows as fp16, zero rows past V (the row scaled
+    # by 2^40 lies beyond fp16's range and becomes infinities on both sides)
+    rows = (V + 255) // 256 * 256
+    q16 = f.E16.cpu().numpy().view(np.uint16).reshape(rows, d)
     with np.errstate(over="ignore"):
-        want = of8.dequantize_rows(q_ref, k_ref).astype(np.float16).view(np.uint16).T
-    assert np.array_equal(qT[:, :V], want) and np.all(qT[:, V:] == 0)
+        want = of8.dequantize_rows(q_ref, k_ref).astype(np.float16).view(np.uint16)
+    assert np.array_equal(q16[:V], want) and np.all(q16[V:] == 0)
 
 
 @pytest.mark.parametrize("softcap,prepared", [(None, True), (15.0, True), (None, False)])

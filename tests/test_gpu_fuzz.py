@@ -81,7 +81,7 @@ def test_seeded_fuzz_against_the_oracle():
         wl.step = np.arange(p["n"], dtype=np.int32) * 3 + i
         E_t = runner.bf16_tensor(wl.E)
         b = runner.from_workload(wl, want_selfcond=p["want_sc"], commit_any=True, E=E_t,
-                                 E16T=runner.embedding_f16t(E_t, wl.V, wl.d) if p["prepared"]
+                                 E16=runner.embedding_f16(E_t, wl.V, wl.d) if p["prepared"]
                                  else None)
         if p["draw"] is not None:
             b.draw_temperature = torch.as_tensor(p["draw"]).cuda()

@@ -353,23 +353,23 @@ def test_draw_temperature_equal_to_statistics_is_the_plain_pass():
             assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), (cap, k)
 
 
-# --- the fp16 transposed embedding --------------------------------------------------------
+# --- the fp16 embedding ---------------------------------------------------------------------
 
-def test_embedding_f16t_is_the_fp16_transpose():
-    """dg_embedding_f16t: E16T[k][v] = fp16(E[v][k]) (round to nearest even, numpy's
-    conversion), zero past V up to the padded pitch; tiny and large entries included."""
+def test_embedding_f16_is_the_fp16_conversion():
+    """dg_embedding_f16: E16[v][k] = fp16(E[v][k]) (round to nearest even, numpy's
+    conversion), zero rows past V up to the padded row count; tiny and large entries included."""
     from denoise_step_sampler_amd import runner
     V, d = 1000, 256
     E = synth.bf16_to_f32(synth.make_embedding(V, d, seed=5)).copy()
     E[3, :8] = [1e-6, -3e-8, 6.1e-5, 65000.0, -65000.0, 1.0 + 2.0 ** -8, 2.0 ** -24, 0.0]
     E_bits = synth.round_to_bf16(E.astype(np.float32))
-    t = runner.embedding_f16t(runner.bf16_tensor(E_bits), V, d)
+    t = runner.embedding_f16(runner.bf16_tensor(E_bits), V, d)
     torch.cuda.synchronize()
-    pitch = (V + 255) // 256 * 256
-    got = t.cpu().numpy().view(np.uint16).reshape(d, pitch)
-    want = synth.bf16_to_f32(E_bits).astype(np.float16).view(np.uint16).T
-    assert np.array_equal(got[:, :V], want)
-    assert np.all(got[:, V:] == 0)
+    rows = (V + 255) // 256 * 256
+    got = t.cpu().numpy().view(np.uint16).reshape(rows, d)
+    want = synth.bf16_to_f32(E_bits).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got[:V], want)
+    assert np.all(got[V:] == 0)
 
 
 def test_prepared_embedding_gives_the_same_bits():
@@ -380,7 +380,7 @@ def test_prepared_embedding_gives_the_same_bits():
     wl.commit = np.array([0, 1, 0], np.uint8)
     a = runner.from_workload(wl)
     runner.vocab_pass(a, 6)
-    b = runner.from_workload(wl, E=a.E, E16T=runner.embedding_f16t(a.E, wl.V, wl.d))
+    b = runner.from_workload(wl, E=a.E, E16=runner.embedding_f16(a.E, wl.V, wl.d))
     runner.vocab_pass(b, 6)
     torch.cuda.synchronize()
     for k in ("lse", "entropy", "argmax_tok", "gumbel_tok", "selfcond"):
@@ -399,3 +399,30 @@ def test_flat_distributions_expectation(V, d, T):
     wl.temperature = np.full(2, T, np.float32)
     _, rep = _check(wl, seed=8, label=f"flat T={T}")
     assert rep["sc_max_rel"] < 1e-3
+
+@pytest.mark.parametrize("levels", [(100.0, 41.0, -18.0, -77.0), (41.0, 100.0, -18.0, -77.0),
+                                    (-120.0, 100.0, 41.0, -18.0)])
+def test_expectation_reference_chains(levels):
+    """Half tiles whose largest logits lie about 85 log2 units apart, in falling, mixed and
+    rising order, the rest of the vocabulary far below: the expectation scales every half
+    tile's weights to one unit per row (15 below the row's largest reference), exactly for the
+    half tiles near the top and to nothing for those far below, whatever the order in which
+    the half tiles arrive; the sums stay finite and meet the oracle at the bars of every
+    other case."""
+    V, d, n = 65536, 128, 1
+    rng = np.random.default_rng(31)
+    E = rng.normal(0.0, 0.05, (V, d)).astype(np.float32)
+    k = np.arange(V) // 128
+    lev = np.full(V, -150.0, np.float32)
+    for i, L in enumerate(levels):
+        lev[k == i] = L
+    E[:, 0] = lev - 0.5 * (np.arange(V) % 8)
+    wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=31, E=synth.round_to_bf16(E))
+    h = np.zeros((wl.R, d), np.float32)
+    h[:, 0] = 1.0
+    h[:, 1:] = rng.normal(0.0, 0.5, (wl.R, d - 1))
+    wl.h = synth.round_to_bf16(h)
+    wl.temperature = np.ones(n, np.float32)
+    wl.commit = np.zeros(n, np.uint8)
+    b, rep = _check(wl, seed=3, rows=np.arange(0, wl.R, 8), label=f"chain {levels}")
+    assert np.isfinite(b.selfcond.cpu().numpy()).all()
