@@ -21,7 +21,7 @@ DG_CANVAS = 256
 
 EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass_ex_workspace_size",
             "dg_embedding_f16_bytes", "dg_embedding_f16", "dg_vocab_pass", "dg_vocab_pass_softcap",
-            "dg_vocab_pass_ex", "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
+            "dg_vocab_pass_ex", "dg_vocab_pass_ex_noalloc", "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
             "dg_selfcond_input", "dg_lite_step", "dg_quantize_embedding_fp8",
             "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8", "dg_status_string",
             "dg_last_error")
@@ -62,6 +62,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_vocab_pass_ex.argtypes = [P, P, P, I, I, I, I, P, P, F, P, U64, P, P, P, P, P, P, P, SZ,
                                      P]
     lib.dg_vocab_pass_ex.restype = I
+    lib.dg_vocab_pass_ex_noalloc.argtypes = [P, P, P, I, I, I, I, P, P, F, P, U64, P, P, P, P, P,
+                                             P, P]
+    lib.dg_vocab_pass_ex_noalloc.restype = I
     lib.dg_accept_renoise.argtypes = [P, P, P, P, I, I, I, F, F, I, U64, P, P, P, P, P, P, P, P]
     lib.dg_accept_renoise.restype = I
     lib.dg_q_sample.argtypes = [P, I, I, I, P, U64, P, P]
@@ -319,6 +322,39 @@ def dg_lite_step(h: torch.Tensor, E: torch.Tensor, temperature: torch.Tensor, ls
         _ptr(final_tokens, torch.int32, R, "final_tokens"),
         _ptr(converged, torch.uint8, n_canvas, "converged"),
         _ptr(mean_entropy, torch.float32, n_canvas, "mean_entropy"), _stream(stream))
+    _check(st)
+
+
+DG_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dg_vocab_pass_ex_noalloc(E: torch.Tensor, E16: Optional[torch.Tensor], h: torch.Tensor,
+                             n_canvas: int, C: int, V: int, d: int,
+                             temperature: torch.Tensor, draw_temperature: Optional[torch.Tensor],
+                             softcap: float, commit: Optional[torch.Tensor], seed: int,
+                             step: torch.Tensor, lse: Optional[torch.Tensor],
+                             entropy: torch.Tensor, argmax_tok: torch.Tensor,
+                             gumbel_tok: torch.Tensor, selfcond: Optional[torch.Tensor],
+                             stream=None) -> None:
+    """dg_vocab_pass_ex in the library's static per-GPU scratch (no workspace, no allocation;
+    shapes beyond DG_NOALLOC_SCRATCH_BYTES of workspace raise DG_ERR_WORKSPACE)."""
+    R = n_canvas * C
+    lib = load()
+    st = lib.dg_vocab_pass_ex_noalloc(
+        _bf16_ptr(E, V * d, "E"), _f16_ptr(E16, d * e16_rows(V), "E16"),
+        _bf16_ptr(h, R * d, "h"), n_canvas, C, V, d,
+        _ptr(temperature, torch.float32, n_canvas, "temperature"),
+        _ptr(draw_temperature, torch.float32, n_canvas, "draw_temperature"),
+        ctypes.c_float(softcap),
+        _ptr(commit, torch.uint8, n_canvas, "commit"),
+        ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+        _ptr(step, torch.int32, n_canvas, "step"),
+        _ptr(lse, torch.float32, R, "lse"),
+        _ptr(entropy, torch.float32, R, "entropy"),
+        _ptr(argmax_tok, torch.int32, R, "argmax_tok"),
+        _ptr(gumbel_tok, torch.int32, R, "gumbel_tok"),
+        _ptr(selfcond, torch.float32, R * d, "selfcond"),
+        _stream(stream))
     _check(st)
 
 

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dg_internal.h"
 
 namespace {
@@ -220,6 +222,71 @@ dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16, const uint16_
   return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
                     nullptr, nullptr, E16, draw_temperature);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of dg_vocab_pass_ex_noalloc: one copy on every GPU the library runs on, held until
+// the process ends.  Host code never passes `scratch` itself (on the host it names a stand-in,
+// not device memory): each device's address comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+static __device__ __align__(256) unsigned char scratch[DG_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dg_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DG_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(DG_ERR_HIP, "scratch of device %d has no usable address", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_vocab_pass_ex_noalloc(const uint16_t* E, const uint16_t* E16, const uint16_t* h,
+                                   int n_canvas, int C, int V, int d, const float* temperature,
+                                   const float* draw_temperature, float softcap,
+                                   const uint8_t* commit, uint64_t seed, const int32_t* step,
+                                   float* lse, float* entropy, int32_t* argmax_tok,
+                                   int32_t* gumbel_tok, float* selfcond, void* stream) {
+  g_err[0] = 0;
+  if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
+    return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
+  if (!E) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  dg_status s = check_vocab_shape(n_canvas, C, V, d);
+  if (s != DG_OK) return s;
+  const size_t need = pass_bytes(n_canvas, V, d, selfcond != nullptr && E16 == nullptr);
+  if (need > DG_NOALLOC_SCRATCH_BYTES)
+    return fail(DG_ERR_WORKSPACE,
+                "n_canvas=%d V=%d d=%d needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use dg_vocab_pass_ex with a workspace)",
+                n_canvas, V, d, need, (size_t)DG_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != DG_OK) return s;
+  // nothing in the scratch needs to start at zero: every byte the kernels read is written
+  // earlier in the same call
+  return vocab_pass(E, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, ws, DG_NOALLOC_SCRATCH_BYTES, stream,
+                    softcap, nullptr, nullptr, E16, draw_temperature);
 }
 
 size_t dg_vocab_pass_fp8_workspace_size(int n_canvas, int C, int V, int d) {

@@ -161,6 +161,25 @@ dg_status dg_vocab_pass_ex(const uint16_t* E, const uint16_t* E16, const uint16_
                            int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* dg_vocab_pass_ex_noalloc -- dg_vocab_pass_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument and no allocation.  The pass runs in a static device array of
+ * DG_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs on until the
+ * process ends (its address is looked up once per device, on the first call with that device
+ * current).  Shapes whose dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, E16 != NULL)
+ * exceeds it fail with DG_ERR_WORKSPACE before anything is launched.  Every call on one GPU
+ * uses that GPU's one array: calls that may overlap on a GPU (different streams, or threads
+ * without ordering) race and give undefined results; calls ordered on one stream are safe.
+ * Arguments, layouts, outputs and results (bit for bit) as dg_vocab_pass_ex.
+ * Errors: as dg_vocab_pass_ex. */
+#define DG_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dg_status dg_vocab_pass_ex_noalloc(const uint16_t* E, const uint16_t* E16, const uint16_t* h,
+                                   int n_canvas, int C, int V, int d, const float* temperature,
+                                   const float* draw_temperature, float softcap,
+                                   const uint8_t* commit, uint64_t seed, const int32_t* step,
+                                   float* lse, float* entropy, int32_t* argmax_tok,
+                                   int32_t* gumbel_tok, float* selfcond, void* stream);
+
 /* dg_quantize_embedding_fp8 -- the tied embedding as FP8 ([VLLM] ships an FP8 checkpoint with
  * quantised weights; the pages give no scale scheme): OCP E4M3 codes (bias 7, largest finite
  * 448, no infinities) with one power-of-two scale 2^k per row,

@@ -30,7 +30,8 @@ def test_header_symbols_exported():
     decl = _declared()
     assert set(decl) == {"dg_vocab_pass_workspace_size", "dg_vocab_pass_ex_workspace_size",
                          "dg_embedding_f16_bytes", "dg_embedding_f16", "dg_vocab_pass",
-                         "dg_vocab_pass_softcap", "dg_vocab_pass_ex", "dg_accept_renoise",
+                         "dg_vocab_pass_softcap", "dg_vocab_pass_ex", "dg_vocab_pass_ex_noalloc",
+                         "dg_accept_renoise",
                          "dg_q_sample",
                          "dg_selfcond_input_workspace_size", "dg_selfcond_input",
                          "dg_lite_step", "dg_quantize_embedding_fp8",
@@ -213,3 +214,30 @@ def test_vocab_pass_ex_refusals_on_host():
     assert e(P, 4096, 192, P, None) == binding.DG_ERR_UNSUPPORTED
     assert e(None, 4096, 256, P, None) == binding.DG_ERR_INVALID_ARG
     assert e(P, 0, 256, P, None) == binding.DG_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    """dg_vocab_pass_ex_noalloc refuses, on the host and before any device call, a shape whose
+    workspace exceeds the static scratch, and a bad soft cap; a shape within it passes the
+    size check (the library's static scratch is 64 MiB, the binding states the same)."""
+    from denoise_step_sampler_amd import binding
+    lib = _lib()
+    assert binding.DG_NOALLOC_SCRATCH_BYTES == 64 << 20
+    f = lib.dg_vocab_pass_ex_noalloc
+    g = lib.dg_vocab_pass_ex_workspace_size
+    P = 1 << 20
+    big = (32, 256, 262144, 2816)
+    assert g(*big, 0) > binding.DG_NOALLOC_SCRATCH_BYTES
+    st = f(P, None, P, *big, P, None, 0.0, None, 0, P, None, P, P, P, P, None)
+    assert st == binding.DG_ERR_WORKSPACE
+    assert b"static scratch" in lib.dg_last_error()
+    # with a prepared fp16 embedding the same shape still needs far more than the scratch
+    st = f(P, P, P, *big, P, None, 0.0, None, 0, P, None, P, P, P, P, None)
+    assert st == binding.DG_ERR_WORKSPACE
+    st = f(P, None, P, 1, 256, 4096, 256, P, None, -1.0, None, 0, P, None, P, P, P, P, None)
+    assert st == binding.DG_ERR_INVALID_ARG and b"softcap" in lib.dg_last_error()
+    st = f(None, None, P, 1, 256, 4096, 256, P, None, 0.0, None, 0, P, None, P, P, P, P, None)
+    assert st == binding.DG_ERR_INVALID_ARG
+    st = f(P, None, P, 1, 256, 4096, 192, P, None, 0.0, None, 0, P, None, P, P, P, P, None)
+    assert st == binding.DG_ERR_UNSUPPORTED
+    assert g(3, 256, 5000, 256, 0) <= binding.DG_NOALLOC_SCRATCH_BYTES
