@@ -15,6 +15,13 @@ row, the row's largest |E| mapped to at most 448:
 
 A power-of-two scale keeps E~ exact in bf16 (E4M3 has 4 significant bits, bf16 8) and
 commutes with every rounding, so the FP8 pass is the bf16 pass on E~.
+
+Dynamic activations (the same page: the FP8 checkpoint quantises activations at run time,
+per token): reading used here, each row of the final hidden states h is quantised the same
+way as an embedding row, with its own power-of-two scale chosen from that row alone when the
+pass runs.  The FP8 x FP8 pass computes the logits of the dequantised rows h~ and E~,
+S~ = h~ E~^T, i.e. the bf16 pass on (h~, E~): both are exact bf16 numbers, and so is every
+product of two of them.
 """
 from __future__ import annotations
 
@@ -91,3 +98,15 @@ def quantize_rows(E: np.ndarray):
 
 def dequantize_rows(codes: np.ndarray, k: np.ndarray) -> np.ndarray:
     return e4m3_value(codes) * np.exp2(np.asarray(k, np.float64))[:, None]
+
+
+def activation_rows(h_bits: np.ndarray):
+    """Dynamic per-row quantisation of the final hidden states (bf16 bits [R, d]) for the
+    FP8 x FP8 pass: (codes uint8 [R, d], exponents int [R], the dequantised rows h~ as bf16
+    bits [R, d], exact)."""
+    h = (np.asarray(h_bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, k = quantize_rows(h)
+    hq = dequantize_rows(codes, k)
+    bits = (hq.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64), hq)
+    return codes, k, bits

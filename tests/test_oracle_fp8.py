@@ -64,3 +64,18 @@ def test_quantized_rows_error_and_bf16_exactness():
     f32 = D.astype(np.float32)
     assert np.array_equal(synth.bf16_to_f32(synth.round_to_bf16(f32)), f32)
     assert np.array_equal(f32.astype(np.float64), D)
+
+
+def test_dynamic_activation_rows_by_hand():
+    """A hidden-state row quantised at run time: max |h| = 3 gives k = -7 (448 2^-8 = 1.75 < 3
+    <= 3.5 = 448 2^-7); 3 * 2^7 = 384 = 1.5 2^8 -> 0x7C, -1 * 2^7 -> 0xF0, bf16(0.3) =
+    0.30078125 -> 38.5 -> 40 = 1.25 2^5 -> 0x62 (dequantised 0.3125), 0 -> 0x00; a zero row
+    takes the floor -117 and zero codes."""
+    row = np.zeros((2, 8), np.float32)
+    row[0, :4] = [3.0, -1.0, 0.3, 0.0]
+    bits = synth.round_to_bf16(row)
+    codes, k, hq = fp8.activation_rows(bits)
+    assert list(k) == [-7, -117]
+    assert list(codes[0, :4]) == [0x7C, 0xF0, 0x62, 0x00] and not codes[1].any()
+    assert list(synth.bf16_to_f32(hq)[0, :4]) == [3.0, -1.0, 0.3125, 0.0]
+    assert not synth.bf16_to_f32(hq)[1].any()
