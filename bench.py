@@ -20,6 +20,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # the logits kernel's source and the headers it includes (the counters are void once any changes)
 KERNEL_SRCS = [os.path.join(ROOT, "denoise_step_sampler_amd", "csrc", f)
@@ -174,7 +175,8 @@ def full_loop(args) -> int:
         "value": res.positions_per_s, "unit": "canvas-positions/s",
         "n_gpus": 1, "steps": res.steps_run, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "fp8-e4m3 logits, fp16 expectation" if args.fp8_act else "bf16",
+        "data": "synthetic",
         "config": {"workload": "full_loop", "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
                    "d": wl.d, "max_steps": 32,
                    "temperature": (float(wl.temperature[0]) if sched is None else
@@ -204,6 +206,9 @@ def main() -> int:
                     help="only run a plain device copy of MB MiB (counter calibration)")
     ap.add_argument("--fp8", action="store_true",
                     help="run the step on the FP8 form of the embedding (dg_vocab_pass_fp8)")
+    ap.add_argument("--fp8-act", action="store_true",
+                    help="FP8 embedding and hidden states quantised per row in the pass, FP8 x "
+                         "FP8 MFMA (dg_vocab_pass_fp8_dyn); implies --fp8")
     ap.add_argument("--softcap", type=float, default=None,
                     help="final-logit soft cap c (logits c tanh(S / c)); default: none")
     ap.add_argument("--ffw-F", type=int, default=2816, metavar="F",
@@ -212,6 +217,7 @@ def main() -> int:
     ap.add_argument("--anneal", default=None, metavar="TMAX,TMIN",
                     help="full_loop only: linear temperature schedule over the 32 steps")
     args = ap.parse_args()
+    args.fp8 = args.fp8 or args.fp8_act
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the vocabulary pass would shard by canvas or by vocabulary range)",
@@ -241,11 +247,12 @@ def main() -> int:
     seed = args.seed
     if args.fp8:
         f8 = runner.quantize_embedding_fp8(b.E, wl.V, wl.d, stream=stream)
-        ws8 = runner.fp8_workspace(wl.n_canvas, wl.V, wl.d)
+        ws8 = runner.fp8_workspace(wl.n_canvas, wl.V, wl.d, activations=args.fp8_act)
 
     def vocab(k_stream):
         if args.fp8:
-            runner.vocab_pass_fp8(b, f8, ws8, seed, k_stream, args.softcap)
+            runner.vocab_pass_fp8(b, f8, ws8, seed, k_stream, args.softcap,
+                                  activations=args.fp8_act)
         else:
             runner.vocab_pass(b, seed, k_stream, args.softcap)
 
@@ -292,10 +299,10 @@ def main() -> int:
     for k in range(args.steps):
         ev2[k][0].record(stream)
         if args.fp8:
-            B.dg_vocab_pass_fp8(f8.codes, f8.E16, f8.row_exp, b.h, b.n_canvas, b.C, b.V, b.d,
-                                b.temperature, b.commit, seed, b.step, b.lse, b.entropy,
-                                b.argmax_tok, b.gumbel_tok, None, ws8, stream=stream,
-                                softcap=args.softcap or 0.0)
+            fn = B.dg_vocab_pass_fp8_dyn if args.fp8_act else B.dg_vocab_pass_fp8
+            fn(f8.codes, f8.E16, f8.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
+               b.commit, seed, b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, None, ws8,
+               stream=stream, softcap=args.softcap or 0.0)
         else:
             B.dg_vocab_pass_ex(b.E, b.E16, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, None,
                                args.softcap or 0.0, b.commit, seed, b.step, b.lse, b.entropy,
@@ -357,6 +364,8 @@ def main() -> int:
     flops = algorithmic_flops(wl)
     flops_k1 = 2.0 * wl.R * wl.V * wl.d
     ach_k1 = flops_k1 / (k1_ms * 1e-3) / 1e12
+    # the logits contraction's own dtype sets its peak (FP8 x FP8 with --fp8-act)
+    peak_k1 = PEAK_FP8_TFLOPS if args.fp8_act else PEAK_BF16_TFLOPS
     positions = wl.R
     res = {
         "metric": "canvas-positions/sec per denoise step",
@@ -365,12 +374,15 @@ def main() -> int:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "fp8-e4m3 logits, fp16 expectation" if args.fp8_act else "bf16",
+        "data": "synthetic",
         "config": {"workload": args.workload, "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
                    "d": wl.d, "commit_canvases": int(wl.commit.sum()),
                    "temperature": float(wl.temperature[0]), "entropy_budget": wl.budget,
                    "softcap": args.softcap,
-                   "embedding": ("fp8-e4m3, power-of-two row scales" if args.fp8 else "bf16")
+                   "embedding": (("fp8-e4m3, power-of-two row scales"
+                                  + (", hidden states quantised per row in the pass"
+                                     if args.fp8_act else "")) if args.fp8 else "bf16")
                    + "; its fp16 copy for the expectation prepared once, untimed",
                    "caches": "warm: no L2 / MALL flush between steps"},
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
@@ -385,8 +397,8 @@ def main() -> int:
                      "tokens_per_s": qw.n_canvas * 256 / (float(np.median(qs_ms)) * 1e-3)},
         "roofline": {
             "kernel": "k_gemm_logits",
-            "bound": "mfma", "achieved": ach_k1, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": ach_k1 / PEAK_BF16_TFLOPS,
+            "bound": "mfma", "achieved": ach_k1, "peak": peak_k1,
+            "unit": "TFLOP/s", "frac": ach_k1 / peak_k1,
             # the counters were taken on the uncapped kernel
             "traffic": (measured_traffic(args.workload)
                         if args.softcap is None and not args.fp8 else None),

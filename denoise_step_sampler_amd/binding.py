@@ -23,7 +23,8 @@ EXPORTED = ("dg_vocab_pass_workspace_size", "dg_vocab_pass_ex_workspace_size",
             "dg_embedding_f16_bytes", "dg_embedding_f16", "dg_vocab_pass", "dg_vocab_pass_softcap",
             "dg_vocab_pass_ex", "dg_vocab_pass_ex_noalloc", "dg_accept_renoise", "dg_q_sample", "dg_selfcond_input_workspace_size",
             "dg_selfcond_input", "dg_lite_step", "dg_quantize_embedding_fp8",
-            "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8", "dg_status_string",
+            "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8",
+            "dg_vocab_pass_fp8_dyn_workspace_size", "dg_vocab_pass_fp8_dyn", "dg_status_string",
             "dg_last_error")
 
 
@@ -83,6 +84,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dg_vocab_pass_fp8.argtypes = [P, P, P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P, SZ,
                                       P, F]
     lib.dg_vocab_pass_fp8.restype = I
+    lib.dg_vocab_pass_fp8_dyn_workspace_size.argtypes = [I, I, I, I]
+    lib.dg_vocab_pass_fp8_dyn_workspace_size.restype = SZ
+    lib.dg_vocab_pass_fp8_dyn.argtypes = [P, P, P, P, I, I, I, I, P, P, U64, P, P, P, P, P, P, P,
+                                          SZ, P, F]
+    lib.dg_vocab_pass_fp8_dyn.restype = I
     lib.dg_status_string.argtypes = [I]
     lib.dg_status_string.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -373,17 +379,10 @@ def dg_vocab_pass_fp8_workspace_size(n_canvas: int, C: int, V: int, d: int) -> i
     return int(load().dg_vocab_pass_fp8_workspace_size(n_canvas, C, V, d))
 
 
-def dg_vocab_pass_fp8(codes: torch.Tensor, E16: Optional[torch.Tensor], row_exp: torch.Tensor,
-                      h: torch.Tensor, n_canvas: int,
-                      C: int, V: int, d: int, temperature: torch.Tensor,
-                      commit: Optional[torch.Tensor], seed: int, step: torch.Tensor,
-                      lse: Optional[torch.Tensor], entropy: torch.Tensor,
-                      argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
-                      selfcond: Optional[torch.Tensor], workspace: torch.Tensor, stream=None,
-                      softcap: float = 0.0) -> None:
+def _fp8_pass(fn, codes, E16, row_exp, h, n_canvas, C, V, d, temperature, commit, seed, step,
+              lse, entropy, argmax_tok, gumbel_tok, selfcond, workspace, stream, softcap):
     R = n_canvas * C
-    lib = load()
-    st = lib.dg_vocab_pass_fp8(
+    st = fn(
         _ptr(codes, torch.uint8, V * d, "codes"),
         _f16_ptr(E16, d * e16_rows(V), "E16"),
         _ptr(row_exp, torch.int32, V, "row_exp"),
@@ -399,3 +398,34 @@ def dg_vocab_pass_fp8(codes: torch.Tensor, E16: Optional[torch.Tensor], row_exp:
         _ptr(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream),
         ctypes.c_float(softcap))
     _check(st)
+
+
+def dg_vocab_pass_fp8(codes: torch.Tensor, E16: Optional[torch.Tensor], row_exp: torch.Tensor,
+                      h: torch.Tensor, n_canvas: int,
+                      C: int, V: int, d: int, temperature: torch.Tensor,
+                      commit: Optional[torch.Tensor], seed: int, step: torch.Tensor,
+                      lse: Optional[torch.Tensor], entropy: torch.Tensor,
+                      argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                      selfcond: Optional[torch.Tensor], workspace: torch.Tensor, stream=None,
+                      softcap: float = 0.0) -> None:
+    _fp8_pass(load().dg_vocab_pass_fp8, codes, E16, row_exp, h, n_canvas, C, V, d, temperature,
+              commit, seed, step, lse, entropy, argmax_tok, gumbel_tok, selfcond, workspace,
+              stream, softcap)
+
+
+def dg_vocab_pass_fp8_dyn_workspace_size(n_canvas: int, C: int, V: int, d: int) -> int:
+    return int(load().dg_vocab_pass_fp8_dyn_workspace_size(n_canvas, C, V, d))
+
+
+def dg_vocab_pass_fp8_dyn(codes: torch.Tensor, E16: Optional[torch.Tensor],
+                          row_exp: torch.Tensor, h: torch.Tensor, n_canvas: int,
+                          C: int, V: int, d: int, temperature: torch.Tensor,
+                          commit: Optional[torch.Tensor], seed: int, step: torch.Tensor,
+                          lse: Optional[torch.Tensor], entropy: torch.Tensor,
+                          argmax_tok: torch.Tensor, gumbel_tok: torch.Tensor,
+                          selfcond: Optional[torch.Tensor], workspace: torch.Tensor,
+                          stream=None, softcap: float = 0.0) -> None:
+    """dg_vocab_pass_fp8 with h quantised per row to FP8 inside the call (FP8 x FP8 MFMA)."""
+    _fp8_pass(load().dg_vocab_pass_fp8_dyn, codes, E16, row_exp, h, n_canvas, C, V, d,
+              temperature, commit, seed, step, lse, entropy, argmax_tok, gumbel_tok, selfcond,
+              workspace, stream, softcap)

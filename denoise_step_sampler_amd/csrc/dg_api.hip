@@ -31,8 +31,14 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace of the vocabulary pass: the two-GEMM pieces, then (when the caller gives no fp16
 // embedding and the expectation is asked for) room to build one.
 size_t gemm_bytes(int n_canvas, int V, int d) { return al256(dg::gemm_plan(n_canvas, V, d).bytes); }
-size_t pass_bytes(int n_canvas, int V, int d, bool build_e16) {
-  return gemm_bytes(n_canvas, V, d) + (build_e16 ? al256(dg::e16_bytes(V, d)) : 0);
+// FP8 x FP8 pass: the hidden states' codes [R, d] and row exponents [R], quantised per call
+size_t a8_bytes(int n_canvas, int d) {
+  const size_t R = (size_t)n_canvas * DG_CANVAS;
+  return al256(R * (size_t)d) + al256(R * 4);
+}
+size_t pass_bytes(int n_canvas, int V, int d, bool build_e16, bool a8 = false) {
+  return gemm_bytes(n_canvas, V, d) + (build_e16 ? al256(dg::e16_bytes(V, d)) : 0) +
+         (a8 ? a8_bytes(n_canvas, d) : 0);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -130,7 +136,7 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
                      int32_t* gumbel_tok, float* selfcond, void* workspace,
                      size_t workspace_bytes, void* stream, float softcap, const uint8_t* E8,
                      const int32_t* E_exp, const uint16_t* E16,
-                     const float* draw_temperature) {
+                     const float* draw_temperature, bool a8 = false) {
   dg_status s = check_vocab_shape(n_canvas, C, V, d);
   if (s != DG_OK) return s;
   if ((!E && !E8) || !h || !temperature || !step || !entropy || !argmax_tok || !gumbel_tok)
@@ -140,7 +146,7 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   if (selfcond && !aligned16(selfcond))
     return fail(DG_ERR_INVALID_ARG, "selfcond must be 16-byte aligned");
   const bool build = selfcond != nullptr && E16 == nullptr;
-  const size_t need = pass_bytes(n_canvas, V, d, build);
+  const size_t need = pass_bytes(n_canvas, V, d, build, a8);
   if (!workspace || workspace_bytes < need)
     return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -154,6 +160,17 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
                             : dg::e16_launch(E, V, d, e16, st);
     if (e != hipSuccess) return hip_fail(e, "fp16 embedding launch");
     E16 = e16;
+  }
+  uint8_t* h8 = nullptr;
+  int32_t* h_exp = nullptr;
+  if (a8) {  // the hidden states quantised per row (dynamic activations)
+    char* q = static_cast<char*>(workspace) + gemm_bytes(n_canvas, V, d) +
+              (build ? al256(dg::e16_bytes(V, d)) : 0);
+    const size_t R = (size_t)n_canvas * DG_CANVAS;
+    h8 = reinterpret_cast<uint8_t*>(q);
+    h_exp = reinterpret_cast<int32_t*>(q + al256(R * (size_t)d));
+    const hipError_t e = dg::fp8_quantize_launch(h, (int)R, d, h8, h_exp, st);
+    if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
   }
   dg::VocabArgs a{};
   a.E = E;
@@ -175,6 +192,8 @@ dg_status vocab_pass(const uint16_t* E, const uint16_t* h, int n_canvas, int C, 
   a.E8 = E8;
   a.E_exp = E_exp;
   a.E16 = E16;
+  a.h8 = h8;
+  a.h_exp = h_exp;
   const hipError_t e = dg::gemm_launch(a, dg::gemm_plan(n_canvas, V, d), workspace, st);
   if (e != hipSuccess) return hip_fail(e, "vocab pass launch");
   return DG_OK;
@@ -327,6 +346,29 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16, const int
   return vocab_pass(nullptr, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
                     argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
                     codes, row_exp, E16, nullptr);
+}
+
+size_t dg_vocab_pass_fp8_dyn_workspace_size(int n_canvas, int C, int V, int d) {
+  const size_t g = dg_vocab_pass_ex_workspace_size(n_canvas, C, V, d, 0);
+  return g == 0 ? 0 : g + a8_bytes(n_canvas, d);
+}
+
+dg_status dg_vocab_pass_fp8_dyn(const uint8_t* codes, const uint16_t* E16,
+                                const int32_t* row_exp, const uint16_t* h, int n_canvas, int C,
+                                int V, int d, const float* temperature, const uint8_t* commit,
+                                uint64_t seed, const int32_t* step, float* lse, float* entropy,
+                                int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                float softcap) {
+  g_err[0] = 0;
+  if (!codes || !row_exp) return fail(DG_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(codes) || !aligned16(row_exp))
+    return fail(DG_ERR_INVALID_ARG, "codes and row_exp must be 16-byte aligned");
+  if (softcap != 0.0f && (!(softcap > 0.0f) || !isfinite(softcap)))
+    return fail(DG_ERR_INVALID_ARG, "softcap must be 0 or finite and > 0");
+  return vocab_pass(nullptr, h, n_canvas, C, V, d, temperature, commit, seed, step, lse, entropy,
+                    argmax_tok, gumbel_tok, selfcond, workspace, workspace_bytes, stream, softcap,
+                    codes, row_exp, E16, nullptr, true);
 }
 
 dg_status dg_accept_renoise(const float* entropy, const int32_t* argmax_tok,

@@ -31,6 +31,10 @@ struct VocabArgs {
   // E = 2^E_exp[v] * value(codes); null: the logits pass reads E (then E is not read at all)
   const uint8_t* E8;
   const int32_t* E_exp;
+  // FP8 hidden states (with E8): E4M3 codes [R, d] and row exponents [R] of h, quantised per
+  // row when the pass runs; the logits pass then multiplies codes by codes on FP8 MFMA
+  const uint8_t* h8;
+  const int32_t* h_exp;
   // the expectation pass's operand: the embedding as fp16, [e16_rows(V)][d], rows past V zero
   // (required with selfcond)
   const uint16_t* E16;

@@ -425,25 +425,46 @@ __device__ __forceinline__ u32x4 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
 #undef DG_CV
 }
 
-// kF8: E arrives as E4M3 codes with a power-of-two scale per row (g.a.E8, g.a.E_exp).  The
-// codes are staged as 64-byte rows; one 16-byte read gives a lane the codes of two 16-wide K
-// steps, widened to bf16 in registers; the h fragments use the same permutation of K within
-// the chunk (step 2 j + t, lane half f: K = 32 j + 16 f + 8 t + 0..7), and the accumulator of
-// entry v is scaled by 2^E_exp[v] before the epilogue (exact).
-template <bool kCap, bool kF8, bool kSep = false>
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 x E4M3 (format codes 0): a lane's 32 codes of A
+// (row lane % 32) and of B (column lane % 32) as two 16-byte halves each; E8M0 scales sa, sb
+// (byte 0 of each) of the lane's A row and B column, 2^(s - 127).
+__device__ __forceinline__ f32x16 mfma32x32x64f8(const u32x4& a0, const u32x4& a1,
+                                                 const u32x4& b0, const u32x4& b1, f32x16 c,
+                                                 int sa, int sb) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// kMode 1 (kF8): E arrives as E4M3 codes with a power-of-two scale per row (g.a.E8,
+// g.a.E_exp).  The codes are staged as 64-byte rows; one 16-byte read gives a lane the codes of
+// two 16-wide K steps, widened to bf16 in registers; the h fragments use the same permutation
+// of K within the chunk (step 2 j + t, lane half f: K = 32 j + 16 f + 8 t + 0..7), and the
+// accumulator of entry v is scaled by 2^E_exp[v] before the epilogue (exact).
+// kMode 2 (kA8): E and h both as E4M3 codes with power-of-two row scales (h quantised per row
+// when the pass runs).  Both are staged like the bf16 operands, 128-byte rows, now 128 K
+// elements a chunk; v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 64-wide K steps (lane half f
+// holds K = 64 s + 32 f + 0..31 of its row, two 16-byte reads) and applies the two row scales
+// as its E8M0 block scales, so the accumulator holds S itself.  The MFMA's own summation of a
+// 64-wide step is not exact (measured: within 2^-11.9 of the step's largest product).
+template <bool kCap, int kMode, bool kSep = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
+  constexpr bool kF8 = kMode == 1, kA8 = kMode == 2;
   constexpr int kERow = kF8 ? kKC1 : kRow1;    // bytes of one staged E row
   constexpr int kHOff = kTile * kERow;         // 256 E rows, then 256 h rows
   constexpr int kStage = kHOff + kTile * kRow1;
   __shared__ __attribute__((aligned(1024))) char stg[kNst1][kStage];
-  const char* Eb = kF8 ? reinterpret_cast<const char*>(g.a.E8) : reinterpret_cast<const char*>(g.a.E);
-  const uint16_t* h = g.a.h;
+  const char* Eb = (kF8 || kA8) ? reinterpret_cast<const char*>(g.a.E8)
+                                : reinterpret_cast<const char*>(g.a.E);
   const int V = g.a.V, d = g.a.d, n_canvas = g.a.n_canvas;
   const int t = threadIdx.x, lane = t & 63, fr = lane & 31, fh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int vh = w & 1, rq = w >> 1;  // wave tile: vocabulary half vh x rows [64 rq, 64 rq + 64)
   const int T = g.n_tiles;
-  const int nk = d / kKC1;  // even (d % 128 == 0)
+  const int nk = kA8 ? d / 128 : d / kKC1;  // chunks; even but for kA8 (d % 128 == 0)
   const size_t R = (size_t)n_canvas * kTile;
 
   int start, gsz;
@@ -459,7 +480,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   uint32_t rdE[4], rdH[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    if (kF8) {
+    if (kA8) {
+      // 64-wide step s = ks / 2, its 16-byte half ks % 2: segment 4 s + 2 fh + ks % 2
+      const int seg = 4 * (ks >> 1) + 2 * fh + (ks & 1);
+      rdE[ks] = (uint32_t)((128 * vh + fr) * kRow1 + 16 * (seg ^ sw));
+      rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 + 16 * (seg ^ sw));
+    } else if (kF8) {
       // code rows: 16-byte segment q of row r at q ^ ((r >> 2) & 3); reads j = 0, 1
       rdE[ks] = (uint32_t)((128 * vh + fr) * kERow + 16 * (((2 * (ks & 1) + fh)) ^ ((fr >> 2) & 3)));
       rdH[ks] = (uint32_t)(kHOff + (64 * rq + fr) * kRow1 +
@@ -473,13 +499,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   // global segment slot ^ swz1(row).  Wave w copies E rows and h rows [32 w, 32 w + 32) of
   // the stage, four copies each.  Sources: a wave-uniform base plus a 32-bit lane offset.
   const int dlrow = lane >> 3;
-  const uint32_t pitch = 2u * (uint32_t)d;
-  const uint32_t epitch = kF8 ? (uint32_t)d : pitch;
+  const uint32_t pitch = kA8 ? (uint32_t)d : 2u * (uint32_t)d;  // bytes of an h row
+  const uint32_t epitch = (kF8 || kA8) ? (uint32_t)d : pitch;
   uint32_t offH[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     offH[j] = (uint32_t)(8 * j + dlrow) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
-  const char* hb = reinterpret_cast<const char*>(h) + ((size_t)c * kTile + 32 * w) * pitch;
+  const char* hb = (kA8 ? reinterpret_cast<const char*>(g.a.h8)
+                        : reinterpret_cast<const char*>(g.a.h)) +
+                   ((size_t)c * kTile + 32 * w) * pitch;
   // E rows of the wave's block of tile tt, clamped to V - 1: base row and lane offsets
   // (code rows: two copies of 16 rows, lane -> row 16 j + lane / 4, segment lane % 4)
   auto e_src = [&](int tt, const char*& eb, uint32_t (&oe)[4]) {
@@ -493,7 +521,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
         oe[j] = (uint32_t)(rv - rb) * epitch + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
       } else {
         const int rv = min(r0 + 8 * j + dlrow, V - 1);
-        oe[j] = (uint32_t)(rv - rb) * pitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
+        oe[j] = (uint32_t)(rv - rb) * epitch + 16u * (uint32_t)((lane & 7) ^ swz1(8 * j + dlrow));
       }
     }
   };
@@ -598,6 +626,36 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
                                   : e4m3x8_bf16(c8[mb][2], c8[mb][3]);
     }
   };
+  // kA8: both 64-wide steps of the chunk, their fragments read at once (two 16-byte halves
+  // per operand block), E rows scaled by 2^(sA - 127), h rows by 2^(sB - 127)
+  int sA[4] = {127, 127, 127, 127}, sB[2] = {127, 127};
+  auto chunk_a8 = [&](const char* sc, uint32_t sn, int kn, const char* eb,
+                      const uint32_t (&oe)[4]) {
+    vm_wait<0>();
+    __syncthreads();
+    const lds_char* s = (const lds_char*)sc;
+    u32x4 a8[2][4][2], b8[2][2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) a8[st][mb][hf] = lds_read16(s + rdE[2 * st + hf] + 32 * kRow1 * mb);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) b8[st][nb][hf] = lds_read16(s + rdH[2 * st + hf] + 32 * kRow1 * nb);
+      }
+    issue_e(kn, eb, oe, sn);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st == 1) issue_h(kn, sn);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = mfma32x32x64f8(a8[st][mb][0], a8[st][mb][1], b8[st][nb][0], b8[st][nb][1],
+                                       acc[mb][nb], sA[mb], sB[nb]);
+    }
+  };
   auto chunk = [&](auto deferred, const char* sc, uint32_t sn, int kn, const char* eb,
                    const uint32_t (&oe)[4]) {
     if constexpr (kF8) {
@@ -664,8 +722,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
   uint32_t oe[4];
   e_src(ln.lane, eb, oe);
   issue(0, eb, oe, sa[0]);
-  // nk is even: every tile starts on stage 0, and its last chunk copies the next tile's
-  // first chunk (or, after the last tile, repeats this tile's; never read)
+  if constexpr (kA8) {
+    sB[0] = g.a.h_exp[(size_t)c * kTile + 64 * rq + fr] + 127;
+    sB[1] = g.a.h_exp[(size_t)c * kTile + 64 * rq + 32 + fr] + 127;
+  }
+  int cur = 0;  // kA8: the stage holding the tile's first chunk (nk may be odd)
+  // bf16 and kF8: nk is even, every tile starts on stage 0, and its last chunk copies the next
+  // tile's first chunk (or, after the last tile, repeats this tile's; never read)
   for (int tt = ln.lane; tt < T; tt += ln.L) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -674,14 +737,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
     const char* ebn;
     uint32_t oen[4];
     e_src(tt + ln.L < T ? tt + ln.L : tt, ebn, oen);
-    // chunk j is computed from stage j % 2 and copies chunk j + 1 into the other stage
-    chunk(std::false_type{}, stg[0], sa[1], 1, eb, oe);
-    for (int kc = 1; kc < nk - 1; kc += 2) {
-      chunk(std::true_type{}, stg[1], sa[0], kc + 1, eb, oe);
-      chunk(std::true_type{}, stg[0], sa[1], kc + 2, eb, oe);
+    if constexpr (kA8) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        sA[mb] = g.a.E_exp[min(tt * kTile + kHalf * vh + 32 * mb + fr, V - 1)] + 127;
+      // chunk kc from stage cur, copying chunk kc + 1 (after the last: the next tile's first)
+      // into the other stage
+      for (int kc = 0; kc < nk; ++kc) {
+        const bool last = kc + 1 == nk;
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = last ? oen[j] : oe[j];
+        chunk_a8(cur ? stg[1] : stg[0], cur ? sa[0] : sa[1], last ? 0 : kc + 1,
+                 last ? ebn : eb, o);
+        cur ^= 1;
+      }
+    } else {
+      // chunk j is computed from stage j % 2 and copies chunk j + 1 into the other stage
+      chunk(std::false_type{}, stg[0], sa[1], 1, eb, oe);
+      for (int kc = 1; kc < nk - 1; kc += 2) {
+        chunk(std::true_type{}, stg[1], sa[0], kc + 1, eb, oe);
+        chunk(std::true_type{}, stg[0], sa[1], kc + 2, eb, oe);
+      }
+      chunk(std::true_type{}, stg[1], sa[0], 0, ebn, oen);
+      last_step();
     }
-    chunk(std::true_type{}, stg[1], sa[0], 0, ebn, oen);
-    last_step();
     eb = ebn;
 #pragma unroll
     for (int j = 0; j < 4; ++j) oe[j] = oen[j];
@@ -1371,20 +1451,25 @@ hipError_t gemm_launch(const VocabArgs& a, const GemmPlan& p, void* workspace,
   if (e != hipSuccess) return e;
   const dim3 grid1((unsigned)(kWG * p.n_rounds));
   const bool cap = a.softcap != 0.0f, sep = a.draw_temperature != nullptr;
-  if (a.E8 != nullptr) {
+  if (a.E8 != nullptr && a.h8 != nullptr) {
     if (cap)
-      hipLaunchKernelGGL((k_gemm_logits<true, true>), grid1, dim3(512), 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_logits<true, 2>), grid1, dim3(512), 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_logits<false, true>), grid1, dim3(512), 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_logits<false, 2>), grid1, dim3(512), 0, stream, g);
+  } else if (a.E8 != nullptr) {
+    if (cap)
+      hipLaunchKernelGGL((k_gemm_logits<true, 1>), grid1, dim3(512), 0, stream, g);
+    else
+      hipLaunchKernelGGL((k_gemm_logits<false, 1>), grid1, dim3(512), 0, stream, g);
   } else if (sep) {
     if (cap)
-      hipLaunchKernelGGL((k_gemm_logits<true, false, true>), grid1, dim3(512), 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_logits<true, 0, true>), grid1, dim3(512), 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_logits<false, false, true>), grid1, dim3(512), 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_logits<false, 0, true>), grid1, dim3(512), 0, stream, g);
   } else if (cap) {
-    hipLaunchKernelGGL((k_gemm_logits<true, false>), grid1, dim3(512), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_logits<true, 0>), grid1, dim3(512), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((k_gemm_logits<false, false>), grid1, dim3(512), 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_logits<false, 0>), grid1, dim3(512), 0, stream, g);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

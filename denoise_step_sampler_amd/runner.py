@@ -214,20 +214,26 @@ def quantize_embedding_fp8(E: torch.Tensor, V: int, d: int, stream=None,
     return f
 
 
-def fp8_workspace(n_canvas: int, V: int, d: int, device="cuda") -> torch.Tensor:
-    n = B.dg_vocab_pass_fp8_workspace_size(n_canvas, B.DG_CANVAS, V, d)
+def fp8_workspace(n_canvas: int, V: int, d: int, device="cuda",
+                  activations: bool = False) -> torch.Tensor:
+    """Workspace of vocab_pass_fp8 (activations=True: of the FP8 x FP8 pass)."""
+    f = B.dg_vocab_pass_fp8_dyn_workspace_size if activations else B.dg_vocab_pass_fp8_workspace_size
+    n = f(n_canvas, B.DG_CANVAS, V, d)
     if n == 0:
         raise ValueError(f"unsupported shape n={n_canvas} V={V} d={d}")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def vocab_pass_fp8(b: VocabBuffers, f: Fp8Embedding, workspace: torch.Tensor, seed: int,
-                   stream=None, softcap: Optional[float] = None) -> None:
-    """The vocabulary pass on the FP8 embedding f (b.E is not read)."""
-    B.dg_vocab_pass_fp8(f.codes, f.E16, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature,
-                        b.commit, seed, b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok,
-                        b.selfcond, workspace, stream=stream,
-                        softcap=0.0 if softcap is None else softcap)
+                   stream=None, softcap: Optional[float] = None,
+                   activations: bool = False) -> None:
+    """The vocabulary pass on the FP8 embedding f (b.E is not read); activations=True
+    quantises h per row too and multiplies FP8 by FP8 (workspace from
+    fp8_workspace(..., activations=True))."""
+    fn = B.dg_vocab_pass_fp8_dyn if activations else B.dg_vocab_pass_fp8
+    fn(f.codes, f.E16, f.row_exp, b.h, b.n_canvas, b.C, b.V, b.d, b.temperature, b.commit, seed,
+       b.step, b.lse, b.entropy, b.argmax_tok, b.gumbel_tok, b.selfcond, workspace,
+       stream=stream, softcap=0.0 if softcap is None else softcap)
 
 
 def temperature_schedule(i: int, N: int, t_max: float, t_min: float) -> float:

@@ -215,6 +215,30 @@ dg_status dg_vocab_pass_fp8(const uint8_t* codes, const uint16_t* E16, const int
                             int32_t* gumbel_tok, float* selfcond, void* workspace,
                             size_t workspace_bytes, void* stream, float softcap);
 
+/* dg_vocab_pass_fp8_dyn_workspace_size -- bytes of workspace dg_vocab_pass_fp8_dyn needs
+ * ([host], pure; 0 if unsupported): dg_vocab_pass_fp8_workspace_size plus room for the
+ * quantised hidden states (n_canvas C d bytes of codes and n_canvas C exponents). */
+size_t dg_vocab_pass_fp8_dyn_workspace_size(int n_canvas, int C, int V, int d);
+
+/* dg_vocab_pass_fp8_dyn -- dg_vocab_pass_fp8 with the hidden states in FP8 as well ([VLLM]:
+ * an FP8 checkpoint with quantised weights and dynamic activations).  Each row of h is
+ * quantised when the pass runs, by the rule of dg_quantize_embedding_fp8 applied to that row
+ * alone (E4M3 codes, power-of-two scale 2^kh_r), and the logits are those of the dequantised
+ * rows: S~[r, v] = 2^(kh_r + row_exp[v]) sum_j value(hq_rj) value(codes_vj), multiplied code by
+ * code on FP8 MFMA with both scales applied by the MFMA.  The MFMA sums each 64-wide block of
+ * products with an error of up to about 2^-12 of the block's largest product (its own
+ * rounding, not fp32's), so S~ is met to that accuracy rather than to fp32 rounding; the
+ * statistics, samples and expectation follow from it as in dg_vocab_pass.
+ *  workspace  dg_vocab_pass_fp8_dyn_workspace_size(n_canvas, C, V, d) bytes.
+ * Other arguments, layouts, outputs and errors as dg_vocab_pass_fp8. */
+dg_status dg_vocab_pass_fp8_dyn(const uint8_t* codes, const uint16_t* E16,
+                                const int32_t* row_exp, const uint16_t* h, int n_canvas, int C,
+                                int V, int d, const float* temperature, const uint8_t* commit,
+                                uint64_t seed, const int32_t* step, float* lse, float* entropy,
+                                int32_t* argmax_tok, int32_t* gumbel_tok, float* selfcond,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                float softcap);
+
 /* dg_accept_renoise -- per-canvas acceptance, renoising and convergence of one step.
  *
  * For a canvas that does not commit ([TR] sec. 3.3 "Entropy-bounded token refinement",

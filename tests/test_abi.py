@@ -36,6 +36,7 @@ def test_header_symbols_exported():
                          "dg_selfcond_input_workspace_size", "dg_selfcond_input",
                          "dg_lite_step", "dg_quantize_embedding_fp8",
                          "dg_vocab_pass_fp8_workspace_size", "dg_vocab_pass_fp8",
+                         "dg_vocab_pass_fp8_dyn_workspace_size", "dg_vocab_pass_fp8_dyn",
                          "dg_status_string", "dg_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
@@ -50,6 +51,13 @@ def test_header_symbols_exported():
 def test_workspace_size_pure_host():
     lib = _lib()
     f = lib.dg_vocab_pass_workspace_size
+    # the FP8 x FP8 pass adds the quantised hidden states (codes and exponents, 256-aligned)
+    dyn, f8 = lib.dg_vocab_pass_fp8_dyn_workspace_size, lib.dg_vocab_pass_fp8_workspace_size
+    for n, V, d in ((1, 4096, 256), (3, 5000, 384), (32, 262144, 2816)):
+        R = 256 * n
+        assert dyn(n, 256, V, d) == f8(n, 256, V, d) + (R * d + 255) // 256 * 256 + \
+            (4 * R + 255) // 256 * 256
+    assert dyn(1, 256, 4096, 192) == 0
     assert f(1, 256, 4096, 256) > 0
     assert f(32, 256, 262144, 2816) > f(1, 256, 262144, 2816) > 0
     assert f(1, 128, 4096, 256) == 0      # C != 256

@@ -170,3 +170,76 @@ def test_fp8_full_size_batched():
     runner.vocab_pass_fp8(c1, f, runner.fp8_workspace(1, V, d), 7)
     torch.cuda.synchronize()
     _against_oracle(c1, wl1, Eq64, np.array([0, 5, 77, 128, 254]), 7, label="one canvas:")
+
+
+# --- FP8 x FP8: hidden states quantised per row when the pass runs ----------------------------
+
+def _dyn_reference(wl, E_codes, ke, rows, seed, softcap=None, want_sc=True):
+    """The oracle on the dequantised rows (h~, E~) and the FP8 MFMA's logit bound."""
+    from parity import fp8_logit_bound
+    h_codes, kh, hq_bits = of8.activation_rows(wl.h)
+    Eq = of8.dequantize_rows(E_codes, ke)
+    T = np.repeat(wl.temperature, C)
+    cm = np.repeat(wl.commit.astype(bool), C)
+    st = np.repeat(wl.step, C)
+    ref = ovp.vocab_pass_rows(Eq, hq_bits, rows, T, cm, seed, st, softcap=softcap,
+                              want_sc=want_sc)
+    inp = VocabInputs(E64=Eq, h_bits=hq_bits, temperature_row=T, step_row=st, seed=seed,
+                      softcap=softcap)
+    return ref, cm, inp, fp8_logit_bound(h_codes, kh, E_codes, ke)
+
+
+@pytest.mark.parametrize("V,d,n,softcap", [(5000, 256, 3, None), (777, 384, 2, None),
+                                           (129, 128, 1, None), (3000, 512, 2, 15.0)])
+def test_fp8_dyn_parity(V, d, n, softcap):
+    """The FP8 x FP8 pass against the oracle on the dequantised hidden states and embedding:
+    statistics and expectation at the usual bars; tokens equal except where the oracle's
+    margin lies within the FP8 MFMA's summation bound of the two candidates (those recomputed
+    from exact sums and counted against a budget of 5 %).  d = 384 and 128 give an odd number
+    of 128-wide K chunks, V = 129 a single ragged tile."""
+    from denoise_step_sampler_amd import runner
+    wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=V + d)
+    wl.commit = (np.arange(n) % 3 == 1).astype(np.uint8)
+    wl.temperature = np.linspace(0.7, 1.3, n).astype(np.float32)
+    f, codes, k = _quantize_gpu(wl.E, V, d)
+    seed = 0xD8
+    _say(f"[vocab_pass_fp8_dyn] V={V} d={d} n={n} softcap={softcap}")
+    b = runner.from_workload(wl, commit_any=True)
+    ws = runner.fp8_workspace(n, V, d, activations=True)
+    runner.vocab_pass_fp8(b, f, ws, seed, softcap=softcap, activations=True)
+    torch.cuda.synchronize()
+    rows = np.arange(n * C)
+    ref, cm, inp, bound = _dyn_reference(wl, codes, k, rows, seed, softcap)
+    rep = compare_vocab(_host(b), ref, cm, inputs=inp, logit_bound=bound,
+                        max_exempt=max(2, int(0.05 * rows.size)))
+    _say("   ", rep)
+
+
+def test_fp8_dyn_full_size_sampled():
+    """V = 262144, d = 2816: the FP8 x FP8 pass for 32 canvases and for one canvas on sampled
+    rows against the oracle on the dequantised rows."""
+    from denoise_step_sampler_amd import runner
+    _say("[vocab_pass_fp8_dyn] generating V=262144 d=2816 embedding")
+    E = synth.make_embedding(262144, 2816, seed=0)
+    wl = synth.workload("batched", E=E)
+    V, d, n = wl.V, wl.d, wl.n_canvas
+    f, codes, k = _quantize_gpu(E, V, d)
+    b = runner.from_workload(wl)
+    runner.vocab_pass_fp8(b, f, runner.fp8_workspace(n, V, d, activations=True), 5,
+                          activations=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    canv = [0, 3, 6, 13, 31]     # 3 and 31 commit
+    rows = np.sort(np.concatenate([c * C + rng.choice(C, 3, replace=False) for c in canv]))
+    ref, cm, inp, bound = _dyn_reference(wl, codes, k, rows, 5)
+    _say("    32 canvases:", compare_vocab(_host(b, rows), ref, cm, inputs=inp, logit_bound=bound))
+    del b
+    wl1 = synth.workload("large_v", E=E)
+    c1 = runner.from_workload(wl1)
+    runner.vocab_pass_fp8(c1, f, runner.fp8_workspace(1, V, d, activations=True), 7,
+                          activations=True)
+    torch.cuda.synchronize()
+    rows1 = np.array([0, 5, 77, 128, 254])
+    ref1, cm1, inp1, bound1 = _dyn_reference(wl1, codes, k, rows1, 7)
+    _say("    one canvas:", compare_vocab(_host(c1, rows1), ref1, cm1, inputs=inp1,
+                                          logit_bound=bound1))
