@@ -175,8 +175,7 @@ def full_loop(args) -> int:
         "value": res.positions_per_s, "unit": "canvas-positions/s",
         "n_gpus": 1, "steps": res.steps_run, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8-e4m3 logits, fp16 expectation" if args.fp8_act else "bf16",
-        "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "full_loop", "n_canvas": wl.n_canvas, "C": wl.C, "V": wl.V,
                    "d": wl.d, "max_steps": 32,
                    "temperature": (float(wl.temperature[0]) if sched is None else
