@@ -626,35 +626,66 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
                                   : e4m3x8_bf16(c8[mb][2], c8[mb][3]);
     }
   };
-  // kA8: both 64-wide steps of the chunk, their fragments read at once (two 16-byte halves
-  // per operand block), E rows scaled by 2^(sA - 127), h rows by 2^(sB - 127)
+  // kA8: the two 64-wide steps of the chunk, E rows scaled by 2^(sA - 127), h rows by
+  // 2^(sB - 127).  Software-pipelined by E row block: the fragments of block mb + 1 (after the
+  // last block: the next step's h fragments and first block) are read before block mb's two
+  // MFMAs, so each read has two MFMAs (128 cycles) to land in.
   int sA[4] = {127, 127, 127, 127}, sB[2] = {127, 127};
   auto chunk_a8 = [&](const char* sc, uint32_t sn, int kn, const char* eb,
                       const uint32_t (&oe)[4]) {
     vm_wait<0>();
     __syncthreads();
     const lds_char* s = (const lds_char*)sc;
-    u32x4 a8[2][4][2], b8[2][2][2];
+    u32x4 b8[2][2], a8[2][2];  // h fragments of the step; E fragments, double-buffered
+    auto read_b = [&](int st) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+        for (int hf = 0; hf < 2; ++hf) b8[nb][hf] = lds_read16(s + rdH[2 * st + hf] + 32 * kRow1 * nb);
+    };
+    auto read_a = [&](int st, int mb, int buf) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) a8[st][mb][hf] = lds_read16(s + rdE[2 * st + hf] + 32 * kRow1 * mb);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) b8[st][nb][hf] = lds_read16(s + rdH[2 * st + hf] + 32 * kRow1 * nb);
-      }
+      for (int hf = 0; hf < 2; ++hf) a8[buf][hf] = lds_read16(s + rdE[2 * st + hf] + 32 * kRow1 * mb);
+    };
+    read_b(0);
+    read_a(0, 0, 0);
     issue_e(kn, eb, oe, sn);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      if (st == 1) issue_h(kn, sn);
+      u32x4 bc[2][2];  // this step's h fragments (the next step's are read during block 3)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int nb = 0; nb < 2; ++nb) bc[nb][0] = b8[nb][0], bc[nb][1] = b8[nb][1];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int cur = (4 * st + mb) & 1;
+        if (mb < 3) {
+          read_a(st, mb + 1, cur ^ 1);
+        } else if (st == 0) {
+          read_b(1);
+          read_a(1, 0, cur ^ 1);
+        }
+        if (st == 1 && mb == 0) issue_h(kn, sn);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = mfma32x32x64f8(a8[st][mb][0], a8[st][mb][1], b8[st][nb][0], b8[st][nb][1],
-                                       acc[mb][nb], sA[mb], sB[nb]);
+          acc[mb][nb] = mfma32x32x64f8(a8[cur][0], a8[cur][1], bc[nb][0], bc[nb][1], acc[mb][nb],
+                                       sA[mb], sB[nb]);
+      }
     }
+    // order: the first block's reads, then per block the next block's reads before its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
   auto chunk = [&](auto deferred, const char* sc, uint32_t sn, int kn, const char* eb,
                    const uint32_t (&oe)[4]) {
