@@ -959,7 +959,10 @@ constexpr int kZero = -25;  // scale-table entry of a half tile whose weights va
 
 // fp16 bits of 2^k for kZero <= k <= kUp (0 for kZero), twice
 __device__ __forceinline__ uint32_t f16_pow2x2(int k) {
-  const uint32_t h = k >= -14 ? (uint32_t)(k + 15) << 10 : (k > kZero ? 1u << (k + 24) : 0u);
+  const uint32_t hn = (uint32_t)(k + 15) << 10;      // normal: exponent field k + 15
+  const uint32_t hs = 1u << ((uint32_t)(k + 24) & 31u);  // subnormal: 2^(k + 24) quanta
+  uint32_t h = k >= -14 ? hn : hs;
+  h = k > kZero ? h : 0u;
   return h | (h << 16);
 }
 
