@@ -35,8 +35,8 @@ struct VocabArgs {
   // row when the pass runs; the logits pass then multiplies codes by codes on FP8 MFMA
   const uint8_t* h8;
   const int32_t* h_exp;
-  // the expectation pass's operand: the embedding as fp16, [e16_rows(V)][d], rows past V zero
-  // (required with selfcond)
+  // the expectation pass's operand: the embedding as fp16 in the expectation MFMA's B-fragment
+  // order (embedding_f16.hip), e16_rows(V) x d entries, zero past V (required with selfcond)
   const uint16_t* E16;
 };
 

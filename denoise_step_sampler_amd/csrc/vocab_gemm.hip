@@ -878,8 +878,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_logits(GemmK g) {
 //
 // Operands, both fp16 on v_mfma_f32_16x16x32_f16: the weights 2^(z2 - ref) the logits pass
 // stored, each relative to the integer reference ref of its row and 128-entry half tile, and
-// E16 [vp][d] (the embedding as fp16, rows padded with zeros to whole tiles), staged row-major
-// and read as B fragments with transpose reads.  Every row's partial is kept in units of 2^U,
+// E16 (the embedding as fp16, rows padded with zeros to whole tiles) in B-fragment order: the
+// 1 KB block of entries 32 b .. 32 b + 31 and columns 16 c .. 16 c + 15 at (b d / 16 + c) KB, lane
+// n + 16 g's 16 bytes holding column n's entries 8 g .. 8 g + 7, so a chunk's blocks are one
+// contiguous run for the copies and a B fragment is one 16-byte read.  Every row's partial is kept in units of 2^U,
 // U = M - 15 with M the row's largest half-tile reference over the unit's vocabulary range
 // (the prologue reads them all first): a half tile with reference rf enters with its weights
 // multiplied by 2^(rf - U) in fp16 (one packed multiply per A register).  For rf >= U that is
@@ -924,34 +926,6 @@ __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(p);
 }
 
-// Bank swizzle of the staged E rows of the expectation pass: the 32-byte column pair p of
-// staged row `row` sits at pair p ^ e_swz(row).  A transpose read touches, per lane group,
-// rows k0 + 8 g + (0..3) (and + 4): with 16 pairs a row (NCB >= 4, 512- or 256-byte rows, so
-// every row starts on the same bank) the low two row bits and bit 3 spread those rows over
-// the eight 32-byte bank windows; with 4 pairs a row (NCB = 2, two rows per 256 bytes) row
-// bit 0 already alternates the half, so bits 1 and 3 pick the pair.
-template <int NCB>
-__device__ __forceinline__ int e_swz(int row) {
-  return NCB >= 4 ? ((row & 3) | (((row >> 3) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
-}
-
-// B operand of v_mfma_f32_16x16x32_f16 for 16 columns of the staged E rows [0, 32) (row pitch
-// `pitch` bytes): lane (g = lane / 16, i = lane % 16) needs E[8 g + 0..7][col i].  Two transpose
-// reads: lane j of a 16-lane group addresses row 8 g + 4 half + j / 4, bytes 8 (j % 4) .. + 7 of
-// the columns' 32-byte pair; lane i then holds rows + 0..3 of column i.  `a` is the lane's byte
-// address of row 8 g + j / 4 and of the columns' swizzled pair
-// (row * pitch + 32 (pair ^ e_swz(row)) + 8 (j % 4)).
-__device__ __forceinline__ u32x4 e_frag(const lds_char* e, int pitch, int a) {
-  typedef short i16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const lds_char* q = e + a;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q));
-  const i16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<lds_char*>(q + 4 * pitch));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
 // A unit spans at most kMaxUnitTiles vocabulary tiles (its scale table fits in LDS).
 constexpr int kMaxUnitTiles = 64;
 constexpr int kUp = 15;     // U = M - kUp: the largest half tile's weights enter times 2^15
@@ -976,15 +950,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   constexpr int kKC2 = 32;                // K chunk (vocabulary entries) per stage
   constexpr int kNst2 = 4;                // stages: copies run three chunks ahead
   constexpr int kPB = kTile * 2 * kKC2;   // weights: 16 fragment blocks of 1 KB (16 KB)
-  constexpr int kPitchE = 2 * BN;         // bytes of one staged E row
-  constexpr int kEB = kKC2 * kPitchE;     // E: 32 rows x BN columns
+  constexpr int kEB = kKC2 * 2 * BN;      // E: 32 entries x BN columns, 2 NCB blocks of 1 KB
   constexpr int kStage = kPB + kEB;
   constexpr int kNE = kEB / 1024;         // E copies per stage (2 NCB)
   constexpr int kNEw = kNE >= 8 ? kNE / 8 : 1;  // E copies per wave (waves >= kNE repeat one)
   static_assert(kNE % 8 == 0 || kNE < 8, "E copies must divide among the eight waves");
   constexpr int kCpw = 2 + kNEw;          // copies per wave and chunk
-  constexpr int kC16 = BN / 8;            // 16-byte chunks per staged E row
-  constexpr int kRowsPerCopy = 1024 / kPitchE;  // E rows per 1 KB copy
   __shared__ __attribute__((aligned(1024))) char stg[kNst2][kStage];
   // scale exponent rf - U of (half tile ht, row): byte 256 ht + 64 rw + 4 (row % 16) + rb for
   // row = 64 rw + 16 rb + row % 16, so that one 32-bit read gives a lane its four A rows
@@ -1027,30 +998,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   }
 
   // ---- copies.  Weights: copy j of wave w moves the fragment block of row16 2 w + j for the
-  // chunk (LDS 1 KB number 2 w + j).  E: copy m moves the stage's 1 KB number (w + 8 m) % kNE,
-  // i.e. rows kRowsPerCopy ((w + 8 m) % kNE) + lane / kC16, each lane 16 bytes of a row
-  // holding the swizzled 16-byte column chunk.
+  // chunk (LDS 1 KB number 2 w + j).  E: copy m moves fragment block (w + 8 m) % kNE of the
+  // unit's 2 NCB column blocks for the chunk (contiguous in E16), to the same 1 KB of the stage.
   const size_t nvb = g.vpad / 32;
   const char* pbase = reinterpret_cast<const char*>(g.P) +
                       (((size_t)u.pc * 16 + 2 * w) * nvb + (size_t)u.t0 * (kTile / 32)) * 1024;
   const uint32_t offP = 16u * (uint32_t)lane;
-  const uint32_t epitch = 2u * (uint32_t)g.a.d;
-  const char* ebase = reinterpret_cast<const char*>(g.a.E16) +
-                      ((size_t)u.t0 * kTile) * epitch + (size_t)u.j * BN * 2;
-  const int erow0 = lane / kC16;                     // row within the copy
+  const size_t ncb16 = (size_t)g.a.d / 16;              // column blocks of E16
   const int ew = kNE >= 8 ? w : w % kNE;             // this wave's first E copy
-  // swizzled 16-byte column chunk this lane fetches into its (linear) LDS slot; the rows a
-  // lane fills, kRowsPerCopy (ew + 8 m) + erow0, agree in their low four bits for every m, so
-  // one value serves all of the lane's copies
-  static_assert((8 * kRowsPerCopy) % 16 == 0, "copies of one lane share the swizzle");
-  static_assert(kC16 >= 8 && (NCB >= 4 ? kC16 >= 16 : true), "swizzle stays within a row");
-  const uint32_t ecol =
-      16u * (uint32_t)((lane % kC16) ^ (2 * e_swz<NCB>(kRowsPerCopy * ew + erow0)));
-  // this lane's transpose-read address of column block 0 (block cb: ea0 ^ 32 cb; the swizzle is
-  // an XOR on the pair index and the blocks of a wave are pairs 8 cw .. 8 cw + 7, or 4 cw ..
-  // + 3, or 2 cw .. + 1: XOR with 32 cb stays among them)
-  const int erl = 8 * (lane >> 4) + ((lane & 15) >> 2);
-  const int ea0 = erl * kPitchE + ((32 * NCB * cw) ^ (32 * e_swz<NCB>(erl))) + 8 * (lane & 3);
+  const char* ebase = reinterpret_cast<const char*>(g.a.E16) +
+                      (((size_t)u.t0 * (kTile / 32)) * ncb16 + (size_t)u.j * 2 * NCB + ew) * 1024;
   const int nkc = (u.t1 - u.t0) * (kTile / kKC2);  // a multiple of 8
   uint32_t sa[kNst2];  // LDS addresses of the stages
 #pragma unroll
@@ -1068,16 +1025,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   };
   auto issue_e = [&](int kc, uint32_t dst) {
     kc = min(kc, nkc - 1);
-    const char* eb = uniform_ptr(ebase + (size_t)kc * kKC2 * epitch);
-    // the lane's first row, opaque here so that each copy's row offset is formed next to its
-    // copy instead of being kept per copy for the whole loop
-    int row0 = kRowsPerCopy * ew + erow0;
-    asm volatile("" : "+v"(row0));
+    const char* eb = ebase + (size_t)kc * ncb16 * 1024;
 #pragma unroll
-    for (int m = 0; m < kNEw; ++m) {
-      const int row = row0 + 8 * kRowsPerCopy * m;
-      dma_asm(eb, (uint32_t)row * epitch + ecol, dst + (uint32_t)kPB + 1024u * (uint32_t)(ew + 8 * m));
-    }
+    for (int m = 0; m < kNEw; ++m)
+      dma_asm(uniform_ptr(eb + (size_t)m * 8 * 1024), offP,
+              dst + (uint32_t)kPB + 1024u * (uint32_t)(ew + 8 * m));
   };
 
   const int ar = lane & 15;
@@ -1095,12 +1047,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     // the E copies at once (E may miss in L2), the weight copies halfway through the chunk
     issue_e(kn, sn);
     const lds_char* sp = (const lds_char*)sc;
-    const lds_char* se = (const lds_char*)(sc + kPB);
-    // the swizzle term, opaque to the compiler per chunk: the swizzled read addresses are
-    // formed next to their reads instead of being hoisted out of the loop (which holds one
-    // register per column block for the whole loop and spills)
-    int ea = ea0;
-    asm volatile("" : "+v"(ea));
+    const lds_char* se = (const lds_char*)(sc + kPB) + NCB * cw * 1024 + 16 * lane;
     u32x4 fa[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -1111,7 +1058,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       if (cb == NCB / 2) issue_p(kn, sn);
-      const u32x4 fb = e_frag(se, kPitchE, ea ^ (32 * cb));
+      const u32x4 fb = lds_read16(se + 1024 * cb);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[rb][cb] = mfma16x16x32h(fa[rb], fb, acc[rb][cb]);
     }

@@ -68,15 +68,19 @@ size_t dg_vocab_pass_workspace_size(int n_canvas, int C, int V, int d);
 size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int with_e16);
 
 /* dg_embedding_f16 -- the embedding in the form the self-conditioning expectation multiplies:
- * fp16, row-major, rows padded with zeros to whole 256-entry tiles: E16[v * d + k] =
- * fp16(E[v, k]) for v < V (round to nearest even), 0 for V <= v < DG_E16_ROWS(V).  The expectation sum_v p_v E_v ([TR] eq. (6)) runs on
- * fp16 MFMA because probability weights in bf16 (8 significant bits) leave a relative error of
- * about 1e-3 in the expectation of a flat distribution, at the 2e-3 bar; fp16 has 11 bits.
- * The embedding is constant across denoising steps: a caller builds this once (like the FP8
- * codes) and hands it to dg_vocab_pass_ex; the other entry points build it per call.
+ * fp16 (round to nearest even), the vocabulary padded with zero entries to DG_E16_ROWS(V), in
+ * the B-fragment order of the expectation's MFMA: for the entry block b (entries 32 b ..
+ * 32 b + 31) and the column block c (columns 16 c .. 16 c + 15), the 1,024-byte block at byte
+ * offset (b * (d / 16) + c) * 1024 holds fp16(E[32 b + 8 g + e, 16 c + n]) at byte
+ * 16 (n + 16 g) + 2 e (n < 16, g < 4, e < 8); entries V .. DG_E16_ROWS(V) - 1 are 0.  The
+ * expectation sum_v p_v E_v ([TR] eq. (6)) runs on fp16 MFMA because probability weights in
+ * bf16 (8 significant bits) leave a relative error of about 1e-3 in the expectation of a flat
+ * distribution, at the 2e-3 bar; fp16 has 11 bits.  The embedding is constant across denoising
+ * steps: a caller builds this once (like the FP8 codes) and hands it to dg_vocab_pass_ex; the
+ * other entry points build it per call.
  *  E      [V, d] bf16, |E| < 65504 (larger values give unspecified expectation rows).
  *  V      1 .. DG_MAX_V;  d: multiple of 128, 128 .. DG_MAX_D.
- *  E16    [DG_E16_ROWS(V), d] uint16 (fp16 bits) out, dg_embedding_f16_bytes(V, d) bytes.
+ *  E16    DG_E16_ROWS(V) * d uint16 (fp16 bits) out, dg_embedding_f16_bytes(V, d) bytes.
  *  E and E16 16-byte aligned.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
 #define DG_E16_ROWS(V) ((((V) + 255) / 256) * 256)
@@ -188,8 +192,9 @@ dg_status dg_vocab_pass_ex_noalloc(const uint16_t* E, const uint16_t* E16, const
  * A power-of-two scale makes every dequantised value 2^k * value(code) an exact bf16 number.
  *  E        [V, d] bf16, finite, |E| < 2^127.   d % 128 == 0, 128 <= d <= DG_MAX_D.
  *  codes    [V, d] uint8 out;  row_exp [V] int32 out.
- *  E16      [DG_E16_ROWS(V), d] fp16 out, or NULL: the expectation pass's operand built from
- *           the dequantised rows (dg_embedding_f16 of E~ below).
+ *  E16      DG_E16_ROWS(V) * d fp16 out (the layout of dg_embedding_f16), or NULL: the
+ *           expectation pass's operand built from the dequantised rows (dg_embedding_f16 of E~
+ *           below).
  *  E, codes and E16 16-byte aligned.
  * Errors: DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP. */
 dg_status dg_quantize_embedding_fp8(const uint16_t* E, int V, int d, uint8_t* codes,

@@ -109,6 +109,15 @@ def fp8_logit_bound(h_codes, kh, e_codes, ke):
     return bound
 
 
+def fragment_order(rows16: np.ndarray, d: int) -> np.ndarray:
+    """The layout dg.h states for the fp16 embedding, from its row-major form [V_pad, d]: the
+    1 KB block of entry block b and column block c at (b d / 16 + c) KB holds entry 32 b + 8 g
+    + e, column 16 c + n at byte 16 (n + 16 g) + 2 e."""
+    vp = rows16.shape[0]
+    x = rows16.reshape(vp // 32, 4, 8, d // 16, 16)        # b, g, e, c, n
+    return np.ascontiguousarray(x.transpose(0, 3, 1, 4, 2)).reshape(-1)   # b, c, g, n, e
+
+
 def _close(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)

@@ -82,13 +82,15 @@ def test_quantizer_bit_exact():
     assert np.array_equal(k, k_ref), np.nonzero(k != k_ref)[0][:8]
     bad = np.argwhere(codes != q_ref)
     assert bad.size == 0, [(int(r), int(c), int(codes[r, c]), int(q_ref[r, c])) for r, c in bad[:8]]
-    # the expectation's operand: the dequantised rows as fp16, zero rows past V (the row scaled
-    # by 2^40 lies beyond fp16's range and becomes infinities on both sides)
+    # the expectation's operand: the dequantised rows as fp16, zero entries past V, in the
+    # fragment order of the header (the row scaled by 2^40 lies beyond fp16's range and becomes
+    # infinities on both sides)
+    from parity import fragment_order
     rows = (V + 255) // 256 * 256
-    q16 = f.E16.cpu().numpy().view(np.uint16).reshape(rows, d)
+    want = np.zeros((rows, d), np.uint16)
     with np.errstate(over="ignore"):
-        want = of8.dequantize_rows(q_ref, k_ref).astype(np.float16).view(np.uint16)
-    assert np.array_equal(q16[:V], want) and np.all(q16[V:] == 0)
+        want[:V] = of8.dequantize_rows(q_ref, k_ref).astype(np.float16).view(np.uint16)
+    assert np.array_equal(f.E16.cpu().numpy().view(np.uint16), fragment_order(want, d))
 
 
 @pytest.mark.parametrize("softcap,prepared", [(None, True), (15.0, True), (None, False)])

@@ -356,8 +356,9 @@ def test_draw_temperature_equal_to_statistics_is_the_plain_pass():
 # --- the fp16 embedding ---------------------------------------------------------------------
 
 def test_embedding_f16_is_the_fp16_conversion():
-    """dg_embedding_f16: E16[v][k] = fp16(E[v][k]) (round to nearest even, numpy's
-    conversion), zero rows past V up to the padded row count; tiny and large entries included."""
+    """dg_embedding_f16: fp16(E) (round to nearest even, numpy's conversion), zero entries past
+    V up to the padded count, in the fragment order of the header; tiny and large entries
+    included."""
     from denoise_step_sampler_amd import runner
     V, d = 1000, 256
     E = synth.bf16_to_f32(synth.make_embedding(V, d, seed=5)).copy()
@@ -366,10 +367,11 @@ def test_embedding_f16_is_the_fp16_conversion():
     t = runner.embedding_f16(runner.bf16_tensor(E_bits), V, d)
     torch.cuda.synchronize()
     rows = (V + 255) // 256 * 256
-    got = t.cpu().numpy().view(np.uint16).reshape(rows, d)
-    want = synth.bf16_to_f32(E_bits).astype(np.float16).view(np.uint16)
-    assert np.array_equal(got[:V], want)
-    assert np.all(got[V:] == 0)
+    want = np.zeros((rows, d), np.uint16)
+    want[:V] = synth.bf16_to_f32(E_bits).astype(np.float16).view(np.uint16)
+    got = t.cpu().numpy().view(np.uint16)
+    from parity import fragment_order
+    assert np.array_equal(got, fragment_order(want, d))
 
 
 def test_prepared_embedding_gives_the_same_bits():
