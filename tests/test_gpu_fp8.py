@@ -192,13 +192,14 @@ def _dyn_reference(wl, E_codes, ke, rows, seed, softcap=None, want_sc=True):
 
 
 @pytest.mark.parametrize("V,d,n,softcap", [(5000, 256, 3, None), (777, 384, 2, None),
-                                           (129, 128, 1, None), (3000, 512, 2, 15.0)])
+                                           (129, 128, 1, None), (3000, 512, 2, 15.0),
+                                           (300, 8192, 1, None)])
 def test_fp8_dyn_parity(V, d, n, softcap):
     """The FP8 x FP8 pass against the oracle on the dequantised hidden states and embedding:
     statistics and expectation at the usual bars; tokens equal except where the oracle's
     margin lies within the FP8 MFMA's summation bound of the two candidates (those recomputed
     from exact sums and counted against a budget of 5 %).  d = 384 and 128 give an odd number
-    of 128-wide K chunks, V = 129 a single ragged tile."""
+    of 128-wide K chunks, V = 129 a single ragged tile, d = 8192 the widest hidden state."""
     from denoise_step_sampler_amd import runner
     wl = synth.workload("lite", V=V, d=d, n_canvas=n, seed=V + d)
     wl.commit = (np.arange(n) % 3 == 1).astype(np.uint8)

@@ -100,3 +100,67 @@ def test_lite_sampler_loop(softcap, stability, thr):
     assert compared >= 4
     if stability and compared == steps:
         assert stopped.all()
+
+
+def test_lite_step_full_shape_sampled():
+    """Two Lite steps at the serving shape (2 canvases x 256, V = 262,144, d = 2,816), the stop
+    test off, compared with the oracle on 16 sampled positions of each canvas: confidences,
+    canvas tokens, commit flags, the returned canvas and the argmax record.  With the stop test
+    off every output of a position depends on that position alone, so the oracle's step runs on
+    full-size arrays whose unsampled positions hold fixed placeholder values (their outputs are
+    not compared); tau anneals 1.0 -> 0.75."""
+    from denoise_step_sampler_amd import runner
+    wl = synth.workload("full_loop", n_canvas=2, seed=5)
+    n, V, d = wl.n_canvas, wl.V, wl.d
+    assert (V, d) == (262144, 2816)
+    wl.temperature = np.ones(n, np.float32)
+    rng = np.random.default_rng(8)
+    rows = np.sort(np.concatenate([c * C + rng.choice(C, 16, replace=False) for c in range(n)]))
+    _say(f"[lite full shape] widening E ({V} x {d})")
+    E64 = ovp.widen_bf16(wl.E)
+    E_t = runner.bf16_tensor(wl.E)
+    seed, steps = 21, 2
+    st = runner.lite_state(n)
+    R = n * C
+    o = dict(x=np.zeros(R, np.int64), pa=np.full(R, -1), pc=np.full(R, np.inf),
+             cm=np.zeros(R, np.uint8), cnt=np.zeros(n, np.int64))
+    b = None
+    for k in range(steps):
+        tau = runner.temperature_schedule(k, steps, 1.0, 0.5)
+        h = synth.loop_hidden(wl, k, None)
+        if b is None:
+            b = runner.allocate(n, V, d, E_t, runner.bf16_tensor(h), wl.temperature, None,
+                                np.full(n, k, np.int32), want_selfcond=False)
+            b.draw_temperature = torch.empty(n, dtype=torch.float32, device="cuda")
+        else:
+            b.h.copy_(runner.bf16_tensor(h))
+            b.step.fill_(k)
+        b.draw_temperature.fill_(tau)
+        runner.vocab_pass(b, seed)
+        runner.lite_step(b, st, 1.0, 0, seed)
+        torch.cuda.synchronize()
+        ref = ovp.vocab_pass_rows(E64, h, rows, np.repeat(wl.temperature, C), np.zeros(R, bool),
+                                  seed, np.full(R, k), want_sc=False,
+                                  draw_temperature_row=np.full(R, tau))
+        # full-size inputs of the oracle's step: the sampled rows' oracle values, placeholders
+        # elsewhere
+        full = dict(H=np.zeros(R), am=np.zeros(R, np.int64), gt=np.zeros(R, np.int64),
+                    cf=np.full(R, 0.5))
+        full["H"][rows], full["am"][rows] = ref.entropy, ref.argmax
+        full["gt"][rows], full["cf"][rows] = ref.gumbel, ref.conf
+        r = osm.lite_step(full["H"], full["am"], full["gt"], full["cf"], n, C, V, 1.0, 0, seed,
+                          k, o["x"], o["pa"], o["pc"], o["cm"], o["cnt"])
+        conf = st.conf.cpu().numpy()[rows]
+        assert np.all(np.abs(conf - ref.conf) <= 2e-3 * ref.conf + 1e-6), f"step {k}: conf"
+        tie = (ref.mu_argmax < MARGIN) | (ref.mu_gumbel < MARGIN) | (r.mu_commit[rows] < MARGIN)
+        assert tie.sum() <= 2, f"step {k}: {int(tie.sum())} near-ties"
+        got = dict(x=st.x.cpu().numpy(), committed=st.committed.cpu().numpy(),
+                   final=st.final_tokens.cpu().numpy(), prev_argmax=st.prev_argmax.cpu().numpy())
+        for key, v in got.items():
+            bad = (v[rows] != getattr(r, key)[rows]) & ~tie
+            assert not bad.any(), f"step {k}: {key} differs at rows {rows[bad][:8]}"
+        _say(f"   step {k}: {int(r.committed[rows].sum())} of {rows.size} sampled positions "
+             f"committed, {int(tie.sum())} near-ties")
+        o = dict(x=r.x, pa=r.prev_argmax, pc=r.prev_conf, cm=r.committed, cnt=r.stable_count)
+        if tie.any():
+            break
