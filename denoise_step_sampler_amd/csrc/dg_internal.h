@@ -17,7 +17,7 @@ struct VocabArgs {
   int d;
   const float* temperature;
   const float* draw_temperature;  // temperature of the Gumbel-max draw alone, or null (the
-                                  // draw uses `temperature`; two-GEMM path only)
+                                  // draw uses `temperature`)
   const uint8_t* commit;
   uint32_t k0, k1;  // Philox key
   const int32_t* step;
@@ -26,7 +26,7 @@ struct VocabArgs {
   int32_t* argmax_tok;
   int32_t* gumbel_tok;
   float* selfcond;
-  float softcap;  // > 0: z = softcap tanh(S / softcap) / T (two-GEMM path only); 0: z = S / T
+  float softcap;  // > 0: z = softcap tanh(S / softcap) / T; 0: z = S / T
   // FP8 embedding for the logits pass: E4M3 codes [V, d] and row exponents [V],
   // E = 2^E_exp[v] * value(codes); null: the logits pass reads E (then E is not read at all)
   const uint8_t* E8;

@@ -87,7 +87,7 @@ size_t dg_vocab_pass_ex_workspace_size(int n_canvas, int C, int V, int d, int wi
 size_t dg_embedding_f16_bytes(int V, int d);
 dg_status dg_embedding_f16(const uint16_t* E, int V, int d, uint16_t* E16, void* stream);
 
-/* dg_vocab_pass -- the fused vocabulary pass of one denoising step.
+/* dg_vocab_pass -- the vocabulary pass of one denoising step.
  *
  * For each row r (canvas c = r / C) with logits S[r, v] = sum_k h[r, k] E[v, k] (the tied
  * embedding used as the unembedding, [TR] eq. (5); [EXP] tied embeddings) and tempered
@@ -98,8 +98,10 @@ dg_status dg_embedding_f16(const uint16_t* E, int V, int d, uint16_t* E16, void*
  *   gumbel_tok[r] = smallest v attaining max_v (z_v + g_v), g = -ln(-ln u) with u from the
  *                   Gumbel counter of (r, v, step[c])                ([VLLM] Gumbel-max)
  *   selfcond[r,:] = sum_v p_v E[v, :]                    ([TR] eq. (6), the argument of FFW)
- * The [R, V] logits are never written to memory.  For a commit canvas (commit[c] != 0) only
- * argmax_tok is written; its rows of lse, entropy, gumbel_tok and selfcond are untouched.
+ * The [R, V] logits are never written to memory; with selfcond, fp16 probability weights
+ * 2^(z2 - ref) (each relative to its row's 128-entry reference) pass through the workspace
+ * between the logits and the expectation contractions.  For a commit canvas (commit[c] != 0)
+ * only argmax_tok is written; its rows of lse, entropy, gumbel_tok and selfcond are untouched.
  *
  *  E            [V, d] bf16, read only.
  *  h            [n_canvas * C, d] bf16 final hidden states, read only.
