@@ -232,28 +232,31 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int vb0 = vt0 + 4 * (lane >> 5);
+  // the scans keep entry indices relative to the block's first entry, so that each select
+  // takes a constant (no per-entry index arithmetic); the empty value maps back to 0x7FFFFFFF
   float amv = -INFINITY;
-  int ami = 0x7FFFFFFF;
+  int amr = 0x7FFFFFFF - vb0;
   // entries past V exist only in the last tile: a full half tile scans without the checks
   const bool full = vt0 + kHalf <= V;
-  auto scan = [&](auto masked, const f32x16& sb, int vb) {
+  auto scan = [&](auto masked, const f32x16& sb, int ro) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int v = vb + 8 * (i >> 2) + (i & 3);
-      const float x = (!decltype(masked)::value || v < V) ? sb[i] : -INFINITY;
-      argmax_next(amv, ami, x, v);  // v increases along the scan
+      const int o = ro + 8 * (i >> 2) + (i & 3);
+      const float x = (!decltype(masked)::value || vb0 + o < V) ? sb[i] : -INFINITY;
+      argmax_next(amv, amr, x, o);  // o increases along the scan
     }
   };
   auto scan_all = [&](auto masked) {
-    scan(masked, s0, vb0);
-    scan(masked, s1, vb0 + 32);
-    scan(masked, s2, vb0 + 64);
-    scan(masked, s3, vb0 + 96);
+    scan(masked, s0, 0);
+    scan(masked, s1, 32);
+    scan(masked, s2, 64);
+    scan(masked, s3, 96);
   };
   if (full)
     scan_all(std::false_type{});
   else
     scan_all(std::true_type{});
+  int ami = amr + vb0;
   argmax_merge(amv, ami, xor_f(amv, 32), xor_i(ami, 32));
   // the half tile's largest z2: rounding is monotone and c2 > 0, so max_v (S_v c2) rounded
   // equals (max_v S_v) c2 rounded.  With the cap: the z2 of S's argmax, which the block loop
@@ -300,6 +303,7 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
   // no per-entry branches or selects
   auto block = [&](auto masked, const f32x16& sb, int vbb, uint16_t* pbk) {
     constexpr bool kMasked = decltype(masked)::value;
+    int gir = gi - vbb;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int vb = vbb + 8 * q;
@@ -318,20 +322,22 @@ __device__ __forceinline__ void epi_row(const f32x16& s0, const f32x16& s1, cons
           const float pe = ok ? hw_exp2(dz) : 0.0f;
           ls += pe;
           as = __builtin_fmaf(pe, ok ? dz : 0.0f, as);
-          argmax_next(gv, gi, ok ? zk + g2 : -INFINITY, vb + j);
+          argmax_next(gv, gir, ok ? zk + g2 : -INFINITY, 8 * q + j);
           pv[j] = pe;
         } else {
           const float pe = hw_exp2(dz);
           ls += pe;
           as = __builtin_fmaf(pe, dz, as);
-          argmax_next(gv, gi, zk + g2, vb + j);  // entries in increasing order
+          argmax_next(gv, gir, zk + g2, 8 * q + j);  // entries in increasing order
           pv[j] = pe;
         }
       }
       const uint32_t w01 = pack_f16x2(pv[0], pv[1]), w23 = pack_f16x2(pv[2], pv[3]);
-      lsb = add_f16x2(add_f16x2(lsb, w01), w23);
+      // the rounded weights' sum normalises the expectation: needed only when it is asked for
+      if (kStore) lsb = add_f16x2(add_f16x2(lsb, w01), w23);
       if (kStore) *reinterpret_cast<u32x2*>(pbk + 128 * q) = u32x2{w01, w23};
     }
+    gi = gir + vbb;
   };
   // one 32-entry block at a time, in a run-time loop (one copy of the block's code: unrolled,
   // the blocks' Philox streams would compete for the registers that hold the logits)
