@@ -935,19 +935,20 @@ __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) {
 // A unit spans at most kMaxUnitTiles vocabulary tiles (its scale table fits in LDS).
 constexpr int kMaxUnitTiles = 64;
 constexpr int kUp = 15;     // U = M - kUp: the largest half tile's weights enter times 2^15
-constexpr int kZero = -25;  // scale-table entry of a half tile whose weights vanish (or past V)
+// scale-table entry of a half tile whose weights vanish (2^(rf - U) below 2^-24, or past V):
+// far enough below fp16's smallest subnormal that 2^kZero rounds to 0
+constexpr int kZero = -32;
 
-// fp16 bits of 2^k for kZero <= k <= kUp (0 for kZero), twice
-__device__ __forceinline__ uint32_t f16_pow2x2(int k) {
-  const uint32_t hn = (uint32_t)(k + 15) << 10;      // normal: exponent field k + 15
-  const uint32_t hs = 1u << ((uint32_t)(k + 24) & 31u);  // subnormal: 2^(k + 24) quanta
-  uint32_t h = k >= -14 ? hn : hs;
-  h = k > kZero ? h : 0u;
-  return h | (h << 16);
+// 2^k in fp16 for kZero <= k <= kUp: exact for k >= -24 (subnormal below -14), 0 for k <= -26
+// (one v_ldexp_f16; the scale table holds no -25)
+__device__ __forceinline__ _Float16 f16_pow2(int k) {
+  return __builtin_amdgcn_ldexph((_Float16)1.0f, k);
 }
 
-__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b));
+// both fp16 halves of a times s (one v_pk_mul_f16, s broadcast by op_sel); the operands are
+// taken by value
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, _Float16 s) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * (f16x2){s, s});
 }
 
 template <int NCB>
@@ -995,7 +996,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
     for (int ht = hh; ht < nh; ht += 2) {
       const int rf = rp[(size_t)ht * R];
       // rf <= M; references lie within +-2^24, so the difference does not overflow
-      shb[ht * kTile + pos] = (int8_t)(rf == INT32_MIN ? kZero : max(rf - M + kUp, kZero));
+      const int k = rf - M + kUp;
+      shb[ht * kTile + pos] = (int8_t)(rf == INT32_MIN || k < -24 ? kZero : k);
     }
     if (hh == 0 && u.j == 0)
       g.accM[(size_t)u.s * R + (size_t)u.pc * kTile + row] =
@@ -1047,7 +1049,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   // one chunk from stage sc once its copies have landed (the two chunks issued after it may
   // still be in flight), its weights scaled by sc2 (per A row of the lane: 64 rw + 16 rb + ar);
   // copies chunk kn into stage sn, which every wave finished reading before the barrier
-  auto chunk = [&](const char* sc, uint32_t sn, int kn, const uint32_t (&sc2)[4]) {
+  auto chunk = [&](const char* sc, uint32_t sn, int kn, const _Float16 (&sc2)[4]) {
     vm_wait<2 * kCpw>();
     __syncthreads();
     // the E copies at once (E may miss in L2), the weight copies halfway through the chunk
@@ -1078,9 +1080,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_selfcond(GemmK g) {
   const lds_char* shp = (const lds_char*)shb + 64 * rw + 4 * ar;
   for (int kc = 0; kc < nkc; kc += kNst2) {  // one half tile (four chunks) per iteration
     const uint32_t shw = lds_u32(shp + (kc >> 2) * kTile);
-    uint32_t sc2[4];
+    _Float16 sc2[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) sc2[rb] = f16_pow2x2((int)(int8_t)(uint8_t)(shw >> (8 * rb)));
+    for (int rb = 0; rb < 4; ++rb) sc2[rb] = f16_pow2((int)(int8_t)(uint8_t)(shw >> (8 * rb)));
     chunk(stg[0], sa[3], kc + 3, sc2);
     chunk(stg[1], sa[0], kc + 4, sc2);
     chunk(stg[2], sa[1], kc + 5, sc2);
