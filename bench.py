@@ -6,6 +6,7 @@ d = 2816, 8 canvases commit).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload batched|large_v|lite|tiny|full_loop] [--no-cpu-baseline]
+                    [--graph] [--fp8 | --fp8-act] [--softcap C]
 """
 from __future__ import annotations
 
@@ -215,6 +216,9 @@ def main() -> int:
                          "(0: skip)")
     ap.add_argument("--anneal", default=None, metavar="TMAX,TMIN",
                     help="full_loop only: linear temperature schedule over the 32 steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as a captured HIP graph (the step counter advanced by a "
+                         "kernel inside it), one replay per step, instead of eager launches")
     args = ap.parse_args()
     args.fp8 = args.fp8 or args.fp8_act
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -288,6 +292,36 @@ def main() -> int:
     vp_avg = float(np.mean(vp_ms))
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.3f}s), "
         f"vocab pass {vp_avg:.3f} ms (min {min(vp_ms):.3f})")
+    eager_ms_step = ms_step
+    if args.graph:
+        # the same step captured once (the entry points queue only kernels: no allocation,
+        # memset or synchronisation) and replayed; a kernel inside advances the step counter
+        def graph_step():
+            cur = torch.cuda.current_stream()
+            b.step.add_(1)
+            vocab(cur)
+            runner.accept_renoise(b, wl.budget, wl.confidence, wl.stability, seed, cur)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            graph_step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            graph_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / args.steps
+        log(f"[bench] {args.steps} graph replays: {ms_step:.3f} ms/step "
+            f"(eager launches: {eager_ms_step:.3f})")
 
     # the dominant kernel, k_gemm_logits (logits + epilogue, 2 R V d flops): the same pass
     # without the expectation runs it plus two small kernels (canvas order, row statistics),
@@ -383,7 +417,10 @@ def main() -> int:
                                   + (", hidden states quantised per row in the pass"
                                      if args.fp8_act else "")) if args.fp8 else "bf16")
                    + "; its fp16 copy for the expectation prepared once, untimed",
-                   "caches": "warm: no L2 / MALL flush between steps"},
+                   "caches": "warm: no L2 / MALL flush between steps",
+                   "launch": ("one HIP graph replay per step (eager launches: "
+                              f"{eager_ms_step:.3f} ms/step)") if args.graph
+                   else "eager launches on one stream"},
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "e_stream_hbm_frac": (2.0 * wl.V * wl.d) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "vocab_pass": {"avg_launch_ms": vp_avg, "algorithmic_flops": flops,
